@@ -15,13 +15,9 @@ import oracle as O
 import synthetic as S
 from tests.exact import bf16 as ex_bf16
 from tests.exact import fl32 as ex_fl32
-from tests.exact import rne_int, round_sig
+from tests.exact import rne_int
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
-
-
-def _f(bits16):
-    return float(O.bf16_to_f64(np.array([bits16], dtype=np.uint16))[0])
 
 
 # ---------------------------------------------------------------- rounding ---
@@ -447,3 +443,19 @@ def test_svdquant_beats_plain_w4a4_on_outlier_inputs():
         errs[r] = np.linalg.norm(y - ref) / np.linalg.norm(ref)
     assert errs[0] < errs["plain"]
     assert errs[16] < errs[0] and errs[32] < errs[16]
+
+
+def test_weight_scale_is_one_rounding_at_a_constructed_near_tie():
+    """A/7 just above a bf16 midpoint whose lower neighbour is even: one rounding
+    from float64 goes up; a detour through float32 would land on the tie and go
+    down to the even neighbour."""
+    b_lo = O.bf16_to_f64(np.array([0x3C10], np.uint16))[0]      # even mantissa
+    b_hi = O.bf16_to_f64(np.array([0x3C11], np.uint16))[0]
+    tie = (b_lo + b_hi) / 2
+    target = tie * (1 + 2.0 ** -35)
+    R = np.zeros((1, 64))
+    R[0, 0] = 7.0 * target
+    R[0, 1] = -0.3 * target
+    q, s_bits = O.quantize_weight_groups(R)
+    assert Fraction(float(O.bf16_to_f64(s_bits)[0, 0])) == ex_bf16(Fraction(float(R[0, 0])) / 7)
+    assert int(s_bits[0, 0]) == 0x3C11

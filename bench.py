@@ -1,0 +1,238 @@
+"""Benchmark of the SVDQuant W4A4 + low-rank linear on one MI355X.
+
+One step = the whole per-inference hot path on one batch: call 1
+(svdq_quantize_act_lora_down: smoothing, int4 quantization, packing, fused
+lora_down) followed by call 2 (svdq_w4a4_gemm_lora_up: W4A4 GEMM, group dequant,
+fused lora_up, bias), back to back on one stream, inputs resident in HBM.
+Weight packing is offline (once per layer) and is not part of a step; its host
+time is reported separately.
+
+Workload (default): the MLP up-projection of a 12B-class DiT at 1024x1024,
+M = 4608 tokens (4096 image + 512 text), K = 3072, N = 12288, rank 32, group 64,
+synthetic seeded inputs (see the ``synthetic`` module).  Four input/output
+buffer sets (> 512 MB) rotate so the 256 MB last-level cache cannot hold the
+working set between steps.
+
+Prints ONE JSON line.  ``value`` = effective TOPS = 2*M*N*K / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective TOPS + % int8-MFMA peak, W4A4+LoRA linear M=4608 K=3072 N=12288"
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+NSETS = 4
+GEMM_SRC = os.path.join(ROOT, "bit_diffusion_transformer_svdq_amd", "csrc", "w4a4_gemm_lora_up.hip")
+QUANT_SRC = os.path.join(ROOT, "bit_diffusion_transformer_svdq_amd", "csrc", "quant_lora_down.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mlp_up.json")
+
+
+def gemm_min_bytes(M, N, K, r):
+    """Algorithmic HBM bytes of call 2 (every operand read once, Y written once)."""
+    return (M * K // 2 + N * K // 2 + 2 * M * K // 64 + 2 * N * K // 64 + 2 * M * r + 2 * N * r
+            + 2 * N + 2 * M * N)
+
+
+def quant_min_bytes(M, K, r):
+    """Algorithmic HBM bytes of call 1."""
+    return 2 * M * K + 4 * K + 2 * K * r + M * K // 2 + 2 * M * K // 64 + 2 * M * r
+
+
+def _sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def _bf(bits, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def measure_gpu(spec_name, M, steps, warmup, seed=0):
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K
+    import synthetic as S
+
+    spec = S.SPECS[spec_name].with_m(M) if M else S.SPECS[spec_name]
+    d = S.make_linear(spec)
+    Mv, Kd, N, r = spec.M, spec.K, spec.N, spec.r
+    # host-side packer (offline step of the product path)
+    absmax = np.abs(S.bf16_bits_to_f32(d["x"])).max(axis=0).astype(np.float32)
+    t0 = time.perf_counter()
+    lam = K.smooth_from_absmax(absmax, d["w"])
+    packed = K.pack_weights(d["w"], lam, r, seed=seed)
+    pack_s = time.perf_counter() - t0
+
+    dev = torch.device("cuda:0")
+    K.check_device(0)
+    sets = []
+    for _ in range(NSETS):
+        sets.append(dict(
+            x=_bf(d["x"], dev), lam=torch.from_numpy(lam).to(dev),
+            down=_bf(packed["lora_down"], dev), up=_bf(packed["lora_up"], dev),
+            wc=torch.from_numpy(packed["w_codes"]).to(dev), ws=_bf(packed["w_scales"], dev),
+            bias=_bf(d["bias"], dev),
+            codes=torch.empty((Mv, Kd // 2), dtype=torch.uint8, device=dev),
+            scales=torch.empty((Mv, Kd // 64), dtype=torch.bfloat16, device=dev),
+            la=torch.empty((Mv, r), dtype=torch.bfloat16, device=dev),
+            y=torch.empty((Mv, N), dtype=torch.bfloat16, device=dev)))
+    stream = torch.cuda.current_stream()
+
+    def step(s, evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        K.quantize_act_lora_down(s["x"], s["lam"], s["down"], out=(s["codes"], s["scales"], s["la"]),
+                                 stream=stream)
+        if evs is not None:
+            evs[1].record(stream)
+        K.w4a4_gemm_lora_up(s["codes"], s["scales"], s["wc"], s["ws"], s["la"], s["up"], s["bias"],
+                            out=s["y"], stream=stream)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for i in range(warmup):
+        step(sets[i % NSETS])
+    torch.cuda.synchronize()
+    # wall clock over exactly `steps` steps
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(sets[i % NSETS])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # per-kernel durations with HIP events on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(sets[i % NSETS], evs[i])
+    torch.cuda.synchronize()
+    tq = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    tg = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    return dict(spec=spec, M=Mv, K=Kd, N=N, r=r, wall_s=wall, steps=steps, t_quant=tq, t_gemm=tg,
+                pack_s=pack_s)
+
+
+def cpu_baseline(spec_name, rows=64):
+    """The oracle as written, single-threaded, on a bounded row sample of the workload."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    import synthetic as S
+    spec = S.SPECS[spec_name].with_m(max(rows, 256))
+    d = S.make_linear(spec)
+    lam = O.smooth_factors(O.activation_absmax(d["x"]), d["w"])
+    packed = O.pack_weights(d["w"], lam, spec.r)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        a = O.quantize_act_lora_down(d["x"][:rows], lam, packed["lora_down"])
+        O.linear_output(a["act_codes"], a["act_scales"], packed["w_codes"], packed["w_scales"],
+                        a["lora_act"], packed["lora_up"], d["bias"])
+        t = time.perf_counter() - t0
+    ops = 2.0 * rows * spec.N * spec.K
+    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {S.SPECS[spec_name].M} token rows of the same linear "
+                      f"(K={spec.K}, N={spec.N}, r={spec.r}), calls 1+2, numpy float64, "
+                      f"BLAS limited to 1 thread; {t:.1f} s"}
+
+
+def traffic_for(kernel_src_sha):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it matches this source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    info = json.load(open(TRAFFIC_FILE))
+    if info.get("kernel_source_sha") != kernel_src_sha:
+        return None
+    return info.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="mlp_up")
+    ap.add_argument("--m", type=int, default=0, help="override the token count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=64)
+    ap.add_argument("--extra", default="", help="write per-kernel details of extra shapes here (JSON)")
+    ap.add_argument("--extra-configs", default="attn_out,qkv,mlp_down")
+    ap.add_argument("--extra-m", default="64,256,1024")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the layer would shard along tokens with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    res = measure_gpu(args.config, args.m, args.steps, args.warmup)
+    M, Kd, N, r = res["M"], res["K"], res["N"], res["r"]
+    ops = 2.0 * M * N * Kd
+    ms = res["wall_s"] / res["steps"] * 1e3
+    tq, tg = float(np.mean(res["t_quant"])), float(np.mean(res["t_gemm"]))
+    gemm_tops = ops / tg / 1e12
+    quant_gbs = quant_min_bytes(M, Kd, r) / tq / 1e9
+    gemm_gbs = gemm_min_bytes(M, N, Kd, r) / tg / 1e9
+    out = {
+        "metric": METRIC,
+        "value": ops / (ms * 1e-3) / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded; shapes and value distributions of a 12B-class DiT linear)",
+        "config": {"workload": f"{res['spec'].name}: SVDQuant W4A4 linear M={M} K={Kd} N={N} rank={r} "
+                               f"group=64 (one 1024x1024 image: 4096 image + 512 text tokens)",
+                   "M": M, "K": Kd, "N": N, "rank": r, "group_size": 64, "buffer_sets": NSETS},
+        "pct_int8_peak": 100.0 * ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+        "roofline": {"bound": "mfma", "achieved": gemm_tops, "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                     "frac": gemm_tops / INT8_PEAK_TOPS,
+                     "traffic": traffic_for(_sha(GEMM_SRC)),
+                     "kernel": "svdq_w4a4_gemm_lora_up (w4a4_gemm_kernel)",
+                     "algorithmic_ops_per_launch": ops},
+        "kernels": {
+            "quantize_act_lora_down": {"us": tq * 1e6, "min_bytes": quant_min_bytes(M, Kd, r),
+                                       "GB/s": quant_gbs, "hbm_frac": quant_gbs / HBM_PEAK_GBS},
+            "w4a4_gemm_lora_up": {"us": tg * 1e6, "TOP/s": gemm_tops, "int8_frac": gemm_tops / INT8_PEAK_TOPS,
+                                  "min_bytes": gemm_min_bytes(M, N, Kd, r), "GB/s": gemm_gbs},
+        },
+        "offline_pack_s": res["pack_s"],
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_rows)
+
+    if args.extra:
+        extra = []
+        shapes = [(c, 0) for c in args.extra_configs.split(",") if c] + \
+                 [(args.config, int(m)) for m in args.extra_m.split(",") if m]
+        for name, m in shapes:
+            e = measure_gpu(name, m, 50, 5)
+            tq_, tg_ = float(np.mean(e["t_quant"])), float(np.mean(e["t_gemm"]))
+            ops_ = 2.0 * e["M"] * e["N"] * e["K"]
+            extra.append({"config": name, "M": e["M"], "K": e["K"], "N": e["N"], "r": e["r"],
+                          "us_quant": tq_ * 1e6, "us_gemm": tg_ * 1e6,
+                          "eff_TOPS": ops_ / (e["wall_s"] / e["steps"]) / 1e12,
+                          "gemm_TOPS": ops_ / tg_ / 1e12,
+                          "quant_GBs": quant_min_bytes(e["M"], e["K"], e["r"]) / tq_ / 1e9,
+                          "gemm_GBs": gemm_min_bytes(e["M"], e["N"], e["K"], e["r"]) / tg_ / 1e9})
+        with open(args.extra, "w") as f:
+            json.dump(extra, f, indent=1)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

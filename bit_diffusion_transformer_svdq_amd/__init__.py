@@ -1,0 +1,162 @@
+"""MI355X-native SVDQuant W4A4 + low-rank linear.
+
+Thin Python binding over libsvdq.so (C ABI: include/svdq.h).  Every step of
+the hot path runs in the library's HIP kernels; this module only marshals
+arguments: it checks dtypes and shapes, allocates outputs with torch on the
+current device, and passes raw pointers and the current HIP stream.
+
+Two online calls (the charmloop.ai news item on Nunchaku in Diffusers,
+paragraph on the 16-bit branch, names the two fusions):
+
+    codes, scales, lora_act = quantize_act_lora_down(x, smooth, lora_down)
+    y = w4a4_gemm_lora_up(codes, scales, w_codes, w_scales, lora_act, lora_up, bias)
+
+and the offline host packer (``smooth_from_absmax``, ``pack_weights``).
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from ._lib import SvdqError, check, lib
+
+__all__ = ["SvdqError", "lib", "check_device", "quantize_act_lora_down", "w4a4_gemm_lora_up",
+           "w4a4_group_acc_debug", "smooth_from_absmax", "pack_weights", "GROUP_SIZE"]
+
+GROUP_SIZE = 64
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, shape, name):
+    torch = _torch()
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.numel() and t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor")
+    del torch
+
+
+def check_device(device: int = 0) -> None:
+    """Raise unless HIP device ``device`` is a gfx950."""
+    check(lib().svdq_check_device(int(device)), "svdq_check_device")
+
+
+def quantize_act_lora_down(x, smooth, lora_down=None, out=None, stream=None):
+    """Call 1: smoothing + int4 quantization + packing + fused lora_down.
+
+    x bf16 [M, K], smooth fp32 [K], lora_down bf16 [r, K] or None (r = 0).
+    Returns (act_codes uint8 [M, K/2], act_scales bf16 [M, K/64], lora_act bf16 [M, r]).
+    """
+    torch = _torch()
+    M, K = x.shape
+    r = 0 if lora_down is None else lora_down.shape[0]
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(smooth, torch.float32, (K,), "smooth")
+    if r:
+        _need(lora_down, torch.bfloat16, (r, K), "lora_down")
+    dev = x.device
+    if out is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((M, K // GROUP_SIZE), dtype=torch.bfloat16, device=dev)
+        lora_act = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+    else:
+        codes, scales, lora_act = out
+    st = lib().svdq_quantize_act_lora_down(
+        _ptr(x), _ptr(smooth), _ptr(lora_down) if r else None, M, K, r, GROUP_SIZE,
+        _ptr(codes), _ptr(scales), _ptr(lora_act) if r else None, _stream(stream))
+    check(st, "svdq_quantize_act_lora_down")
+    return codes, scales, lora_act
+
+
+def w4a4_gemm_lora_up(act_codes, act_scales, w_codes, w_scales, lora_act=None, lora_up=None,
+                      bias=None, out=None, stream=None):
+    """Call 2: W4A4 GEMM + per-group dequant + fused lora_up + bias -> Y bf16 [M, N]."""
+    torch = _torch()
+    M = act_codes.shape[0]
+    K = act_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    r = 0 if lora_up is None else lora_up.shape[1]
+    _need(act_codes, torch.uint8, (M, K // 2), "act_codes")
+    _need(act_scales, torch.bfloat16, (M, K // GROUP_SIZE), "act_scales")
+    _need(w_codes, torch.uint8, (N, K // 2), "w_codes")
+    _need(w_scales, torch.bfloat16, (N, K // GROUP_SIZE), "w_scales")
+    if r:
+        _need(lora_act, torch.bfloat16, (M, r), "lora_act")
+        _need(lora_up, torch.bfloat16, (N, r), "lora_up")
+    if bias is not None:
+        _need(bias, torch.bfloat16, (N,), "bias")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=act_codes.device) if out is None else out
+    st = lib().svdq_w4a4_gemm_lora_up(
+        _ptr(act_codes), _ptr(act_scales), _ptr(w_codes), _ptr(w_scales),
+        _ptr(lora_act) if r else None, _ptr(lora_up) if r else None, _ptr(bias),
+        M, N, K, r, GROUP_SIZE, _ptr(y), _stream(stream))
+    check(st, "svdq_w4a4_gemm_lora_up")
+    return y
+
+
+def w4a4_group_acc_debug(act_codes, w_codes, stream=None):
+    """Test hook: the exact int32 group accumulators [M, N, K/64] of call 2's main loop."""
+    torch = _torch()
+    M = act_codes.shape[0]
+    K = act_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    _need(act_codes, torch.uint8, (M, K // 2), "act_codes")
+    _need(w_codes, torch.uint8, (N, K // 2), "w_codes")
+    acc = torch.empty((M, N, K // GROUP_SIZE), dtype=torch.int32, device=act_codes.device)
+    st = lib().svdq_w4a4_group_acc_debug(_ptr(act_codes), _ptr(w_codes), M, N, K, GROUP_SIZE,
+                                         _ptr(acc), _stream(stream))
+    check(st, "svdq_w4a4_group_acc_debug")
+    return acc
+
+
+def smooth_from_absmax(x_absmax: np.ndarray, w_bf16: np.ndarray) -> np.ndarray:
+    """Host packer step 1: lambda (fp32 [K]) from activation absmax fp32 [K] and W bf16 bits [N, K]."""
+    a = np.ascontiguousarray(x_absmax, dtype=np.float32)
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    N, K = w.shape
+    out = np.empty(K, dtype=np.float32)
+    st = lib().svdq_smooth_from_absmax(a.ctypes.data_as(ctypes.c_void_p), w.ctypes.data_as(ctypes.c_void_p),
+                                       N, K, out.ctypes.data_as(ctypes.c_void_p))
+    check(st, "svdq_smooth_from_absmax")
+    return out
+
+
+def pack_weights(w_bf16: np.ndarray, smooth: np.ndarray, rank: int, seed: int = 0) -> dict:
+    """Host packer step 2: W bf16 bits [N, K] + lambda -> packed residual and low-rank factors.
+
+    Returns numpy arrays: w_codes uint8 [N, K/2], w_scales uint16 (bf16 bits) [N, K/64],
+    lora_down uint16 [r, K], lora_up uint16 [N, r].
+    """
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    lam = np.ascontiguousarray(smooth, dtype=np.float32)
+    N, K = w.shape
+    codes = np.empty((N, K // 2), dtype=np.uint8)
+    scales = np.empty((N, K // GROUP_SIZE), dtype=np.uint16)
+    down = np.empty((rank, K), dtype=np.uint16)
+    up = np.empty((N, rank), dtype=np.uint16)
+    vp = ctypes.c_void_p
+    st = lib().svdq_pack_weights(
+        w.ctypes.data_as(vp), lam.ctypes.data_as(vp), N, K, int(rank), GROUP_SIZE, int(seed),
+        codes.ctypes.data_as(vp), scales.ctypes.data_as(vp),
+        down.ctypes.data_as(vp) if rank else None, up.ctypes.data_as(vp) if rank else None)
+    check(st, "svdq_pack_weights")
+    return {"w_codes": codes, "w_scales": scales, "lora_down": down, "lora_up": up}

@@ -1,0 +1,209 @@
+// C ABI of libsvdq (declarations and the contract: include/svdq.h).
+//
+// Every entry point validates its arguments before touching the HIP runtime,
+// so shape and pointer errors are reported synchronously and also on a machine
+// without a GPU.  The device check mirrors the load-time GPU validation of the
+// integration described on mind-verse.de ("Effiziente Optimierung von
+// Diffusionsmodellen durch Nunchaku 4-Bit-Quantisierung", section
+// "Hardware-Unterstützung"): unsupported GPU generations are refused.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "svdq.h"
+#include "svdq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = {0};
+
+svdq_status fail(svdq_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+svdq_status ok() {
+  g_err[0] = 0;
+  return SVDQ_STATUS_SUCCESS;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, otherwise 1 + svdq_status
+std::atomic<int> g_dev_state[kMaxDevices];
+
+svdq_status check_device_uncached(int device) {
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return fail(SVDQ_STATUS_NO_DEVICE, "no HIP device visible (%s)", hipGetErrorString(e));
+  }
+  if (device < 0 || device >= count)
+    return fail(SVDQ_STATUS_INVALID_VALUE, "device index %d out of range [0, %d)", device, count);
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) return fail(SVDQ_STATUS_HIP_ERROR, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(SVDQ_STATUS_ARCH_MISMATCH, "device %d is %s; this library is built for gfx950 (MI355X)",
+                device, prop.gcnArchName);
+  return ok();
+}
+
+svdq_status check_current_device() {
+  int dev = 0;
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return fail(SVDQ_STATUS_NO_DEVICE, "no HIP device visible");
+  }
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SVDQ_STATUS_HIP_ERROR, "hipGetDevice: %s", hipGetErrorString(e));
+  return svdq_check_device(dev);
+}
+
+bool rank_supported(int64_t r) { return r >= 0 && r <= 128 && r % 16 == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* svdq_status_string(svdq_status s) {
+  switch (s) {
+    case SVDQ_STATUS_SUCCESS: return "SVDQ_STATUS_SUCCESS";
+    case SVDQ_STATUS_INVALID_VALUE: return "SVDQ_STATUS_INVALID_VALUE";
+    case SVDQ_STATUS_NOT_SUPPORTED: return "SVDQ_STATUS_NOT_SUPPORTED";
+    case SVDQ_STATUS_ARCH_MISMATCH: return "SVDQ_STATUS_ARCH_MISMATCH";
+    case SVDQ_STATUS_NO_DEVICE: return "SVDQ_STATUS_NO_DEVICE";
+    case SVDQ_STATUS_HIP_ERROR: return "SVDQ_STATUS_HIP_ERROR";
+    case SVDQ_STATUS_INTERNAL: return "SVDQ_STATUS_INTERNAL";
+  }
+  return "SVDQ_STATUS_UNKNOWN";
+}
+
+const char* svdq_last_error(void) { return g_err; }
+
+int svdq_version(void) { return 100; }
+
+svdq_status svdq_check_device(int device) {
+  if (device < 0) return fail(SVDQ_STATUS_INVALID_VALUE, "negative device index %d", device);
+  if (device < kMaxDevices) {
+    const int st = g_dev_state[device].load(std::memory_order_acquire);
+    if (st != 0) {
+      const svdq_status s = static_cast<svdq_status>(st - 1);
+      if (s == SVDQ_STATUS_SUCCESS) return ok();
+      return fail(s, "device %d failed the gfx950 check earlier", device);
+    }
+  }
+  const svdq_status s = check_device_uncached(device);
+  if (device < kMaxDevices && (s == SVDQ_STATUS_SUCCESS || s == SVDQ_STATUS_ARCH_MISMATCH))
+    g_dev_state[device].store(1 + static_cast<int>(s), std::memory_order_release);
+  return s;
+}
+
+svdq_status svdq_quantize_act_lora_down(const void* x, const float* smooth, const void* lora_down,
+                                        int64_t M, int64_t K, int64_t r, int64_t group_size,
+                                        void* act_codes, void* act_scales, void* lora_act,
+                                        void* stream) {
+  if (M < 0 || K <= 0 || r < 0 || group_size <= 0)
+    return fail(SVDQ_STATUS_INVALID_VALUE, "bad dims M=%lld K=%lld r=%lld group_size=%lld",
+                (long long)M, (long long)K, (long long)r, (long long)group_size);
+  if (group_size != 64) return fail(SVDQ_STATUS_NOT_SUPPORTED, "group_size %lld (only 64)", (long long)group_size);
+  if (K % 64 != 0) return fail(SVDQ_STATUS_NOT_SUPPORTED, "K=%lld is not a multiple of 64", (long long)K);
+  if (!rank_supported(r)) return fail(SVDQ_STATUS_NOT_SUPPORTED, "rank %lld (need 0..128, multiple of 16)", (long long)r);
+  if (M > (1ll << 24) || K > (1ll << 20) || M * K > (1ll << 40))
+    return fail(SVDQ_STATUS_NOT_SUPPORTED, "problem too large M=%lld K=%lld", (long long)M, (long long)K);
+  if (!x || !smooth || !act_codes || !act_scales)
+    return fail(SVDQ_STATUS_INVALID_VALUE, "null x/smooth/act_codes/act_scales");
+  if (r > 0 && (!lora_down || !lora_act))
+    return fail(SVDQ_STATUS_INVALID_VALUE, "r=%lld needs lora_down and lora_act", (long long)r);
+  if (!aligned16(x) || !aligned16(smooth) || !aligned16(act_codes) || !aligned16(act_scales) ||
+      (r > 0 && (!aligned16(lora_down) || !aligned16(lora_act))))
+    return fail(SVDQ_STATUS_INVALID_VALUE, "device pointers must be 16-byte aligned");
+  if (M == 0) return ok();
+  svdq_status s = check_current_device();
+  if (s != SVDQ_STATUS_SUCCESS) return s;
+  hipError_t e = svdq::launch_quant_lora_down(
+      static_cast<const uint16_t*>(x), smooth, static_cast<const uint16_t*>(lora_down), M, K, r,
+      static_cast<uint8_t*>(act_codes), static_cast<uint16_t*>(act_scales),
+      static_cast<uint16_t*>(lora_act), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SVDQ_STATUS_HIP_ERROR, "quantize launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+static svdq_status validate_gemm(const void* act_codes, const void* w_codes, int64_t M, int64_t N,
+                                 int64_t K, int64_t r, int64_t group_size) {
+  if (M < 0 || N <= 0 || K <= 0 || r < 0 || group_size <= 0)
+    return fail(SVDQ_STATUS_INVALID_VALUE, "bad dims M=%lld N=%lld K=%lld r=%lld group_size=%lld",
+                (long long)M, (long long)N, (long long)K, (long long)r, (long long)group_size);
+  if (group_size != 64) return fail(SVDQ_STATUS_NOT_SUPPORTED, "group_size %lld (only 64)", (long long)group_size);
+  if (K % 64 != 0) return fail(SVDQ_STATUS_NOT_SUPPORTED, "K=%lld is not a multiple of 64", (long long)K);
+  if (N % 64 != 0) return fail(SVDQ_STATUS_NOT_SUPPORTED, "N=%lld is not a multiple of 64", (long long)N);
+  if (!rank_supported(r)) return fail(SVDQ_STATUS_NOT_SUPPORTED, "rank %lld (need 0..128, multiple of 16)", (long long)r);
+  if (M > (1ll << 24) || N > (1ll << 20) || K > (1ll << 20))
+    return fail(SVDQ_STATUS_NOT_SUPPORTED, "problem too large M=%lld N=%lld K=%lld", (long long)M,
+                (long long)N, (long long)K);
+  if (!act_codes || !w_codes) return fail(SVDQ_STATUS_INVALID_VALUE, "null act_codes/w_codes");
+  if (!aligned16(act_codes) || !aligned16(w_codes))
+    return fail(SVDQ_STATUS_INVALID_VALUE, "device pointers must be 16-byte aligned");
+  return SVDQ_STATUS_SUCCESS;
+}
+
+svdq_status svdq_w4a4_gemm_lora_up(const void* act_codes, const void* act_scales,
+                                   const void* w_codes, const void* w_scales,
+                                   const void* lora_act, const void* lora_up, const void* bias,
+                                   int64_t M, int64_t N, int64_t K, int64_t r, int64_t group_size,
+                                   void* y, void* stream) {
+  svdq_status s = validate_gemm(act_codes, w_codes, M, N, K, r, group_size);
+  if (s != SVDQ_STATUS_SUCCESS) return s;
+  if (!act_scales || !w_scales || !y) return fail(SVDQ_STATUS_INVALID_VALUE, "null act_scales/w_scales/y");
+  if (r > 0 && (!lora_act || !lora_up))
+    return fail(SVDQ_STATUS_INVALID_VALUE, "r=%lld needs lora_act and lora_up", (long long)r);
+  if (!aligned16(act_scales) || !aligned16(w_scales) || !aligned16(y) ||
+      (bias && !aligned16(bias)) || (r > 0 && (!aligned16(lora_act) || !aligned16(lora_up))))
+    return fail(SVDQ_STATUS_INVALID_VALUE, "device pointers must be 16-byte aligned");
+  if (M == 0) return ok();
+  s = check_current_device();
+  if (s != SVDQ_STATUS_SUCCESS) return s;
+  hipError_t e = svdq::launch_w4a4_gemm_lora_up(
+      static_cast<const uint8_t*>(act_codes), static_cast<const uint16_t*>(act_scales),
+      static_cast<const uint8_t*>(w_codes), static_cast<const uint16_t*>(w_scales),
+      static_cast<const uint16_t*>(lora_act), static_cast<const uint16_t*>(lora_up),
+      static_cast<const uint16_t*>(bias), M, N, K, r, static_cast<uint16_t*>(y), nullptr,
+      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SVDQ_STATUS_HIP_ERROR, "gemm launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+svdq_status svdq_w4a4_group_acc_debug(const void* act_codes, const void* w_codes, int64_t M,
+                                      int64_t N, int64_t K, int64_t group_size, int32_t* acc,
+                                      void* stream) {
+  svdq_status s = validate_gemm(act_codes, w_codes, M, N, K, 0, group_size);
+  if (s != SVDQ_STATUS_SUCCESS) return s;
+  if (!acc) return fail(SVDQ_STATUS_INVALID_VALUE, "null acc");
+  if (M * N * (K / 64) > (1ll << 31)) return fail(SVDQ_STATUS_NOT_SUPPORTED, "accumulator dump too large");
+  if (M == 0) return ok();
+  s = check_current_device();
+  if (s != SVDQ_STATUS_SUCCESS) return s;
+  hipError_t e = svdq::launch_w4a4_gemm_lora_up(
+      static_cast<const uint8_t*>(act_codes), nullptr, static_cast<const uint8_t*>(w_codes), nullptr,
+      nullptr, nullptr, nullptr, M, N, K, 0, nullptr, acc, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SVDQ_STATUS_HIP_ERROR, "gemm debug launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"
+
+// host packer entry points live in packer.cpp; they use these helpers for errors
+svdq_status svdq_internal_fail(svdq_status s, const char* msg) { return fail(s, "%s", msg); }
+svdq_status svdq_internal_ok() { return ok(); }

@@ -1,0 +1,355 @@
+// Host-side weight packer of libsvdq (CPU only): smoothing vector, rank-r
+// truncated SVD of the smoothed weight, residual, per-group int4 quantization
+// and nibble packing.  Contract: include/svdq.h.
+//
+// Method (mind-verse.de, "Effiziente Optimierung von Diffusionsmodellen durch
+// Nunchaku 4-Bit-Quantisierung", section "Nunchaku und SVDQuant"; ai2day.live,
+// "AI-Bildmodelle auf normalen GPUs ausführen", section "Was ist Nunchaku Lite
+// und was macht es genau?"): activation outliers are moved into the weights
+// (W' = W diag(lambda)), the dominant part of W' is kept as a 16-bit rank-r
+// product, the remainder is quantized to 4 bits.  The rank (32 in the example
+// config) and the group size come from the quantization config shown in the
+// section "Native Ladefunktion in Diffusers".
+//
+// The SVD is randomized subspace iteration (Halko, Martinsson, Tropp, "Finding
+// structure with randomness", SIAM Review 2011, algorithm 4.4) with
+// oversampling, followed by one-sided Jacobi (Hestenes) on the small projected
+// matrix.  No LAPACK.  Every output element is produced by one thread in a fixed
+// order, so results do not depend on the thread count.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <numeric>
+#include <thread>
+#include <vector>
+
+#include "svdq.h"
+
+svdq_status svdq_internal_fail(svdq_status s, const char* msg);
+svdq_status svdq_internal_ok();
+
+namespace {
+
+double bf16_to_double(uint16_t h) {
+  const uint32_t u = static_cast<uint32_t>(h) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return static_cast<double>(f);
+}
+
+// bfloat16 nearest-even of a finite double, rounded once from the double value.
+uint16_t double_to_bf16(double v) {
+  uint64_t b;
+  std::memcpy(&b, &v, 8);
+  const uint16_t sign = static_cast<uint16_t>((b >> 63) << 15);
+  const double a = std::fabs(v);
+  if (a == 0.0) return sign;
+  if (a < 0x1p-126) {  // bf16 subnormal range: quantum 2^-133 (128 -> smallest normal)
+    return sign | static_cast<uint16_t>(std::nearbyint(a * 0x1p133));
+  }
+  const uint64_t ab = b & 0x7FFFFFFFFFFFFFFFull;
+  int e = static_cast<int>(ab >> 52);
+  const uint64_t m = (ab & ((1ull << 52) - 1)) | (1ull << 52);
+  uint64_t q = m >> 45;
+  const uint64_t rem = m & ((1ull << 45) - 1);
+  const uint64_t half = 1ull << 44;
+  if (rem > half || (rem == half && (q & 1))) ++q;
+  if (q == 256) {
+    q = 128;
+    ++e;
+  }
+  const int eb = e - 1023 + 127;
+  if (eb >= 255) return sign | 0x7F80;
+  return sign | static_cast<uint16_t>(eb << 7) | static_cast<uint16_t>(q & 0x7F);
+}
+
+int thread_count() {
+  int t = static_cast<int>(std::thread::hardware_concurrency());
+  if (const char* env = std::getenv("SVDQ_PACK_THREADS")) t = std::atoi(env);
+  return std::max(1, std::min(t, 64));
+}
+
+template <class F>
+void parallel_for(int64_t n, F f) {
+  const int T = static_cast<int>(std::min<int64_t>(thread_count(), n));
+  if (T <= 1) {
+    f(int64_t{0}, n);
+    return;
+  }
+  std::vector<std::thread> th;
+  th.reserve(T);
+  for (int t = 0; t < T; ++t) {
+    const int64_t a = n * t / T, b = n * (t + 1) / T;
+    th.emplace_back([=] { f(a, b); });
+  }
+  for (auto& x : th) x.join();
+}
+
+uint64_t splitmix64(uint64_t x) {
+  x += 0x9E3779B97F4A7C15ull;
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  return x ^ (x >> 31);
+}
+
+// standard normal sample number `idx` of stream `seed` (Box-Muller on two hashed uniforms)
+double gauss(uint64_t seed, uint64_t idx) {
+  const uint64_t h1 = splitmix64(seed * 0x632BE59BD9B4E019ull + 2 * idx);
+  const uint64_t h2 = splitmix64(seed * 0x632BE59BD9B4E019ull + 2 * idx + 1);
+  const double u1 = (static_cast<double>(h1 >> 11) + 0.5) * 0x1p-53;
+  const double u2 = static_cast<double>(h2 >> 11) * 0x1p-53;
+  return std::sqrt(-2.0 * std::log(u1)) * std::cos(6.283185307179586 * u2);
+}
+
+// Y[n, :] = A[n, :] @ X  (A: N x K row-major, X: K x l row-major, Y: N x l)
+void mul_a(const std::vector<double>& A, int64_t N, int64_t K, const std::vector<double>& X, int l,
+           std::vector<double>& Y) {
+  Y.assign(static_cast<size_t>(N) * l, 0.0);
+  parallel_for(N, [&](int64_t n0, int64_t n1) {
+    std::vector<double> acc(l);
+    for (int64_t n = n0; n < n1; ++n) {
+      std::fill(acc.begin(), acc.end(), 0.0);
+      const double* a = &A[static_cast<size_t>(n) * K];
+      for (int64_t k = 0; k < K; ++k) {
+        const double av = a[k];
+        const double* x = &X[static_cast<size_t>(k) * l];
+        for (int c = 0; c < l; ++c) acc[c] += av * x[c];
+      }
+      std::copy(acc.begin(), acc.end(), &Y[static_cast<size_t>(n) * l]);
+    }
+  });
+}
+
+// Z[k, :] = sum_n A[n, k] * Q[n, :]   (Z = A^T Q, K x l)
+void mul_at(const std::vector<double>& A, int64_t N, int64_t K, const std::vector<double>& Q, int l,
+            std::vector<double>& Z) {
+  Z.assign(static_cast<size_t>(K) * l, 0.0);
+  constexpr int64_t kBlock = 64;
+  const int64_t nblk = (K + kBlock - 1) / kBlock;
+  parallel_for(nblk, [&](int64_t b0, int64_t b1) {
+    for (int64_t b = b0; b < b1; ++b) {
+      const int64_t k0 = b * kBlock, k1 = std::min(K, k0 + kBlock);
+      for (int64_t n = 0; n < N; ++n) {
+        const double* a = &A[static_cast<size_t>(n) * K];
+        const double* q = &Q[static_cast<size_t>(n) * l];
+        for (int64_t k = k0; k < k1; ++k) {
+          const double av = a[k];
+          double* z = &Z[static_cast<size_t>(k) * l];
+          for (int c = 0; c < l; ++c) z[c] += av * q[c];
+        }
+      }
+    }
+  });
+}
+
+// Orthonormalise the columns of a rows x l row-major matrix (classical
+// Gram-Schmidt applied twice).  Columns that vanish are set to zero.
+void orthonormalize(std::vector<double>& Y, int64_t rows, int l) {
+  std::vector<double> col(rows), proj(l);
+  for (int c = 0; c < l; ++c) {
+    for (int64_t n = 0; n < rows; ++n) col[n] = Y[static_cast<size_t>(n) * l + c];
+    double norm0 = 0.0;
+    for (int64_t n = 0; n < rows; ++n) norm0 += col[n] * col[n];
+    norm0 = std::sqrt(norm0);
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int j = 0; j < c; ++j) {
+        double d = 0.0;
+        for (int64_t n = 0; n < rows; ++n) d += Y[static_cast<size_t>(n) * l + j] * col[n];
+        proj[j] = d;
+      }
+      for (int j = 0; j < c; ++j)
+        for (int64_t n = 0; n < rows; ++n) col[n] -= proj[j] * Y[static_cast<size_t>(n) * l + j];
+    }
+    double norm = 0.0;
+    for (int64_t n = 0; n < rows; ++n) norm += col[n] * col[n];
+    norm = std::sqrt(norm);
+    const double inv = (norm > 1e-13 * norm0 && norm > 0.0) ? 1.0 / norm : 0.0;
+    for (int64_t n = 0; n < rows; ++n) Y[static_cast<size_t>(n) * l + c] = col[n] * inv;
+  }
+}
+
+// One-sided Jacobi on the columns of Mt (l columns of length K, stored
+// column-major as Mt[c * K + k]); accumulates the rotations in J (l x l,
+// row-major, J[j * l + c]).
+void one_sided_jacobi(std::vector<double>& Mt, int64_t K, int l, std::vector<double>& J) {
+  J.assign(static_cast<size_t>(l) * l, 0.0);
+  for (int c = 0; c < l; ++c) J[static_cast<size_t>(c) * l + c] = 1.0;
+  for (int sweep = 0; sweep < 60; ++sweep) {
+    bool rotated = false;
+    for (int p = 0; p < l - 1; ++p) {
+      for (int q = p + 1; q < l; ++q) {
+        double* x = &Mt[static_cast<size_t>(p) * K];
+        double* y = &Mt[static_cast<size_t>(q) * K];
+        double alpha = 0.0, beta = 0.0, gamma = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+          alpha += x[k] * x[k];
+          beta += y[k] * y[k];
+          gamma += x[k] * y[k];
+        }
+        if (gamma == 0.0 || std::fabs(gamma) <= 1e-15 * std::sqrt(alpha * beta)) continue;
+        rotated = true;
+        const double zeta = (beta - alpha) / (2.0 * gamma);
+        const double t = (zeta >= 0 ? 1.0 : -1.0) / (std::fabs(zeta) + std::sqrt(1.0 + zeta * zeta));
+        const double cs = 1.0 / std::sqrt(1.0 + t * t);
+        const double sn = cs * t;
+        for (int64_t k = 0; k < K; ++k) {
+          const double xv = x[k], yv = y[k];
+          x[k] = cs * xv - sn * yv;
+          y[k] = sn * xv + cs * yv;
+        }
+        for (int j = 0; j < l; ++j) {
+          double* jr = &J[static_cast<size_t>(j) * l];
+          const double a = jr[p], b = jr[q];
+          jr[p] = cs * a - sn * b;
+          jr[q] = sn * a + cs * b;
+        }
+      }
+    }
+    if (!rotated) break;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+svdq_status svdq_smooth_from_absmax(const float* x_absmax, const uint16_t* w, int64_t N, int64_t K,
+                                    float* smooth) {
+  if (!x_absmax || !w || !smooth) return svdq_internal_fail(SVDQ_STATUS_INVALID_VALUE, "null pointer");
+  if (N <= 0 || K <= 0) return svdq_internal_fail(SVDQ_STATUS_INVALID_VALUE, "N and K must be positive");
+  const double eps = 1e-5;
+  std::vector<double> wmax(static_cast<size_t>(K), 0.0);
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k)
+      wmax[k] = std::max(wmax[k], std::fabs(bf16_to_double(w[static_cast<size_t>(n) * K + k])));
+  for (int64_t k = 0; k < K; ++k) {
+    const double a = std::max(static_cast<double>(x_absmax[k]), eps);
+    const double b = std::max(wmax[k], eps);
+    smooth[k] = static_cast<float>(std::sqrt(a / b));
+  }
+  return svdq_internal_ok();
+}
+
+svdq_status svdq_pack_weights(const uint16_t* w, const float* smooth, int64_t N, int64_t K, int64_t r,
+                              int64_t group_size, uint64_t seed, uint8_t* w_codes, uint16_t* w_scales,
+                              uint16_t* lora_down, uint16_t* lora_up) {
+  if (!w || !smooth || !w_codes || !w_scales) return svdq_internal_fail(SVDQ_STATUS_INVALID_VALUE, "null pointer");
+  if (N <= 0 || K <= 0 || r < 0 || group_size <= 0)
+    return svdq_internal_fail(SVDQ_STATUS_INVALID_VALUE, "bad dimensions");
+  if (group_size != 64) return svdq_internal_fail(SVDQ_STATUS_NOT_SUPPORTED, "group_size must be 64");
+  if (K % 64 != 0) return svdq_internal_fail(SVDQ_STATUS_NOT_SUPPORTED, "K must be a multiple of 64");
+  if (r > 128 || r > std::min(N, K)) return svdq_internal_fail(SVDQ_STATUS_NOT_SUPPORTED, "rank too large");
+  if (r > 0 && (!lora_down || !lora_up))
+    return svdq_internal_fail(SVDQ_STATUS_INVALID_VALUE, "r > 0 needs lora_down and lora_up");
+
+  // W' = W diag(lambda), exact in double (8 + 24 significant bits)
+  std::vector<double> A(static_cast<size_t>(N) * K);
+  parallel_for(N, [&](int64_t n0, int64_t n1) {
+    for (int64_t n = n0; n < n1; ++n)
+      for (int64_t k = 0; k < K; ++k)
+        A[static_cast<size_t>(n) * K + k] =
+            bf16_to_double(w[static_cast<size_t>(n) * K + k]) * static_cast<double>(smooth[k]);
+  });
+
+  std::vector<double> up_d(static_cast<size_t>(N) * r), down_d(static_cast<size_t>(r) * K);
+  if (r > 0) {
+    const int l = static_cast<int>(std::min<int64_t>(r + 16, std::min(N, K)));
+    const int power_iters = 8;  // residual within ~1e-4 of Eckart-Young even on a flat spectrum
+    std::vector<double> Omega(static_cast<size_t>(K) * l), Y, Z;
+    parallel_for(K, [&](int64_t k0, int64_t k1) {
+      for (int64_t k = k0; k < k1; ++k)
+        for (int c = 0; c < l; ++c)
+          Omega[static_cast<size_t>(k) * l + c] = gauss(seed, static_cast<uint64_t>(k) * l + c);
+    });
+    mul_a(A, N, K, Omega, l, Y);
+    orthonormalize(Y, N, l);
+    for (int it = 0; it < power_iters; ++it) {
+      mul_at(A, N, K, Y, l, Z);
+      orthonormalize(Z, K, l);
+      mul_a(A, N, K, Z, l, Y);
+      orthonormalize(Y, N, l);
+    }
+    // B^T = A^T Q (K x l); SVD of B^T by one-sided Jacobi: B^T J = V S
+    mul_at(A, N, K, Y, l, Z);
+    std::vector<double> Mt(static_cast<size_t>(l) * K);
+    for (int64_t k = 0; k < K; ++k)
+      for (int c = 0; c < l; ++c) Mt[static_cast<size_t>(c) * K + k] = Z[static_cast<size_t>(k) * l + c];
+    std::vector<double> J;
+    one_sided_jacobi(Mt, K, l, J);
+    std::vector<double> sigma(l);
+    for (int c = 0; c < l; ++c) {
+      double s = 0.0;
+      for (int64_t k = 0; k < K; ++k) s += Mt[static_cast<size_t>(c) * K + k] * Mt[static_cast<size_t>(c) * K + k];
+      sigma[c] = std::sqrt(s);
+    }
+    std::vector<int> order(l);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return sigma[a] > sigma[b]; });
+    // A ~= (Q J) S V^T: lora_up = (Q J)[:, c] sqrt(s_c); lora_down = sqrt(s_c) V[:, c]^T
+    for (int i = 0; i < r; ++i) {
+      const int c = order[i];
+      const double s = sigma[c];
+      const double root = std::sqrt(s);
+      const double inv = s > 0 ? 1.0 / s : 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const double v = Mt[static_cast<size_t>(c) * K + k] * inv;
+        const uint16_t h = double_to_bf16(root * v);
+        lora_down[static_cast<size_t>(i) * K + k] = h;
+        down_d[static_cast<size_t>(i) * K + k] = bf16_to_double(h);
+      }
+    }
+    parallel_for(N, [&](int64_t n0, int64_t n1) {
+      for (int64_t n = n0; n < n1; ++n) {
+        const double* q = &Y[static_cast<size_t>(n) * l];
+        for (int i = 0; i < r; ++i) {
+          const int c = order[i];
+          double u = 0.0;
+          for (int j = 0; j < l; ++j) u += q[j] * J[static_cast<size_t>(j) * l + c];
+          const uint16_t h = double_to_bf16(u * std::sqrt(sigma[c]));
+          lora_up[static_cast<size_t>(n) * r + i] = h;
+          up_d[static_cast<size_t>(n) * r + i] = bf16_to_double(h);
+        }
+      }
+    });
+  }
+
+  // residual against the rounded factors, then per-group symmetric int4
+  const int64_t G = K / 64;
+  parallel_for(N, [&](int64_t n0, int64_t n1) {
+    std::vector<double> R(static_cast<size_t>(K));
+    for (int64_t n = n0; n < n1; ++n) {
+      const double* a = &A[static_cast<size_t>(n) * K];
+      for (int64_t k = 0; k < K; ++k) {
+        double lowrank = 0.0;
+        for (int64_t i = 0; i < r; ++i)
+          lowrank += up_d[static_cast<size_t>(n) * r + i] * down_d[static_cast<size_t>(i) * K + k];
+        R[k] = a[k] - lowrank;
+      }
+      for (int64_t g = 0; g < G; ++g) {
+        const double* seg = &R[static_cast<size_t>(g) * 64];
+        double amax = 0.0;
+        for (int e = 0; e < 64; ++e) amax = std::max(amax, std::fabs(seg[e]));
+        const uint16_t sb = double_to_bf16(amax / 7.0);
+        w_scales[static_cast<size_t>(n) * G + g] = sb;
+        const double s = bf16_to_double(sb);
+        uint8_t* out = &w_codes[static_cast<size_t>(n) * (K / 2) + g * 32];
+        for (int e = 0; e < 64; e += 2) {
+          int q0 = 0, q1 = 0;
+          if (s > 0) {
+            q0 = static_cast<int>(std::nearbyint(seg[e] / s));
+            q1 = static_cast<int>(std::nearbyint(seg[e + 1] / s));
+            q0 = std::max(-7, std::min(7, q0));
+            q1 = std::max(-7, std::min(7, q1));
+          }
+          out[e / 2] = static_cast<uint8_t>((q0 & 0xF) | ((q1 & 0xF) << 4));
+        }
+      }
+    }
+  });
+  return svdq_internal_ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,193 @@
+/*
+ * svdq.h - C ABI of libsvdq: the SVDQuant W4A4 + low-rank linear on MI355X (gfx950).
+ *
+ * The layer (mind-verse.de, "Effiziente Optimierung von Diffusionsmodellen durch
+ * Nunchaku 4-Bit-Quantisierung", section "Nunchaku und SVDQuant"): activation
+ * outliers are moved into the weights by a per-input-channel smoothing vector
+ * lambda, the hardest part of each smoothed weight matrix W' = W diag(lambda) is
+ * kept in a 16-bit rank-r branch (L1 [K,r], L2 [r,N]), and the residual R runs as
+ * 4-bit weights against 4-bit activations:
+ *
+ *     Y = X W^T + b  ~=  dequant(Q(X_hat) . Q(R)^T) + (X_hat L1) L2 + b,
+ *     X_hat = X diag(lambda)^-1.
+ *
+ * The online work is split into the two fused calls named by the charmloop.ai
+ * news item on Nunchaku in Diffusers (paragraph on the 16-bit branch): the
+ * low-rank down-projection runs inside the activation-quantization kernel, the
+ * low-rank up-projection inside the 4-bit compute kernel.  Composed, they are a
+ * drop-in for an nn.Linear(K, N) forward (mind-verse.de, section "Native
+ * Ladefunktion in Diffusers": the module tree stays that of the dense model).
+ *
+ * Conventions common to every call
+ *  - Layouts follow nn.Linear: X [M,K], W [N,K], Y [M,N]; lora_down = L1^T [r,K];
+ *    lora_up = L2^T [N,r].  Every array is dense, row-major, no padding.
+ *  - bf16 arrays are passed as raw 16-bit patterns (IEEE bfloat16).
+ *  - int4 codes: two per byte along K, element 2i in the low nibble of byte i,
+ *    two's complement, values in [-7, 7].  Codes are [rows, K/2] bytes.
+ *  - Scales: bf16 [rows, K/group_size], one per row per group of group_size
+ *    consecutive k.  Only group_size == 64 and int4 are supported (the int4
+ *    scheme's group size in the quantization config on mind-verse.de, section
+ *    "Native Ladefunktion in Diffusers").
+ *  - Ownership: the caller allocates and frees every buffer; the library never
+ *    allocates device memory and keeps no state besides a per-device
+ *    capability cache.  Device pointers must be 16-byte aligned.  Outputs must
+ *    not overlap inputs or each other.
+ *  - Errors: argument and shape errors are returned synchronously, before any
+ *    HIP call.  Kernels run asynchronously on `stream` (a hipStream_t; NULL is
+ *    the default stream) on the current HIP device; a launch failure returns
+ *    SVDQ_STATUS_HIP_ERROR, device faults surface at the caller's next
+ *    synchronisation.  svdq_last_error() gives a thread-local message for the
+ *    last failing call.  No C++ exception crosses this boundary.
+ *  - Calls on distinct streams may run concurrently from several threads.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum svdq_status {
+  SVDQ_STATUS_SUCCESS = 0,
+  SVDQ_STATUS_INVALID_VALUE = 1,   /* null required pointer, negative dim, misalignment */
+  SVDQ_STATUS_NOT_SUPPORTED = 2,   /* group_size != 64, K % 64, N % 64, r not in {0,16,...,128} */
+  SVDQ_STATUS_ARCH_MISMATCH = 3,   /* current device is not gfx950 */
+  SVDQ_STATUS_NO_DEVICE = 4,       /* no HIP device visible */
+  SVDQ_STATUS_HIP_ERROR = 5,       /* the HIP runtime reported an error */
+  SVDQ_STATUS_INTERNAL = 6
+} svdq_status;
+
+/* Static name of a status code. */
+const char* svdq_status_string(svdq_status status);
+
+/* Thread-local message describing the last failing call on this thread ("" if none). */
+const char* svdq_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int svdq_version(void);
+
+/*
+ * Checks that HIP device `device` is a gfx950 (MI355X).  The result is cached per
+ * device.  The loader of the pages validates the GPU generation when a
+ * checkpoint is loaded and errors out on unsupported ones (mind-verse.de,
+ * section "Hardware-Unterstützung"); this is that check for this library.
+ * Returns SUCCESS, NO_DEVICE, ARCH_MISMATCH or INVALID_VALUE (bad index).
+ */
+svdq_status svdq_check_device(int device);
+
+/*
+ * Call 1 - smoothing, per-token per-group int4 quantization, packing, and the
+ * fused low-rank down-projection (charmloop.ai item, fusion paragraph;
+ * ai2day.live, "AI-Bildmodelle auf normalen GPUs ausführen", section "Was ist
+ * Nunchaku Lite und was macht es genau?": 4 bits also for the live activations).
+ *
+ *   mu_k      = fl32(1 / lambda_k)
+ *   x_hat     = bf16(fl32(X * mu))                     (one canonical bf16 X_hat)
+ *   per row m and group g of 64 k:
+ *     s       = bf16(fl32(max|x_hat| / 7))
+ *     q       = clamp(rint_even(x_hat * fl32(1/s)), -7, 7)   (s == 0 -> q = 0)
+ *   lora_act  = bf16(x_hat @ lora_down^T)              (fp32 accumulation)
+ *
+ *   x          device, bf16 [M, K]
+ *   smooth     device, fp32 [K]   lambda (X is divided by it, W multiplied)
+ *   lora_down  device, bf16 [r, K]; may be NULL iff r == 0
+ *   M >= 0 (M == 0 is a no-op), K > 0 with K % 64 == 0, r in {0,16,...,128},
+ *   group_size == 64
+ *   act_codes  device out, u8   [M, K/2]
+ *   act_scales device out, bf16 [M, K/64]
+ *   lora_act   device out, bf16 [M, r]; may be NULL iff r == 0
+ *   stream     hipStream_t or NULL
+ * Codes and scales are exactly defined (bit-exact to the rule above); lora_act
+ * may differ from a float64 evaluation by one bf16 ulp (summation order).
+ */
+svdq_status svdq_quantize_act_lora_down(
+    const void* x, const float* smooth, const void* lora_down,
+    int64_t M, int64_t K, int64_t r, int64_t group_size,
+    void* act_codes, void* act_scales, void* lora_act, void* stream);
+
+/*
+ * Call 2 - W4A4 GEMM with per-group int32 accumulation, per-group
+ * dequantization, the fused low-rank up-projection and the bias
+ * (mind-verse.de, section "Nunchaku und SVDQuant": fused kernels for the 4-bit
+ * path and the low-rank branch; charmloop.ai item, fusion paragraph).
+ *
+ *   acc_g[m,n] = sum_{k in g} q_x[m,k] * q_w[n,k]     (exact int32)
+ *   Y[m,n]     = bf16( sum_g s_x[m,g] s_w[n,g] acc_g[m,n]
+ *                      + lora_act[m,:] . lora_up[n,:] + bias[n] )  (fp32 accumulation)
+ *
+ *   act_codes, act_scales  device, as produced by call 1 ([M,K/2] u8, [M,K/64] bf16)
+ *   w_codes    device, u8   [N, K/2]   packed residual codes (svdq_pack_weights)
+ *   w_scales   device, bf16 [N, K/64]
+ *   lora_act   device, bf16 [M, r]; NULL iff r == 0
+ *   lora_up    device, bf16 [N, r]; NULL iff r == 0
+ *   bias       device, bf16 [N] or NULL (no bias)
+ *   M >= 0 (0 is a no-op), N > 0 with N % 64 == 0, K > 0 with K % 64 == 0,
+ *   r in {0,16,...,128}, group_size == 64
+ *   y          device out, bf16 [M, N]
+ */
+svdq_status svdq_w4a4_gemm_lora_up(
+    const void* act_codes, const void* act_scales,
+    const void* w_codes, const void* w_scales,
+    const void* lora_act, const void* lora_up, const void* bias,
+    int64_t M, int64_t N, int64_t K, int64_t r, int64_t group_size,
+    void* y, void* stream);
+
+/*
+ * Test hook for call 2: runs the same main loop as svdq_w4a4_gemm_lora_up and
+ * writes the int32 group accumulators acc_g[m,n] (the exact integer sums
+ * sum_{k in g} q_x q_w, with any internal scaling removed) instead of Y.
+ *   acc  device out, int32 [M, N, K/64]  (M * N * K/64 elements)
+ * Same shape rules as call 2; no lora, scales or bias are read.
+ */
+svdq_status svdq_w4a4_group_acc_debug(
+    const void* act_codes, const void* w_codes,
+    int64_t M, int64_t N, int64_t K, int64_t group_size,
+    int32_t* acc, void* stream);
+
+/*
+ * Host-side packer, step 1: the smoothing vector (mind-verse.de, section
+ * "Nunchaku und SVDQuant": outliers of the activations are shifted into the
+ * weights).  lambda_j = fl32(sqrt(max(a_j, 1e-5) / max(max_n |W_nj|, 1e-5))),
+ * evaluated in double and rounded once.
+ *   x_absmax  host, fp32 [K]   per-channel max |X| from calibration
+ *   w         host, bf16 [N, K]
+ *   smooth    host out, fp32 [K]
+ * CPU only; never touches a GPU.
+ */
+svdq_status svdq_smooth_from_absmax(const float* x_absmax, const uint16_t* w,
+                                    int64_t N, int64_t K, float* smooth);
+
+/*
+ * Host-side packer, step 2: offline packing of one linear (mind-verse.de,
+ * section "Nunchaku und SVDQuant"; config example with rank 32 in section
+ * "Native Ladefunktion in Diffusers"; ai2day.live section "Was ist Nunchaku
+ * Lite und was macht es genau?" for the SVD).
+ *   W' = W diag(lambda) in double; a rank-r truncated SVD W' ~= U S V^T by
+ *   randomized subspace iteration (seeded by `seed`), singular values shared
+ *   evenly: lora_up = bf16(U S^1/2) [N,r], lora_down = bf16(S^1/2 V^T) [r,K];
+ *   R = W' - lora_up lora_down (with the rounded factors, in double);
+ *   per row n and group g: s = bf16(max|R| / 7) (one rounding),
+ *   q = clamp(rint_even(R / s), -7, 7), packed as described above.
+ *   w         host, bf16 [N, K];  smooth  host, fp32 [K]
+ *   N > 0, K > 0 with K % 64 == 0, r in {0,...,min(N,K,128)} (any r here),
+ *   group_size == 64
+ *   w_codes   host out, u8   [N, K/2]
+ *   w_scales  host out, bf16 [N, K/64]
+ *   lora_down host out, bf16 [r, K]  (may be NULL iff r == 0)
+ *   lora_up   host out, bf16 [N, r]  (may be NULL iff r == 0)
+ * CPU only (threads); deterministic for a given seed and thread count.
+ */
+svdq_status svdq_pack_weights(const uint16_t* w, const float* smooth,
+                              int64_t N, int64_t K, int64_t r, int64_t group_size,
+                              uint64_t seed,
+                              uint8_t* w_codes, uint16_t* w_scales,
+                              uint16_t* lora_down, uint16_t* lora_up);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

@@ -1,0 +1,67 @@
+"""Helpers for the GPU parity tests: host <-> device conversion and comparisons."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as O
+import synthetic as S
+
+_CASES: dict = {}
+
+
+def to_dev_bf16(bits: np.ndarray):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).cuda()
+
+
+def to_dev(a: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bf16_bits(t) -> np.ndarray:
+    import torch
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """Distance in bf16 units in the last place (monotone integer order of the patterns)."""
+    def order(b):
+        b = b.astype(np.int64)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    return np.abs(order(a_bits) - order(b_bits))
+
+
+def y_errors(y_bits: np.ndarray, y_ref: np.ndarray):
+    y = O.bf16_to_f64(y_bits)
+    rel_fro = np.linalg.norm(y - y_ref) / max(np.linalg.norm(y_ref), 1e-300)
+    max_abs = np.abs(y - y_ref).max() / max(np.abs(y_ref).max(), 1e-300)
+    return rel_fro, max_abs
+
+
+# tolerance on Y against the float64 oracle: relative Frobenius and max-abs / max|Y*|
+Y_REL_FRO = 5e-3
+Y_MAX_ABS = 1e-2
+
+
+def oracle_case(spec, M=None, r=None):
+    """Inputs plus the oracle's own packing of the weights (cached per shape)."""
+    if isinstance(spec, str):
+        spec = S.SPECS[spec]
+    key = (spec, M, r)
+    if key not in _CASES:
+        d = S.make_linear(spec, M=M)
+        lam = O.smooth_factors(O.activation_absmax(d["x"]), d["w"])
+        rr = spec.r if r is None else r
+        packed = O.pack_weights(d["w"], lam, rr)
+        for k in ("residual", "w_smooth", "q_w"):
+            packed.pop(k, None)
+        _CASES[key] = (d, lam, packed)
+    return _CASES[key]
+
+
+def custom_case(M, K, N, r, seed=0, outliers=4):
+    spec = S.LinearSpec(f"custom{M}x{K}x{N}r{r}", 9, M, K, N, r, outlier_channels=min(outliers, K),
+                        outlier_scale=30.0, heavy_tail=True, layer_id=seed)
+    return oracle_case(spec)

@@ -1,0 +1,159 @@
+"""C ABI checks that need no GPU: exports, status strings, argument validation.
+
+Argument errors must be reported before any HIP call, so they are testable on a
+machine without a GPU; a well-formed call there must report NO_DEVICE rather
+than crash.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from bit_diffusion_transformer_svdq_amd import _lib
+from bit_diffusion_transformer_svdq_amd._lib import (ARCH_MISMATCH, INVALID_VALUE, NO_DEVICE,
+                                                     NOT_SUPPORTED, SUCCESS, lib)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svdq.h")
+FAKE = ctypes.c_void_p(0x10000)     # non-null, 16-byte aligned, never dereferenced
+FAKE_ODD = ctypes.c_void_p(0x10008)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(svdq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = _declared_functions()
+    for must in ("svdq_quantize_act_lora_down", "svdq_w4a4_gemm_lora_up", "svdq_pack_weights",
+                 "svdq_smooth_from_absmax", "svdq_check_device", "svdq_w4a4_group_acc_debug"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = lib()
+    names = _declared_functions()
+    assert set(names) == set(_lib.SIGNATURES)
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(svdq_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_status_strings_and_version():
+    L = lib()
+    assert L.svdq_status_string(SUCCESS) == b"SVDQ_STATUS_SUCCESS"
+    assert L.svdq_status_string(NOT_SUPPORTED) == b"SVDQ_STATUS_NOT_SUPPORTED"
+    assert L.svdq_status_string(99) == b"SVDQ_STATUS_UNKNOWN"
+    assert L.svdq_version() >= 100
+
+
+def _quant(**kw):
+    a = dict(x=FAKE, smooth=FAKE, lora_down=FAKE, M=64, K=256, r=16, g=64,
+             codes=FAKE, scales=FAKE, la=FAKE, stream=None)
+    a.update(kw)
+    return lib().svdq_quantize_act_lora_down(a["x"], a["smooth"], a["lora_down"], a["M"], a["K"], a["r"],
+                                             a["g"], a["codes"], a["scales"], a["la"], a["stream"])
+
+
+def _gemm(**kw):
+    a = dict(ac=FAKE, asc=FAKE, wc=FAKE, ws=FAKE, la=FAKE, lu=FAKE, bias=FAKE, M=64, N=256, K=256,
+             r=16, g=64, y=FAKE, stream=None)
+    a.update(kw)
+    return lib().svdq_w4a4_gemm_lora_up(a["ac"], a["asc"], a["wc"], a["ws"], a["la"], a["lu"], a["bias"],
+                                        a["M"], a["N"], a["K"], a["r"], a["g"], a["y"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID_VALUE),
+    (dict(smooth=None), INVALID_VALUE),
+    (dict(codes=None), INVALID_VALUE),
+    (dict(scales=None), INVALID_VALUE),
+    (dict(lora_down=None), INVALID_VALUE),
+    (dict(la=None), INVALID_VALUE),
+    (dict(M=-1), INVALID_VALUE),
+    (dict(K=0), INVALID_VALUE),
+    (dict(K=96), NOT_SUPPORTED),
+    (dict(g=32), NOT_SUPPORTED),
+    (dict(r=8), NOT_SUPPORTED),
+    (dict(r=144), NOT_SUPPORTED),
+    (dict(x=FAKE_ODD), INVALID_VALUE),
+    (dict(M=0), SUCCESS),                       # empty batch: a no-op
+    (dict(r=0, lora_down=None, la=None, M=0), SUCCESS),
+])
+def test_quantize_argument_errors(kw, status):
+    assert _quant(**kw) == status
+    if status != SUCCESS:
+        assert len(lib().svdq_last_error()) > 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ac=None), INVALID_VALUE),
+    (dict(wc=None), INVALID_VALUE),
+    (dict(asc=None), INVALID_VALUE),
+    (dict(ws=None), INVALID_VALUE),
+    (dict(y=None), INVALID_VALUE),
+    (dict(la=None), INVALID_VALUE),
+    (dict(lu=None), INVALID_VALUE),
+    (dict(N=96), NOT_SUPPORTED),
+    (dict(N=0), INVALID_VALUE),
+    (dict(K=100), NOT_SUPPORTED),
+    (dict(r=20), NOT_SUPPORTED),
+    (dict(g=128), NOT_SUPPORTED),
+    (dict(bias=FAKE_ODD), INVALID_VALUE),
+    (dict(M=0), SUCCESS),
+    (dict(M=0, bias=None, r=0, la=None, lu=None), SUCCESS),
+])
+def test_gemm_argument_errors(kw, status):
+    assert _gemm(**kw) == status
+
+
+def test_debug_hook_argument_errors():
+    L = lib()
+    assert L.svdq_w4a4_group_acc_debug(FAKE, FAKE, 4, 64, 64, 64, None, None) == INVALID_VALUE
+    assert L.svdq_w4a4_group_acc_debug(FAKE, FAKE, 4, 64, 96, 64, FAKE, None) == NOT_SUPPORTED
+    assert L.svdq_w4a4_group_acc_debug(FAKE, FAKE, 0, 64, 64, 64, FAKE, None) == SUCCESS
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="checks the no-GPU path")
+def test_well_formed_calls_without_a_gpu_report_no_device():
+    assert lib().svdq_check_device(0) in (NO_DEVICE, ARCH_MISMATCH)
+    assert _quant() == NO_DEVICE
+    assert _gemm() == NO_DEVICE
+    assert lib().svdq_check_device(-1) == INVALID_VALUE
+
+
+def test_packer_argument_errors():
+    L = lib()
+    assert L.svdq_pack_weights(None, FAKE, 4, 64, 0, 64, 0, FAKE, FAKE, None, None) == INVALID_VALUE
+    assert L.svdq_smooth_from_absmax(None, FAKE, 4, 64, FAKE) == INVALID_VALUE
+    import numpy as np
+    w = np.zeros((4, 96), np.uint16)
+    lam = np.ones(96, np.float32)
+    codes = np.zeros((4, 48), np.uint8)
+    sc = np.zeros((4, 2), np.uint16)
+    vp = ctypes.c_void_p
+    st = L.svdq_pack_weights(w.ctypes.data_as(vp), lam.ctypes.data_as(vp), 4, 96, 0, 64, 0,
+                             codes.ctypes.data_as(vp), sc.ctypes.data_as(vp), None, None)
+    assert st == NOT_SUPPORTED
+    w = np.zeros((4, 64), np.uint16)
+    lam = np.ones(64, np.float32)
+    st = L.svdq_pack_weights(w.ctypes.data_as(vp), lam.ctypes.data_as(vp), 4, 64, 4, 64, 0,
+                             codes.ctypes.data_as(vp), sc.ctypes.data_as(vp), None, None)
+    assert st == INVALID_VALUE   # r > 0 needs the factor outputs
+    st = L.svdq_pack_weights(w.ctypes.data_as(vp), lam.ctypes.data_as(vp), 4, 64, 8, 64, 0,
+                             codes.ctypes.data_as(vp), sc.ctypes.data_as(vp), FAKE, FAKE)
+    assert st == NOT_SUPPORTED   # rank larger than min(N, K)

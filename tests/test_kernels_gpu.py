@@ -1,0 +1,218 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.  Needs an MI355X.
+
+Bar: activation codes, activation scales and the int32 group accumulators are
+bit-exact; lora_act is within one bf16 ulp (fp32 vs float64 summation order);
+Y is within relative Frobenius 5e-3 and max-abs 1e-2 * max|Y*| of the float64
+oracle.  Weights are packed by the oracle, so the kernels are judged on the
+oracle's own inputs; the C++ packer is checked separately on the CPU.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synthetic as S
+from tests.gpu_util import (Y_MAX_ABS, Y_REL_FRO, bf16_bits, custom_case, oracle_case, to_dev,
+                            to_dev_bf16, ulp_distance, y_errors)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    from bit_diffusion_transformer_svdq_amd import check_device
+    check_device(0)
+
+
+def _run(d, lam, packed, bias=True):
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K
+    r = packed["lora_down"].shape[0]
+    x = to_dev_bf16(d["x"])
+    lam_t = to_dev(np.asarray(lam, np.float32))
+    down = to_dev_bf16(packed["lora_down"]) if r else None
+    up = to_dev_bf16(packed["lora_up"]) if r else None
+    wc = to_dev(packed["w_codes"])
+    ws = to_dev_bf16(packed["w_scales"])
+    b = to_dev_bf16(d["bias"]) if bias else None
+    codes, scales, la = K.quantize_act_lora_down(x, lam_t, down)
+    y = K.w4a4_gemm_lora_up(codes, scales, wc, ws, la if r else None, up, b)
+    torch.cuda.synchronize()
+    return {"act_codes": codes.cpu().numpy(), "act_scales": bf16_bits(scales),
+            "lora_act": bf16_bits(la), "y": bf16_bits(y)}
+
+
+def _check_quant(got, ref):
+    assert np.array_equal(got["act_scales"], ref["act_scales"]), \
+        np.argwhere(got["act_scales"] != ref["act_scales"])[:5]
+    assert np.array_equal(got["act_codes"], ref["act_codes"]), \
+        np.argwhere(got["act_codes"] != ref["act_codes"])[:5]
+    if ref["lora_act"].size:
+        assert ulp_distance(got["lora_act"], ref["lora_act"]).max() <= 1
+
+
+def _check_y(y_bits, d, lam, packed, ref_a, rows=None, bias=True):
+    y_ref, _ = O.linear_output(ref_a["act_codes"], ref_a["act_scales"], packed["w_codes"],
+                               packed["w_scales"], ref_a["lora_act"], packed["lora_up"],
+                               d["bias"] if bias else None, rows=rows)
+    got = y_bits if rows is None else y_bits[np.asarray(rows)]
+    rel, mx = y_errors(got, y_ref)
+    assert rel <= Y_REL_FRO and mx <= Y_MAX_ABS, (rel, mx)
+    return rel, mx
+
+
+def test_tiny_config_full_parity():
+    d, lam, packed = oracle_case("tiny")
+    got = _run(d, lam, packed)
+    ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
+    _check_quant(got, ref)
+    _check_y(got["y"], d, lam, packed, ref)
+
+
+def test_group_accumulators_bit_exact_tiny():
+    import bit_diffusion_transformer_svdq_amd as K
+    d, lam, packed = oracle_case("tiny")
+    ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
+    acc = K.w4a4_group_acc_debug(to_dev(ref["act_codes"]), to_dev(packed["w_codes"])).cpu().numpy()
+    want = O.group_accumulators(ref["act_codes"], packed["w_codes"])
+    assert np.array_equal(acc, want), np.argwhere(acc != want)[:5]
+
+
+@pytest.mark.parametrize("M,K,N,r", [
+    (1, 64, 64, 0), (17, 128, 192, 16), (127, 320, 64, 48), (129, 256, 320, 64),
+    (255, 192, 128, 32), (300, 512, 448, 16), (64, 1024, 256, 128), (513, 64, 64, 16),
+])
+def test_edge_shapes(M, K, N, r):
+    d, lam, packed = custom_case(M, K, N, r, seed=M + N)
+    got = _run(d, lam, packed)
+    ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
+    _check_quant(got, ref)
+    _check_y(got["y"], d, lam, packed, ref)
+
+
+@pytest.mark.parametrize("M,K,N", [(37, 192, 320), (200, 128, 64)])
+def test_group_accumulators_bit_exact_ragged(M, K, N):
+    import bit_diffusion_transformer_svdq_amd as K_
+    d, lam, packed = custom_case(M, K, N, 0, seed=3)
+    ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
+    acc = K_.w4a4_group_acc_debug(to_dev(ref["act_codes"]), to_dev(packed["w_codes"])).cpu().numpy()
+    want = O.group_accumulators(ref["act_codes"], packed["w_codes"])
+    assert np.array_equal(acc, want)
+
+
+def test_no_bias_and_rank0():
+    d, lam, packed = custom_case(96, 256, 128, 0, seed=11)
+    got = _run(d, lam, packed, bias=False)
+    ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
+    _check_quant(got, ref)
+    _check_y(got["y"], d, lam, packed, ref, bias=False)
+
+
+def test_extreme_groups_zero_and_saturated():
+    """All-zero groups (s = 0, q = 0) and single-spike groups (one code at +-7)."""
+    d, lam, packed = custom_case(48, 256, 128, 16, seed=21)
+    x = d["x"].copy()
+    x[:, 64:128] = 0                     # a whole zero group in every row
+    x[5, :] = 0                          # an all-zero row
+    x[7, 130] = 0x4700                   # a lone spike
+    d = dict(d, x=x)
+    got = _run(d, lam, packed)
+    ref = O.quantize_act_lora_down(x, lam, packed["lora_down"])
+    _check_quant(got, ref)
+    assert np.all(got["act_scales"][:, 1] == 0)
+    _check_y(got["y"], d, lam, packed, ref)
+
+
+def test_bf16_rounding_ties_in_smoothing():
+    """mu = 1.5 and 2.5 exactly: x * mu needs 9-10 significant bits, so the bf16
+    rounding of x_hat hits exact ties often (round half to even decides)."""
+    d, lam, packed = custom_case(64, 128, 64, 16, seed=5)
+    lam2 = np.full_like(lam, np.float32(1.0))
+    lam2[::3] = np.float32(2.0 / 3.0)    # fl32(1 / lambda) = 1.5
+    lam2[1::3] = np.float32(0.4)         # fl32(1 / lambda) = 2.5
+    p = O.f64_to_f32(O.bf16_to_f64(d["x"]) * (1.0 / lam2.astype(np.float64)).astype(np.float32))
+    ties = (p.view(np.uint32) & 0xFFFF) == 0x8000
+    assert ties.sum() > 100
+    got = _run(d, lam2, packed)
+    ref = O.quantize_act_lora_down(d["x"], lam2, packed["lora_down"])
+    _check_quant(got, ref)
+
+
+def test_empty_batch_is_a_noop():
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K
+    d, lam, packed = oracle_case("tiny")
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    codes, scales, la = K.quantize_act_lora_down(x, to_dev(lam), to_dev_bf16(packed["lora_down"]))
+    y = K.w4a4_gemm_lora_up(codes, scales, to_dev(packed["w_codes"]), to_dev_bf16(packed["w_scales"]),
+                            la, to_dev_bf16(packed["lora_up"]), None)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 256)
+
+
+def test_outputs_do_not_write_outside_their_buffers():
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K
+    d, lam, packed = custom_case(77, 256, 192, 32, seed=8)
+    M, Kd, N, r = 77, 256, 192, 32
+    pad = 4096
+    sent = 0x5A
+
+    def guarded(n, dtype):
+        buf = torch.full((n + 2 * pad,), sent, dtype=torch.uint8, device="cuda")
+        return buf
+
+    cb = guarded(M * Kd // 2, torch.uint8)
+    sb = guarded(M * (Kd // 64) * 2, torch.uint8)
+    lb = guarded(M * r * 2, torch.uint8)
+    yb = guarded(M * N * 2, torch.uint8)
+    codes = cb[pad:pad + M * Kd // 2].view(M, Kd // 2)
+    scales = sb[pad:pad + M * (Kd // 64) * 2].view(torch.bfloat16).view(M, Kd // 64)
+    la = lb[pad:pad + M * r * 2].view(torch.bfloat16).view(M, r)
+    y = yb[pad:pad + M * N * 2].view(torch.bfloat16).view(M, N)
+    K.quantize_act_lora_down(to_dev_bf16(d["x"]), to_dev(lam), to_dev_bf16(packed["lora_down"]),
+                             out=(codes, scales, la))
+    K.w4a4_gemm_lora_up(codes, scales, to_dev(packed["w_codes"]), to_dev_bf16(packed["w_scales"]), la,
+                        to_dev_bf16(packed["lora_up"]), to_dev_bf16(d["bias"]), out=y)
+    torch.cuda.synchronize()
+    for buf, n in ((cb, M * Kd // 2), (sb, M * (Kd // 64) * 2), (lb, M * r * 2), (yb, M * N * 2)):
+        h = buf.cpu().numpy()
+        assert np.all(h[:pad] == sent) and np.all(h[pad + n:] == sent)
+
+
+def test_repeated_launches_are_bit_identical():
+    d, lam, packed = custom_case(257, 512, 384, 32, seed=4)
+    first = _run(d, lam, packed)
+    for _ in range(5):
+        again = _run(d, lam, packed)
+        for k in first:
+            assert np.array_equal(first[k], again[k]), k
+
+
+# ---- DiT-scale shapes, in the launch configuration the benchmark times ----
+
+def _full_case(name):
+    d, lam, packed = oracle_case(name)
+    got = _run(d, lam, packed)
+    ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
+    _check_quant(got, ref)           # every row, bit-exact
+    M = d["spec"].M
+    rows = sorted(set([0, 1, 63, 64, 127, 128, 129, 1000, 2047, 2048, 4095, 4096, 4097, M - 2, M - 1]))
+    rows = [r for r in rows if r < M]
+    _check_y(got["y"], d, lam, packed, ref, rows=rows)
+    return d, packed, ref
+
+
+@pytest.mark.parametrize("name", ["attn_out", "qkv", "mlp_up", "mlp_down"])
+def test_dit_shapes_parity(name):
+    _full_case(name)
+
+
+def test_headline_group_accumulators_on_a_row_window():
+    import bit_diffusion_transformer_svdq_amd as K
+    d, lam, packed = oracle_case("mlp_up")
+    ref = O.quantize_act_lora_down(d["x"][4544:4608], lam, packed["lora_down"])
+    acc = K.w4a4_group_acc_debug(to_dev(ref["act_codes"]), to_dev(packed["w_codes"])).cpu().numpy()
+    want = O.group_accumulators(ref["act_codes"], packed["w_codes"])
+    assert np.array_equal(acc, want)

@@ -165,6 +165,8 @@ def main():
     ap.add_argument("--extra", default="", help="write per-kernel details of extra shapes here (JSON)")
     ap.add_argument("--extra-configs", default="attn_out,qkv,mlp_down")
     ap.add_argument("--extra-m", default="64,256,1024")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -174,6 +176,15 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calib:
+        import torch
+        n = args.copy_calib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     res = measure_gpu(args.config, args.m, args.steps, args.warmup)
     M, Kd, N, r = res["M"], res["K"], res["N"], res["r"]
     ops = 2.0 * M * N * Kd

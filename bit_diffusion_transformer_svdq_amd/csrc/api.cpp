@@ -123,6 +123,7 @@ svdq_status svdq_quantize_act_lora_down(const void* x, const float* smooth, cons
   if (!rank_supported(r)) return fail(SVDQ_STATUS_NOT_SUPPORTED, "rank %lld (need 0..128, multiple of 16)", (long long)r);
   if (M > (1ll << 24) || K > (1ll << 20) || M * K > (1ll << 40))
     return fail(SVDQ_STATUS_NOT_SUPPORTED, "problem too large M=%lld K=%lld", (long long)M, (long long)K);
+  if (M == 0) return ok();  // empty batch: nothing is read or written, pointers may be null
   if (!x || !smooth || !act_codes || !act_scales)
     return fail(SVDQ_STATUS_INVALID_VALUE, "null x/smooth/act_codes/act_scales");
   if (r > 0 && (!lora_down || !lora_act))
@@ -130,7 +131,6 @@ svdq_status svdq_quantize_act_lora_down(const void* x, const float* smooth, cons
   if (!aligned16(x) || !aligned16(smooth) || !aligned16(act_codes) || !aligned16(act_scales) ||
       (r > 0 && (!aligned16(lora_down) || !aligned16(lora_act))))
     return fail(SVDQ_STATUS_INVALID_VALUE, "device pointers must be 16-byte aligned");
-  if (M == 0) return ok();
   svdq_status s = check_current_device();
   if (s != SVDQ_STATUS_SUCCESS) return s;
   hipError_t e = svdq::launch_quant_lora_down(
@@ -153,6 +153,7 @@ static svdq_status validate_gemm(const void* act_codes, const void* w_codes, int
   if (M > (1ll << 24) || N > (1ll << 20) || K > (1ll << 20))
     return fail(SVDQ_STATUS_NOT_SUPPORTED, "problem too large M=%lld N=%lld K=%lld", (long long)M,
                 (long long)N, (long long)K);
+  if (M == 0) return SVDQ_STATUS_SUCCESS;  // empty batch: the caller returns before any pointer check
   if (!act_codes || !w_codes) return fail(SVDQ_STATUS_INVALID_VALUE, "null act_codes/w_codes");
   if (!aligned16(act_codes) || !aligned16(w_codes))
     return fail(SVDQ_STATUS_INVALID_VALUE, "device pointers must be 16-byte aligned");
@@ -166,13 +167,13 @@ svdq_status svdq_w4a4_gemm_lora_up(const void* act_codes, const void* act_scales
                                    void* y, void* stream) {
   svdq_status s = validate_gemm(act_codes, w_codes, M, N, K, r, group_size);
   if (s != SVDQ_STATUS_SUCCESS) return s;
+  if (M == 0) return ok();
   if (!act_scales || !w_scales || !y) return fail(SVDQ_STATUS_INVALID_VALUE, "null act_scales/w_scales/y");
   if (r > 0 && (!lora_act || !lora_up))
     return fail(SVDQ_STATUS_INVALID_VALUE, "r=%lld needs lora_act and lora_up", (long long)r);
   if (!aligned16(act_scales) || !aligned16(w_scales) || !aligned16(y) ||
       (bias && !aligned16(bias)) || (r > 0 && (!aligned16(lora_act) || !aligned16(lora_up))))
     return fail(SVDQ_STATUS_INVALID_VALUE, "device pointers must be 16-byte aligned");
-  if (M == 0) return ok();
   s = check_current_device();
   if (s != SVDQ_STATUS_SUCCESS) return s;
   hipError_t e = svdq::launch_w4a4_gemm_lora_up(
@@ -190,9 +191,9 @@ svdq_status svdq_w4a4_group_acc_debug(const void* act_codes, const void* w_codes
                                       void* stream) {
   svdq_status s = validate_gemm(act_codes, w_codes, M, N, K, 0, group_size);
   if (s != SVDQ_STATUS_SUCCESS) return s;
+  if (M == 0) return ok();
   if (!acc) return fail(SVDQ_STATUS_INVALID_VALUE, "null acc");
   if (M * N * (K / 64) > (1ll << 31)) return fail(SVDQ_STATUS_NOT_SUPPORTED, "accumulator dump too large");
-  if (M == 0) return ok();
   s = check_current_device();
   if (s != SVDQ_STATUS_SUCCESS) return s;
   hipError_t e = svdq::launch_w4a4_gemm_lora_up(

@@ -32,6 +32,8 @@
  *    allocates device memory and keeps no state besides a per-device
  *    capability cache.  Device pointers must be 16-byte aligned.  Outputs must
  *    not overlap inputs or each other.
+ *  - Empty batch: M == 0 is a successful no-op once the dimensions are valid;
+ *    nothing is read or written, so the pointers may be NULL.
  *  - Errors: argument and shape errors are returned synchronously, before any
  *    HIP call.  Kernels run asynchronously on `stream` (a hipStream_t; NULL is
  *    the default stream) on the current HIP device; a launch failure returns

@@ -85,6 +85,8 @@ def _gemm(**kw):
     (dict(x=FAKE_ODD), INVALID_VALUE),
     (dict(M=0), SUCCESS),                       # empty batch: a no-op
     (dict(r=0, lora_down=None, la=None, M=0), SUCCESS),
+    (dict(M=0, x=None, codes=None, scales=None), SUCCESS),   # empty tensors may be null
+    (dict(M=0, K=96), NOT_SUPPORTED),           # dimensions are still validated
 ])
 def test_quantize_argument_errors(kw, status):
     assert _quant(**kw) == status
@@ -108,6 +110,8 @@ def test_quantize_argument_errors(kw, status):
     (dict(bias=FAKE_ODD), INVALID_VALUE),
     (dict(M=0), SUCCESS),
     (dict(M=0, bias=None, r=0, la=None, lu=None), SUCCESS),
+    (dict(M=0, ac=None, asc=None, la=None, y=None), SUCCESS),
+    (dict(M=0, N=96), NOT_SUPPORTED),
 ])
 def test_gemm_argument_errors(kw, status):
     assert _gemm(**kw) == status

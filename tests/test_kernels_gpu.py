@@ -43,13 +43,34 @@ def _run(d, lam, packed, bias=True):
             "lora_act": bf16_bits(la), "y": bf16_bits(y)}
 
 
-def _check_quant(got, ref):
+def _check_quant(got, ref, lora_down=None):
     assert np.array_equal(got["act_scales"], ref["act_scales"]), \
         np.argwhere(got["act_scales"] != ref["act_scales"])[:5]
     assert np.array_equal(got["act_codes"], ref["act_codes"]), \
         np.argwhere(got["act_codes"] != ref["act_codes"])[:5]
     if ref["lora_act"].size:
-        assert ulp_distance(got["lora_act"], ref["lora_act"]).max() <= 1
+        _check_lora_act(got["lora_act"], ref, lora_down)
+
+
+def _check_lora_act(got_bits, ref, lora_down):
+    """lora_act = bf16(x_hat @ L1) with fp32 accumulation on the GPU.
+
+    Bound from the arithmetic: both sides round to bf16 once (half an ulp each),
+    and an fp32 sum of K products (exact bf16 x bf16 products) is off by at most
+    K * 2^-24 * sum_k |x_hat_k L1_k|.  Where the sum does not cancel this is
+    below one ulp, and almost every element must be within one ulp."""
+    d = ulp_distance(got_bits, ref["lora_act"])
+    assert (d <= 1).mean() >= 0.999, (d > 1).sum()
+    if lora_down is None:
+        assert d.max() <= 1
+        return
+    xh = np.abs(O.bf16_to_f64(ref["xhat"]))
+    mag = xh @ np.abs(O.bf16_to_f64(lora_down)).T
+    K = xh.shape[1]
+    got = O.bf16_to_f64(got_bits)
+    want = O.bf16_to_f64(ref["lora_act"])
+    ulp = np.maximum(np.abs(want), np.abs(got)) * 2.0 ** -7
+    assert np.all(np.abs(got - want) <= ulp + K * 2.0 ** -24 * mag)
 
 
 def _check_y(y_bits, d, lam, packed, ref_a, rows=None, bias=True):
@@ -196,7 +217,7 @@ def _full_case(name):
     d, lam, packed = oracle_case(name)
     got = _run(d, lam, packed)
     ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
-    _check_quant(got, ref)           # every row, bit-exact
+    _check_quant(got, ref, packed["lora_down"])     # codes and scales: every row, bit-exact
     M = d["spec"].M
     rows = sorted(set([0, 1, 63, 64, 127, 128, 129, 1000, 2047, 2048, 4095, 4096, 4097, M - 2, M - 1]))
     rows = [r for r in rows if r < M]

@@ -13,25 +13,35 @@
 // layout (lane l: column l%16, rows 4*(l/16) + v) every lane then owns four
 // consecutive n of one token row m, so Y rows are written 8 bytes at a time.
 //
-// Main loop, per 64-wide group g:
-//  * staging: each thread loads 16 packed bytes (32 nibbles) of the weight tile
-//    and 16 of the activation tile, widens nibbles to int8 as 16*q with
-//    (x & 0xF0F0F0F0) and ((x << 4) & 0xF0F0F0F0) (no sign extension needed),
-//    and writes them to a double-buffered LDS stage.  Weights and activations
-//    go through the same code, so the K permutation this introduces is the same
-//    on both sides and the dot products are unchanged; the products are 256 *
-//    q_x * q_w.
+// Data movement.  The packed int4 tiles (128 rows x 32 bytes per operand and
+// group) go from memory straight into LDS with global_load_lds_dwordx4, no
+// registers involved, through a ring of kStages stages: group g+3 is in flight
+// while group g is computed, with one barrier per group.  Vector-memory
+// counters retire in issue order, so the wait for stage g is an explicit
+// s_waitcnt vmcnt(4) (the two later stages' loads may stay in flight).  Inside
+// an operand tile the two 16-byte granules of row r sit at slots
+// 2r + (h ^ r[2] ^ r[3]), which makes the 8-byte fragment reads conflict free
+// for 32 and 64 LDS banks.  Scales come 8 groups at a time (one 16-byte load
+// per thread and block), are converted once per workgroup and written to the
+// stage one group ahead.  The lora_up and lora_act tiles are loaded into LDS at
+// kernel start, so the epilogue does not wait for memory.
+//
+// Main loop, per 64-wide group g and wave (64 n x 64 m, 4 x 4 MFMA tiles):
+//  * fragments: 8-byte LDS reads; nibbles widened to int8 as 16*q with
+//    (x & 0xF0F0F0F0) and ((x << 4) & 0xF0F0F0F0), identically for weights and
+//    activations, so the K permutation this introduces cancels in the dot
+//    products; the products are 256 * q_x * q_w.
 //  * MFMA: v_mfma_i32_16x16x64_i8 covers one whole group per instruction.  Its
 //    C operand is the constant 0x4B400000 (the bits of 1.5 * 2^23), so the int32
 //    result read as fp32 is exactly 1.5 * 2^23 + 256 * acc (|256 acc| <= 802816
 //    < 2^22): the int->float conversion is free.
 //  * dequant: t = fma(F, s_x/256, -1.5*2^23 * s_x/256) = fl32(acc * s_x) exactly
-//    (s_x is bf16, so both constants are exact), then y = fma(t, s_w, y).
+//    (s_x is bf16, so both constants are exact), then y = fma(t, s_w, y); each
+//    MFMA is followed by the 8 FMAs of the previous tile.
 // The int32 group accumulator itself is exact; the debug variant of this
 // kernel stores (bits - 0x4B400000) >> 8 instead of dequantizing.
 //
-// Workgroup: 256 threads (4 waves as 2 x 2), tile 128 n x 128 m, wave tile
-// 64 x 64 = 4 x 4 MFMA tiles.
+// Workgroup: 256 threads (4 waves as 2 x 2), tile 128 n x 128 m.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -48,41 +58,59 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned int u32;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
 constexpr int kBN = 128;            // weight rows (n) per workgroup
 constexpr int kBM = 128;            // token rows (m) per workgroup
 constexpr int kThreads = 256;
-constexpr int kStride = 80;         // LDS bytes per int8 row of one group (64 + 16 pad)
+constexpr int kStages = 4;          // LDS ring depth, in groups
+constexpr int kTile = 128 * 32;     // packed bytes of one operand tile for one group
+constexpr int kStageBytes = 2 * kTile + 3 * 128 * 4;  // W tile, A tile, sxp/sxc/sw (128 each)
+constexpr int kLoraOff = kStages * kStageBytes + 2 * 256 * 16;  // static LDS before the lora tiles
 constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
-
-struct Stage {
-  uint8_t w[kBN * kStride];
-  uint8_t a[kBM * kStride];
-  float sxm[kBM * 2];   // per token m (permuted, see below): (s_x / 256, -1.5*2^23 * s_x / 256)
-  float sw[kBN];        // per weight row n: s_w
-};
+constexpr u32 kNib = 0xF0F0F0F0u;
 
 __device__ __forceinline__ u32 pack_bf16(float a, float b) {
   v2f f = {a, b};
   return __builtin_bit_cast(u32, __builtin_convertvector(f, v2bf));
 }
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
-  return __builtin_bit_cast(float, (u32)h << 16);
+
+// Slot p (0..127) of the token-scale arrays -> token m of the tile.  Lane l of
+// wave column wm reads slots wm*64 + 4*(l%16) + j (j = 0..3), i.e. the tokens
+// m = wm*64 + 16j + l%16 it owns, as one contiguous 16-byte LDS read.
+__device__ __forceinline__ int sx_token(int p) {
+  return (p >> 6) * 64 + (p & 3) * 16 + ((p >> 2) & 15);
 }
 
-// Token m (0..127) of the tile -> slot in sxm, so that lane l of wave column wm
-// finds its four m = wm*64 + 16j + l%16 (j = 0..3) as 8 consecutive floats.
-__device__ __forceinline__ int sx_slot(int m) {
-  return (m >> 6) * 64 + (m & 15) * 4 + ((m >> 4) & 3);
+// 16-byte granule slot of (row r, granule h) inside an operand tile.
+__device__ __forceinline__ int gran_slot(int r, int h) {
+  return 2 * r + (h ^ ((r >> 2) & 1) ^ ((r >> 3) & 1));
 }
 
-// widen 16 packed bytes (32 nibbles) to 32 int8 bytes holding 16*q
-__device__ __forceinline__ void widen(const uint4 p, uint4& lo, uint4& hi) {
-  lo.x = (p.x << 4) & 0xF0F0F0F0u;  hi.x = p.x & 0xF0F0F0F0u;
-  lo.y = (p.y << 4) & 0xF0F0F0F0u;  hi.y = p.y & 0xF0F0F0F0u;
-  lo.z = (p.z << 4) & 0xF0F0F0F0u;  hi.z = p.z & 0xF0F0F0F0u;
-  lo.w = (p.w << 4) & 0xF0F0F0F0u;  hi.w = p.w & 0xF0F0F0F0u;
+// wait until at most n vector-memory operations of this wave are outstanding
+// (and, with kLds, until all of its LDS operations are done)
+template <int n, bool kLds>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | ((kLds ? 0 : 0xF) << 8) | ((n >> 4) << 14));
+}
+
+// workgroup barrier without the memory fences of __syncthreads (the waits it
+// needs are explicit above); the empty asm keeps LDS accesses on their side
+__device__ __forceinline__ void barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void dma16(const void* gptr, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((glb_void*)gptr, (lds_void*)lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ v4i widen(uint2 p) {
+  return v4i{(int)((p.x << 4) & kNib), (int)(p.x & kNib), (int)((p.y << 4) & kNib), (int)(p.y & kNib)};
 }
 
 template <bool kDump>
@@ -99,69 +127,122 @@ struct GemmArgs {
   int M, N, K, r;
 };
 
-template <bool kDump>
-__global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(const GemmArgs<kDump> p) {
-  __shared__ Stage st[2];
+// Workgroup id -> (tile_m, tile_n).  Workgroups are dispatched round-robin over
+// the 8 XCDs (id % 8), each XCD with its own L2.  The ids of one XCD are mapped
+// onto one contiguous chunk of the tile list, and the tile list is ordered in
+// bands of kBandM tile rows, so the tiles an XCD runs at the same time share a
+// few activation tiles and a few weight tiles in that XCD's L2.
+constexpr int kXcds = 8;
+constexpr int kBandM = 8;
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int T = tiles_m * tiles_n;
+  const int x = bid % kXcds;
+  const int i = bid / kXcds;
+  const int per = T / kXcds, rem = T % kXcds;
+  const int t = x * per + min(x, rem) + i;
+  const int band = t / (kBandM * tiles_n);
+  const int first = band * kBandM;
+  const int rows = min(tiles_m - first, kBandM);
+  const int in = t - band * kBandM * tiles_n;
+  tm = first + in % rows;
+  tn = in / rows;
+}
 
-  const int M = p.M, N = p.N, K = p.K;
+// kOcc: workgroups per CU the register budget is sized for (main kernel); the
+// accumulator-dump test hook uses 1 so it never spills.  kDmaScales: K is a
+// multiple of 512, so every row's scales for 8 groups are one aligned 16-byte
+// granule and travel by DMA; otherwise each thread loads its scale directly.
+template <bool kDump, int kOcc, bool kDmaScales>
+__global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArgs<kDump> p) {
+  // One LDS object per operand tile, scale area and raw-scale buffer of every
+  // ring stage: the compiler then sees that a DMA in flight into one object
+  // cannot alias the accesses to another and waits only for the DMA a read
+  // really depends on, instead of draining the ring before every LDS access.
+  __shared__ __attribute__((aligned(16))) uint8_t w0[kTile], w1[kTile], w2[kTile], w3[kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t a0[kTile], a1[kTile], a2[kTile], a3[kTile];
+  __shared__ __attribute__((aligned(16))) float s0[384], s1[384], s2[384], s3[384];
+  __shared__ __attribute__((aligned(16))) uint8_t raw0[4096];
+  __shared__ __attribute__((aligned(16))) uint8_t raw1[4096];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lora_smem[];
+  auto wtile = [&](int buf) -> uint8_t* { return buf == 0 ? w0 : buf == 1 ? w1 : buf == 2 ? w2 : w3; };
+  auto atile = [&](int buf) -> uint8_t* { return buf == 0 ? a0 : buf == 1 ? a1 : buf == 2 ? a2 : a3; };
+  auto sarea = [&](int buf) -> float* { return buf == 0 ? s0 : buf == 1 ? s1 : buf == 2 ? s2 : s3; };
+  auto rawbuf = [&](int b) -> uint8_t* { return (b & 1) ? raw1 : raw0; };
+
+  const int M = p.M, N = p.N, K = p.K, r = p.r;
   const int G = K >> 6;
   const int KB = K >> 1;  // bytes per packed row
-  const int tiles_n = (N + kBN - 1) / kBN;
-  const int tn = blockIdx.x % tiles_n;
-  const int tm = blockIdx.x / tiles_n;
+  int tm, tn;
+  tile_of(blockIdx.x, (M + kBM - 1) / kBM, (N + kBN - 1) / kBN, tm, tn);
   const int n0 = tn * kBN;
   const int m0 = tm * kBM;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave >> 1;  // n half of the tile
   const int wm = wave & 1;   // m half of the tile
   const int l16 = lane & 15;
   const int lseg = lane >> 4;
 
-  // staging roles: thread -> (row, half) of the 128 x 32-byte packed group tile
-  const int srow = tid >> 1;
-  const int shalf = tid & 1;
-  const int wrow_g = min(n0 + srow, N - 1);
-  const int arow_g = min(m0 + srow, M - 1);
-  const uint8_t* wsrc = p.w_codes + (size_t)wrow_g * KB + 16 * shalf;
-  const uint8_t* asrc = p.act_codes + (size_t)arow_g * KB + 16 * shalf;
-  // scale staging: threads 0..127 -> token scales, 128..255 -> weight scales
+  // DMA role: lane fills granule slot 64*wave + lane of each operand tile
+  const int slot = 64 * wave + lane;
+  const int drow = slot >> 1;
+  const int dh = (slot & 1) ^ ((drow >> 2) & 1) ^ ((drow >> 3) & 1);
+  const uint8_t* wsrc = p.w_codes + (size_t)min(n0 + drow, N - 1) * KB + 16 * dh;
+  const uint8_t* asrc = p.act_codes + (size_t)min(m0 + drow, M - 1) * KB + 16 * dh;
+  auto dma_group = [&](int g, int buf) {
+    dma16(wsrc + 32 * g, wtile(buf) + 1024 * wave);
+    dma16(asrc + 32 * g, atile(buf) + 1024 * wave);
+  };
+
+  // fragment read offsets (rows wX*64 + 16i + l16 share the swizzle of l16)
+  const int fw = gran_slot(wn * 64 + l16, lseg >> 1) * 16 + 8 * (lseg & 1);
+  const int fa = gran_slot(wm * 64 + l16, lseg >> 1) * 16 + 8 * (lseg & 1);
+
+  // scale role: threads 0..127 -> token slot tid, 128..255 -> weight row tid-128
+  // (the same rows in the raw scale area: wave w, lane l -> row 64w + l)
   const bool s_is_act = tid < kBM;
   const int s_idx = s_is_act ? tid : tid - kBM;
-  const uint16_t* ssrc = s_is_act ? p.act_scales + (size_t)min(m0 + s_idx, M - 1) * G
-                                  : p.w_scales + (size_t)min(n0 + s_idx, N - 1) * G;
-
-  uint4 wpk = *reinterpret_cast<const uint4*>(wsrc);
-  uint4 apk = *reinterpret_cast<const uint4*>(asrc);
-  uint16_t spk = kDump ? 0 : ssrc[0];
-
-  auto stage_store = [&](Stage& s, uint4 wv, uint4 av, uint16_t sv) {
-    uint4 lo, hi;
-    widen(wv, lo, hi);
-    uint4* wd = reinterpret_cast<uint4*>(s.w + srow * kStride + 32 * shalf);
-    wd[0] = uint4{lo.x, hi.x, lo.y, hi.y};
-    wd[1] = uint4{lo.z, hi.z, lo.w, hi.w};
-    widen(av, lo, hi);
-    uint4* ad = reinterpret_cast<uint4*>(s.a + srow * kStride + 32 * shalf);
-    ad[0] = uint4{lo.x, hi.x, lo.y, hi.y};
-    ad[1] = uint4{lo.z, hi.z, lo.w, hi.w};
-    if (!kDump) {
-      const float f = bf16_to_f32(sv);
-      if (s_is_act) {
-        const float sp = f * (1.0f / 256.0f);
-        const int slot = sx_slot(s_idx);
-        s.sxm[2 * slot] = sp;
-        s.sxm[2 * slot + 1] = -kMagic * sp;
-      } else {
-        s.sw[s_idx] = f;
-      }
+  const uint16_t* ssrc = nullptr;
+  if (!kDump)
+    ssrc = s_is_act ? p.act_scales + (size_t)min(m0 + sx_token(s_idx), M - 1) * G
+                    : p.w_scales + (size_t)min(n0 + s_idx, N - 1) * G;
+  // raw bf16 scales of groups 8b .. 8b+7 of every row -> raw buffer b & 1
+  auto dma_scales = [&](int b) {
+    if (kDump || !kDmaScales) return;
+    dma16(ssrc + 8 * min(b, (G - 1) >> 3), rawbuf(b) + 1024 * wave);
+  };
+  // fp32 scale of group g for this thread's row -> stage buffer `buf`; `par` is
+  // the raw-buffer parity of g's block, static at every call site
+  auto put_scale = [&](int g, int par, int buf) {
+    if (kDump) return;
+    const uint16_t h = kDmaScales
+        ? *reinterpret_cast<const uint16_t*>(rawbuf(par) + tid * 16 + (g & 7) * 2)
+        : ssrc[min(g, G - 1)];
+    const float f = __builtin_bit_cast(float, (u32)h << 16);
+    float* sp = sarea(buf);
+    if (s_is_act) {
+      const float sx = f * (1.0f / 256.0f);
+      sp[s_idx] = sx;
+      sp[128 + s_idx] = -kMagic * sx;
+    } else {
+      sp[256 + s_idx] = f;
     }
   };
 
-  stage_store(st[0], wpk, apk, spk);
-  __syncthreads();
+  // lora tiles -> LDS (kept for the epilogue), issued before anything else
+  if (!kDump && r > 0) {
+    const int tile_bytes = kBN * r * 2;  // same for lora_act (kBM == kBN)
+    for (int off = 1024 * wave; off < tile_bytes; off += 4096) {
+      const int byte = off + 16 * lane;
+      const int row = byte / (2 * r), col = byte - row * 2 * r;
+      dma16(reinterpret_cast<const uint8_t*>(p.lora_up) + (size_t)min(n0 + row, N - 1) * 2 * r + col,
+            lora_smem + off);
+      dma16(reinterpret_cast<const uint8_t*>(p.lora_act) + (size_t)min(m0 + row, M - 1) * 2 * r + col,
+            lora_smem + tile_bytes + off);
+    }
+  }
 
   v4f y[4][4];
 #pragma unroll
@@ -170,23 +251,15 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(const GemmArgs<k
     for (int j = 0; j < 4; ++j) y[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   const v4i magic = {kMagicBits, kMagicBits, kMagicBits, kMagicBits};
 
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    const bool more = g + 1 < G;
-    if (more) {
-      wpk = *reinterpret_cast<const uint4*>(wsrc + 32 * (g + 1));
-      apk = *reinterpret_cast<const uint4*>(asrc + 32 * (g + 1));
-      if (!kDump) spk = ssrc[g + 1];
-    }
-    const Stage& s = st[buf];
+  // one group from stage buffer `buf`
+  auto compute = [&](int buf, int g) {
+    const uint8_t* wt = wtile(buf);
+    const uint8_t* at = atile(buf);
     v4i wf[4], af[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      wf[i] = *reinterpret_cast<const v4i*>(s.w + (wn * 64 + 16 * i + l16) * kStride + 16 * lseg);
+    for (int i = 0; i < 4; ++i) wf[i] = widen(*reinterpret_cast<const uint2*>(wt + fw + 512 * i));
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      af[j] = *reinterpret_cast<const v4i*>(s.a + (wm * 64 + 16 * j + l16) * kStride + 16 * lseg);
-
+    for (int j = 0; j < 4; ++j) af[j] = widen(*reinterpret_cast<const uint2*>(at + fa + 512 * j));
     if constexpr (kDump) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -197,58 +270,101 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(const GemmArgs<k
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int n = n0 + wn * 64 + 16 * i + 4 * lseg + v;
-            if (m < M && n < N) p.acc[((size_t)m * N + n) * G + g] = (acc[v] - kMagicBits) >> 8;
+            const int a = acc[v];
+            if (m < M && n < N) p.acc[((size_t)m * N + n) * G + g] = (a - kMagicBits) >> 8;
           }
         }
     } else {
-      const v4f sxa = *reinterpret_cast<const v4f*>(&s.sxm[2 * (wm * 64 + l16 * 4)]);
-      const v4f sxb = *reinterpret_cast<const v4f*>(&s.sxm[2 * (wm * 64 + l16 * 4) + 4]);
-      const float sxp[4] = {sxa[0], sxa[2], sxb[0], sxb[2]};
-      const float sxc[4] = {sxa[1], sxa[3], sxb[1], sxb[3]};
+      const float* sp = sarea(buf);
+      const v4f sxp = *reinterpret_cast<const v4f*>(sp + wm * 64 + l16 * 4);
+      const v4f sxc = *reinterpret_cast<const v4f*>(sp + 128 + wm * 64 + l16 * 4);
       v4f swv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        swv[i] = *reinterpret_cast<const v4f*>(&s.sw[wn * 64 + 16 * i + 4 * lseg]);
+      for (int i = 0; i < 4; ++i) swv[i] = *reinterpret_cast<const v4f*>(sp + 256 + wn * 64 + 16 * i + 4 * lseg);
+      auto dequant = [&](int i, int j, const v4i acc) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i], af[j], magic, 0, 0, 0);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            // element copied to a scalar first: a bit-cast applied directly to
-            // an ext-vector element is lowered as a cast of element 0
-            const int bits = acc[v];
-            const float t = fmaf(__int_as_float(bits), sxp[j], sxc[j]);
-            y[i][j][v] = fmaf(t, swv[i][v], y[i][j][v]);
-          }
+        for (int v = 0; v < 4; ++v) {
+          // element copied to a scalar first: a bit-cast applied directly to
+          // an ext-vector element is lowered as a cast of element 0
+          const int bits = acc[v];
+          const float t = fmaf(__int_as_float(bits), sxp[j], sxc[j]);
+          y[i][j][v] = fmaf(t, swv[i][v], y[i][j][v]);
         }
+      };
+      v4i prev = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[0], af[0], magic, 0, 0, 0);
+#pragma unroll
+      for (int idx = 1; idx < 16; ++idx) {
+        const int i = idx >> 2, j = idx & 3;
+        const v4i cur = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i], af[j], magic, 0, 0, 0);
+        dequant((idx - 1) >> 2, (idx - 1) & 3, prev);
+        prev = cur;
+      }
+      dequant(3, 3, prev);
+      // the accumulators are complete here: keeps the compiler from deferring
+      // the dequant FMAs past the next barrier (which doubles the live registers)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) __asm__ volatile("" : "+v"(y[i][j]));
+      // keep the MFMA pipe fed while the VALU dequantizes: 1 MFMA, then 8 FMAs
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
     }
-    if (more) stage_store(st[buf ^ 1], wpk, apk, spk);
-    __syncthreads();
+  };
+
+  // Prologue: raw scales of block 0 and stages 0..2 in flight; scales of group
+  // 0 staged once block 0 has landed.
+  dma_scales(0);
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) dma_group(min(s, G - 1), s);
+  wait_vm<2 * (kStages - 1), true>();
+  barrier();
+  put_scale(0, 0, 0);
+
+  // Iteration g: stage g complete (own loads: vmcnt, everyone's: barrier); group
+  // g+3 starts loading into the buffer freed by group g-1 (preceded, every 8
+  // groups, by the raw scales of the next block); scales of group g+1 are
+  // staged; group g is computed.  Each iteration issues 2 or 3 DMAs, so after
+  // the two later iterations at least 4 younger ones exist when stage g is
+  // waited for: vmcnt(4) guarantees stage g has landed.  The body is unrolled
+  // over 16 groups so every LDS buffer index is a compile-time constant.
+  for (int b2 = 0; 16 * b2 < G; ++b2) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int g = 16 * b2 + u;
+      wait_vm<4, true>();
+      barrier();
+      if ((u & 7) == 0) dma_scales(2 * b2 + (u >> 3) + 1);
+      dma_group(min(g + kStages - 1, G - 1), (u + kStages - 1) % kStages);
+      put_scale(g + 1, ((u + 1) >> 3) & 1, (u + 1) % kStages);
+      if (g < G) compute(u % kStages, g);
+    }
   }
+  wait_vm<0, true>();
 
   if constexpr (!kDump) {
-    const int r = p.r;
-    // fused lora_up: Y^T[n, m] += lora_up[n, :] . lora_act[m, :]
+    // fused lora_up from the LDS tiles: Y^T[n, m] += lora_up[n, :] . lora_act[m, :]
     if (r > 0) {
+      const uint16_t* lu = reinterpret_cast<const uint16_t*>(lora_smem);
+      const uint16_t* la = lu + kBN * r;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int n = min(n0 + wn * 64 + 16 * i + l16, N - 1);
-        const uint16_t* up = p.lora_up + (size_t)n * r;
+        const uint16_t* up = lu + (wn * 64 + 16 * i + l16) * r;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int m = min(m0 + wm * 64 + 16 * j + l16, M - 1);
-          const uint16_t* la = p.lora_act + (size_t)m * r;
+          const uint16_t* ac = la + (wm * 64 + 16 * j + l16) * r;
           int k0 = 0;
           for (; k0 + 32 <= r; k0 += 32) {
             const v8bf a = *reinterpret_cast<const v8bf*>(up + k0 + 8 * lseg);
-            const v8bf b = *reinterpret_cast<const v8bf*>(la + k0 + 8 * lseg);
+            const v8bf b = *reinterpret_cast<const v8bf*>(ac + k0 + 8 * lseg);
             y[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, y[i][j], 0, 0, 0);
           }
           if (k0 < r) {
             const v4bf a = *reinterpret_cast<const v4bf*>(up + k0 + 4 * lseg);
-            const v4bf b = *reinterpret_cast<const v4bf*>(la + k0 + 4 * lseg);
+            const v4bf b = *reinterpret_cast<const v4bf*>(ac + k0 + 4 * lseg);
             y[i][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, y[i][j], 0, 0, 0);
           }
         }
@@ -258,21 +374,21 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(const GemmArgs<k
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int n = n0 + wn * 64 + 16 * i + 4 * lseg;
-      float b[4] = {0.f, 0.f, 0.f, 0.f};
+      float bb4[4] = {0.f, 0.f, 0.f, 0.f};
       if (p.bias != nullptr && n < N) {
         const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n);
-        b[0] = __builtin_bit_cast(float, bb.x << 16);
-        b[1] = __builtin_bit_cast(float, bb.x & 0xFFFF0000u);
-        b[2] = __builtin_bit_cast(float, bb.y << 16);
-        b[3] = __builtin_bit_cast(float, bb.y & 0xFFFF0000u);
+        bb4[0] = __builtin_bit_cast(float, bb.x << 16);
+        bb4[1] = __builtin_bit_cast(float, bb.x & 0xFFFF0000u);
+        bb4[2] = __builtin_bit_cast(float, bb.y << 16);
+        bb4[3] = __builtin_bit_cast(float, bb.y & 0xFFFF0000u);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int m = m0 + wm * 64 + 16 * j + l16;
         if (m < M && n < N) {
           uint2 o;
-          o.x = pack_bf16(y[i][j][0] + b[0], y[i][j][1] + b[1]);
-          o.y = pack_bf16(y[i][j][2] + b[2], y[i][j][3] + b[3]);
+          o.x = pack_bf16(y[i][j][0] + bb4[0], y[i][j][1] + bb4[1]);
+          o.y = pack_bf16(y[i][j][2] + bb4[2], y[i][j][3] + bb4[3]);
           *reinterpret_cast<uint2*>(p.y + (size_t)m * N + n) = o;
         }
       }
@@ -280,10 +396,20 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(const GemmArgs<k
   }
 }
 
+constexpr int kMainOcc = 2;
+
 template <bool kDump>
 hipError_t launch(const GemmArgs<kDump>& a, hipStream_t stream) {
   const int tiles = ((a.N + kBN - 1) / kBN) * ((a.M + kBM - 1) / kBM);
-  hipLaunchKernelGGL(w4a4_gemm_kernel<kDump>, dim3(tiles), dim3(kThreads), 0, stream, a);
+  const size_t lds = kDump ? 0 : (size_t)2 * kBN * a.r * 2;   // dynamic part: lora tiles
+  auto kern = (a.K % 512 == 0) ? w4a4_gemm_kernel<kDump, kDump ? 1 : kMainOcc, true>
+                               : w4a4_gemm_kernel<kDump, kDump ? 1 : kMainOcc, false>;
+  if (lds + kLoraOff > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(tiles), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -297,7 +423,7 @@ hipError_t launch_w4a4_gemm_lora_up(const uint8_t* act_codes, const uint16_t* ac
                                     hipStream_t stream) {
   if (acc_dump != nullptr) {
     GemmArgs<true> a{act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,
-                     y, acc_dump, (int)M, (int)N, (int)K, (int)r};
+                     y, acc_dump, (int)M, (int)N, (int)K, 0};
     return launch<true>(a, stream);
   }
   GemmArgs<false> a{act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,

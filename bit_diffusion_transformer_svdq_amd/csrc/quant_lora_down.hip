@@ -49,6 +49,7 @@ constexpr int kWaves = 4;
 constexpr int kRows = 16;
 constexpr int kDepth = 3;      // groups in flight per wave (X and lora_down)
 constexpr int kMuChunk = 4096; // channels whose reciprocals are staged in LDS at a time
+constexpr int kRedSlots = kWaves < 4 ? kWaves : 4;  // LDS slots of the lora partial sums
 constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
 
 __device__ __forceinline__ float lo_bf16(u32 w) { return __builtin_bit_cast(float, w << 16); }
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(kWaves * 64) void quant_lora_down_kernel(
     uint16_t* __restrict__ lora_act) {
   constexpr int R = NT * 16;
   __shared__ float mu_s[kMuChunk];
-  __shared__ float red[kWaves][kRows][NT > 0 ? R : 1];
+  __shared__ float red[kRedSlots][kRows][NT > 0 ? R : 1];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -209,18 +210,30 @@ __global__ __launch_bounds__(kWaves * 64) void quant_lora_down_kernel(
   }
 
   if constexpr (NT > 0) {
-    // lane l holds rows 4*(l/16)+v, rank 16t + l%16
+    // lane l holds rows 4*(l/16)+v, rank 16t + l%16.  Waves w, w + kRedSlots,
+    // ... are added into slot w in a fixed order (highest first), then the
+    // slots are summed in order: the result does not depend on timing.
+    constexpr int kPhases = kWaves / kRedSlots;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int ph = kPhases - 1; ph >= 0; --ph) {
+      if (wave / kRedSlots == ph) {
+        float(*dst)[NT > 0 ? R : 1] = red[wave % kRedSlots];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[wave][4 * seg + v][16 * t + rho] = lacc[t][v];
-    __syncthreads();
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float& d = dst[4 * seg + v][16 * t + rho];
+            d = (ph == kPhases - 1) ? lacc[t][v] : d + lacc[t][v];
+          }
+      }
+      __syncthreads();
+    }
     for (int idx = threadIdx.x; idx < kRows * R; idx += kWaves * 64) {
       const int rr = idx / R;
       const int j = idx - rr * R;
       float sum = red[0][rr][j];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) sum += red[w][rr][j];
+      for (int w = 1; w < kRedSlots; ++w) sum += red[w][rr][j];
       if (row0 + rr < M) lora_act[(size_t)(row0 + rr) * R + j] = (uint16_t)(pack_bf16(sum, 0.f) & 0xFFFFu);
     }
   }

@@ -13,18 +13,23 @@
 // layout (lane l: column l%16, rows 4*(l/16) + v) every lane then owns four
 // consecutive n of one token row m, so Y rows are written 8 bytes at a time.
 //
-// Data movement.  The packed int4 tiles (128 rows x 32 bytes per operand and
-// group) go from memory straight into LDS with global_load_lds_dwordx4, no
-// registers involved, through a ring of kStages stages: group g+3 is in flight
-// while group g is computed, with one barrier per group.  Vector-memory
-// counters retire in issue order, so the wait for stage g is an explicit
-// s_waitcnt vmcnt(4) (the two later stages' loads may stay in flight).  Inside
-// an operand tile the two 16-byte granules of row r sit at slots
-// 2r + (h ^ r[2] ^ r[3]), which makes the 8-byte fragment reads conflict free
-// for 32 and 64 LDS banks.  Scales come 8 groups at a time (one 16-byte load
-// per thread and block), are converted once per workgroup and written to the
-// stage one group ahead.  The lora_up and lora_act tiles are loaded into LDS at
-// kernel start, so the epilogue does not wait for memory.
+// Data movement.  The packed int4 codes go from memory straight into LDS with
+// global_load_lds_dwordx4 (no registers involved), two quant groups at a time:
+// each instruction moves 64 contiguous bytes of each of 16 rows.  Runs of 32
+// bytes per row halve what the L2 delivers (measured on the whole chip: about
+// 7 TB/s against 14 TB/s for 64-byte runs), so a ring stage holds a pair of
+// groups (128 rows x 64 bytes per operand).  Pairs q+1 and q+2 are in flight
+// while pair q is computed, with one barrier per pair.  Vector-memory counters
+// retire in issue order, so the wait for stage q is an explicit
+// s_waitcnt vmcnt(4): the four DMAs of the next pair, issued last in every
+// iteration, may stay in flight.  Inside a stage, the 16-byte granule gg (0..3)
+// of row r sits at slot 4r + (gg ^ r[3:2]), which keeps the 8-byte fragment
+// reads free of bank conflicts.  Each of the first 256 threads owns the scales
+// of one token or weight row: it loads those of pair q+3 into a register ring
+// (before the pair's DMAs, so waiting for them never waits for the DMAs) and
+// stores the converted scales of pair q+1 into the stage one pair ahead.  The
+// lora_up and lora_act tiles are loaded into LDS at kernel start, so the
+// epilogue does not wait for memory.
 //
 // Main loop, per 64-wide group g and wave (64 n x 64 m, 4 x 4 MFMA tiles):
 //  * fragments: 8-byte LDS reads; nibbles widened to int8 as 16*q with
@@ -41,7 +46,8 @@
 // The int32 group accumulator itself is exact; the debug variant of this
 // kernel stores (bits - 0x4B400000) >> 8 instead of dequantizing.
 //
-// Workgroup: 256 threads (4 waves as 2 x 2), tile 128 n x 128 m.
+// Workgroup: 256 threads (4 waves as 2 x 2), tile 128 n x 128 m, two
+// workgroups per CU.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -64,10 +70,10 @@ typedef __attribute__((address_space(1))) void glb_void;
 constexpr int kBN = 128;            // weight rows (n) per workgroup
 constexpr int kBM = 128;            // token rows (m) per workgroup
 constexpr int kThreads = 256;
-constexpr int kStages = 4;          // LDS ring depth, in groups
-constexpr int kTile = 128 * 32;     // packed bytes of one operand tile for one group
-constexpr int kStageBytes = 2 * kTile + 3 * 128 * 4;  // W tile, A tile, sxp/sxc/sw (128 each)
-constexpr int kLoraOff = kStages * kStageBytes + 2 * 256 * 16;  // static LDS before the lora tiles
+constexpr int kStages = 3;          // LDS ring depth, in group pairs
+constexpr int kTile = 128 * 64;     // packed bytes of one operand tile for one group pair
+constexpr int kScale = 512;         // floats per stage: per group, s_x/256 (128) and s_w (128)
+constexpr int kStaticLds = kStages * (2 * kTile + 4 * kScale);
 constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 constexpr u32 kNib = 0xF0F0F0F0u;
@@ -82,11 +88,6 @@ __device__ __forceinline__ u32 pack_bf16(float a, float b) {
 // m = wm*64 + 16j + l%16 it owns, as one contiguous 16-byte LDS read.
 __device__ __forceinline__ int sx_token(int p) {
   return (p >> 6) * 64 + (p & 3) * 16 + ((p >> 2) & 15);
-}
-
-// 16-byte granule slot of (row r, granule h) inside an operand tile.
-__device__ __forceinline__ int gran_slot(int r, int h) {
-  return 2 * r + (h ^ ((r >> 2) & 1) ^ ((r >> 3) & 1));
 }
 
 // wait until at most n vector-memory operations of this wave are outstanding
@@ -148,30 +149,26 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   tn = in / rows;
 }
 
-// kOcc: workgroups per CU the register budget is sized for (main kernel); the
-// accumulator-dump test hook uses 1 so it never spills.  kDmaScales: K is a
-// multiple of 512, so every row's scales for 8 groups are one aligned 16-byte
-// granule and travel by DMA; otherwise each thread loads its scale directly.
-template <bool kDump, int kOcc, bool kDmaScales>
+// kOcc: waves per SIMD the register budget is sized for (main kernel); the
+// accumulator-dump test hook uses 1 so it never spills.
+template <bool kDump, int kOcc>
 __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArgs<kDump> p) {
-  // One LDS object per operand tile, scale area and raw-scale buffer of every
-  // ring stage: the compiler then sees that a DMA in flight into one object
-  // cannot alias the accesses to another and waits only for the DMA a read
-  // really depends on, instead of draining the ring before every LDS access.
-  __shared__ __attribute__((aligned(16))) uint8_t w0[kTile], w1[kTile], w2[kTile], w3[kTile];
-  __shared__ __attribute__((aligned(16))) uint8_t a0[kTile], a1[kTile], a2[kTile], a3[kTile];
-  __shared__ __attribute__((aligned(16))) float s0[384], s1[384], s2[384], s3[384];
-  __shared__ __attribute__((aligned(16))) uint8_t raw0[4096];
-  __shared__ __attribute__((aligned(16))) uint8_t raw1[4096];
+  // One LDS object per operand tile and scale area of every ring stage: the
+  // compiler then sees that a DMA in flight into one object cannot alias the
+  // accesses to another and waits only for the DMA a read really depends on,
+  // instead of draining the ring before every LDS access.
+  __shared__ __attribute__((aligned(16))) uint8_t w0[kTile], w1[kTile], w2[kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t a0[kTile], a1[kTile], a2[kTile];
+  __shared__ __attribute__((aligned(16))) float s0[kScale], s1[kScale], s2[kScale];
   extern __shared__ __attribute__((aligned(16))) uint8_t lora_smem[];
-  auto wtile = [&](int buf) -> uint8_t* { return buf == 0 ? w0 : buf == 1 ? w1 : buf == 2 ? w2 : w3; };
-  auto atile = [&](int buf) -> uint8_t* { return buf == 0 ? a0 : buf == 1 ? a1 : buf == 2 ? a2 : a3; };
-  auto sarea = [&](int buf) -> float* { return buf == 0 ? s0 : buf == 1 ? s1 : buf == 2 ? s2 : s3; };
-  auto rawbuf = [&](int b) -> uint8_t* { return (b & 1) ? raw1 : raw0; };
+  auto wtile = [&](int buf) -> uint8_t* { return buf == 0 ? w0 : buf == 1 ? w1 : w2; };
+  auto atile = [&](int buf) -> uint8_t* { return buf == 0 ? a0 : buf == 1 ? a1 : a2; };
+  auto sarea = [&](int buf) -> float* { return buf == 0 ? s0 : buf == 1 ? s1 : s2; };
 
   const int M = p.M, N = p.N, K = p.K, r = p.r;
   const int G = K >> 6;
-  const int KB = K >> 1;  // bytes per packed row
+  const int P = (G + 1) >> 1;  // group pairs
+  const int KB = K >> 1;       // bytes per packed row
   int tm, tn;
   tile_of(blockIdx.x, (M + kBM - 1) / kBM, (N + kBN - 1) / kBN, tm, tn);
   const int n0 = tn * kBN;
@@ -185,50 +182,62 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
   const int l16 = lane & 15;
   const int lseg = lane >> 4;
 
-  // DMA role: lane fills granule slot 64*wave + lane of each operand tile
-  const int slot = 64 * wave + lane;
-  const int drow = slot >> 1;
-  const int dh = (slot & 1) ^ ((drow >> 2) & 1) ^ ((drow >> 3) & 1);
-  const uint8_t* wsrc = p.w_codes + (size_t)min(n0 + drow, N - 1) * KB + 16 * dh;
-  const uint8_t* asrc = p.act_codes + (size_t)min(m0 + drow, M - 1) * KB + 16 * dh;
-  auto dma_group = [&](int g, int buf) {
-    dma16(wsrc + 32 * g, wtile(buf) + 1024 * wave);
-    dma16(asrc + 32 * g, atile(buf) + 1024 * wave);
+  // DMA role: instruction k (0, 1) of a wave fills slots 256k + 64*wave + lane
+  // of each operand tile, i.e. row s >> 2, granule (s & 3) ^ r[3:2]: four lanes
+  // cover the 64 bytes of one row.  32-bit lane offsets from the kernel
+  // arguments (codes arrays are below 2 GiB).
+  u32 woff[2], aoff[2], gsel[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int s = 256 * k + 64 * wave + lane;
+    const int row = s >> 2;
+    gsel[k] = (u32)((s & 3) ^ ((row >> 2) & 3));
+    woff[k] = (u32)min(n0 + row, N - 1) * (u32)KB + 16u * (gsel[k] & 1u);
+    aoff[k] = (u32)min(m0 + row, M - 1) * (u32)KB + 16u * (gsel[k] & 1u);
+  }
+  // group pair q -> stage buffer buf (the second group clamped to the last one)
+  auto dma_pair = [&](int q, int buf) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const u32 col = 32u * (u32)min(2 * q + (int)(gsel[k] >> 1), G - 1);
+      dma16(p.w_codes + (woff[k] + col), wtile(buf) + 4096 * k + 1024 * wave);
+      dma16(p.act_codes + (aoff[k] + col), atile(buf) + 4096 * k + 1024 * wave);
+    }
   };
 
-  // fragment read offsets (rows wX*64 + 16i + l16 share the swizzle of l16)
-  const int fw = gran_slot(wn * 64 + l16, lseg >> 1) * 16 + 8 * (lseg & 1);
-  const int fa = gran_slot(wm * 64 + l16, lseg >> 1) * 16 + 8 * (lseg & 1);
+  // Fragment read offsets for the first group of a pair: row R, granule
+  // lseg >> 1, 8-byte half lseg & 1.  The rows of fragment i (R + 16i) share
+  // the swizzle R[3:2] of R = wX*64 + l16, and the second group of the pair
+  // sits 32 bytes away (granule + 2 flips bit 1 of the slot): offset ^ 32.
+  const int fsw = (l16 >> 2) & 3;
+  const int fw = 64 * (wn * 64 + l16) + 16 * ((lseg >> 1) ^ fsw) + 8 * (lseg & 1);
+  const int fa = 64 * (wm * 64 + l16) + 16 * ((lseg >> 1) ^ fsw) + 8 * (lseg & 1);
 
   // scale role: threads 0..127 -> token slot tid, 128..255 -> weight row tid-128
-  // (the same rows in the raw scale area: wave w, lane l -> row 64w + l)
   const bool s_is_act = tid < kBM;
   const int s_idx = s_is_act ? tid : tid - kBM;
-  const uint16_t* ssrc = nullptr;
-  if (!kDump)
-    ssrc = s_is_act ? p.act_scales + (size_t)min(m0 + sx_token(s_idx), M - 1) * G
-                    : p.w_scales + (size_t)min(n0 + s_idx, N - 1) * G;
-  // raw bf16 scales of groups 8b .. 8b+7 of every row -> raw buffer b & 1
-  auto dma_scales = [&](int b) {
-    if (kDump || !kDmaScales) return;
-    dma16(ssrc + 8 * min(b, (G - 1) >> 3), rawbuf(b) + 1024 * wave);
-  };
-  // fp32 scale of group g for this thread's row -> stage buffer `buf`; `par` is
-  // the raw-buffer parity of g's block, static at every call site
-  auto put_scale = [&](int g, int par, int buf) {
+  const uint16_t* sbase = s_is_act ? p.act_scales : p.w_scales;  // wave-uniform
+  const u32 soff = (u32)(s_is_act ? min(m0 + sx_token(s_idx), M - 1) : min(n0 + s_idx, N - 1)) * (u32)G;
+  // register ring of raw bf16 scales, pair q in slot q % 3
+  u32 slo[3], shi[3];
+  auto load_scales = [&](int q, int k) {
     if (kDump) return;
-    const uint16_t h = kDmaScales
-        ? *reinterpret_cast<const uint16_t*>(rawbuf(par) + tid * 16 + (g & 7) * 2)
-        : ssrc[min(g, G - 1)];
-    const float f = __builtin_bit_cast(float, (u32)h << 16);
-    float* sp = sarea(buf);
-    if (s_is_act) {
-      const float sx = f * (1.0f / 256.0f);
-      sp[s_idx] = sx;
-      sp[128 + s_idx] = -kMagic * sx;
-    } else {
-      sp[256 + s_idx] = f;
-    }
+    slo[k] = sbase[soff + (u32)min(2 * q, G - 1)];
+    shi[k] = sbase[soff + (u32)min(2 * q + 1, G - 1)];
+  };
+  // converted scales of pair q (ring slot k) -> stage buffer `buf`: per group
+  // h, s_x/256 of the token slot (floats 256h + 0..127) or s_w of the weight
+  // row (256h + 128..255)
+  auto put_scale = [&](int q, int k, int buf) {
+    if (kDump) return;
+    u32 o = 4u * (u32)(s_is_act ? s_idx : 128 + s_idx);
+    __asm__ volatile("" : "+v"(o));  // keeps the per-stage addresses out of registers
+    uint8_t* sp = reinterpret_cast<uint8_t*>(sarea(buf)) + o;
+    const float f0 = __builtin_bit_cast(float, slo[k] << 16);
+    const float f1 = __builtin_bit_cast(float, shi[k] << 16);
+    *reinterpret_cast<float*>(sp) = s_is_act ? f0 * (1.0f / 256.0f) : f0;
+    *reinterpret_cast<float*>(sp + 1024) = s_is_act ? f1 * (1.0f / 256.0f) : f1;
+    (void)q;
   };
 
   // lora tiles -> LDS (kept for the epilogue), issued before anything else
@@ -251,96 +260,122 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
     for (int j = 0; j < 4; ++j) y[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   const v4i magic = {kMagicBits, kMagicBits, kMagicBits, kMagicBits};
 
-  // one group from stage buffer `buf`
-  auto compute = [&](int buf, int g) {
+  // One group pair from stage buffer `buf`: the LDS reads of both groups are
+  // issued up front, so those of the second overlap the first one's compute.
+  auto compute_pair = [&](int buf, int q) {
     const uint8_t* wt = wtile(buf);
     const uint8_t* at = atile(buf);
-    v4i wf[4], af[4];
+    const int ng = min(2, G - 2 * q);  // groups in this pair (1 for an odd tail)
+    uint2 rw[2][4], ra[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wf[i] = widen(*reinterpret_cast<const uint2*>(wt + fw + 512 * i));
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) af[j] = widen(*reinterpret_cast<const uint2*>(at + fa + 512 * j));
-    if constexpr (kDump) {
+      for (int i = 0; i < 4; ++i) rw[h][i] = *reinterpret_cast<const uint2*>(wt + (fw ^ (32 * h)) + 1024 * i);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j) ra[h][j] = *reinterpret_cast<const uint2*>(at + (fa ^ (32 * h)) + 1024 * j);
+    }
+    v4f sxp[2], swv[2][4];
+    if constexpr (!kDump) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i], af[j], magic, 0, 0, 0);
-          const int m = m0 + wm * 64 + 16 * j + l16;
+      for (int h = 0; h < 2; ++h) {
+        const float* sp = sarea(buf) + 256 * h;
+        sxp[h] = *reinterpret_cast<const v4f*>(sp + wm * 64 + l16 * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) swv[h][i] = *reinterpret_cast<const v4f*>(sp + 128 + wn * 64 + 16 * i + 4 * lseg);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h >= ng) break;
+      v4i wf[4], af[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wf[i] = widen(rw[h][i]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) af[j] = widen(ra[h][j]);
+      if constexpr (kDump) {
+        const int g = 2 * q + h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i], af[j], magic, 0, 0, 0);
+            const int m = m0 + wm * 64 + 16 * j + l16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int n = n0 + wn * 64 + 16 * i + 4 * lseg + v;
+              const int a = acc[v];
+              if (m < M && n < N) p.acc[((size_t)m * N + n) * G + g] = (a - kMagicBits) >> 8;
+            }
+          }
+      } else {
+        const v4f sx = sxp[h];
+        const v4f sc = sx * -kMagic;
+        auto dequant = [&](int i, int j, const v4i acc) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int n = n0 + wn * 64 + 16 * i + 4 * lseg + v;
-            const int a = acc[v];
-            if (m < M && n < N) p.acc[((size_t)m * N + n) * G + g] = (a - kMagicBits) >> 8;
+            // element copied to a scalar first: a bit-cast applied directly to
+            // an ext-vector element is lowered as a cast of element 0
+            const int bits = acc[v];
+            const float t = fmaf(__int_as_float(bits), sx[j], sc[j]);
+            y[i][j][v] = fmaf(t, swv[h][i][v], y[i][j][v]);
           }
+        };
+        // each tile is dequantized two MFMAs after its own, so its result has
+        // long landed when the FMAs read it
+        v4i p2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[0], af[0], magic, 0, 0, 0);
+        v4i p1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[0], af[1], magic, 0, 0, 0);
+#pragma unroll
+        for (int idx = 2; idx < 16; ++idx) {
+          const int i = idx >> 2, j = idx & 3;
+          const v4i cur = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i], af[j], magic, 0, 0, 0);
+          dequant((idx - 2) >> 2, (idx - 2) & 3, p2);
+          p2 = p1;
+          p1 = cur;
         }
-    } else {
-      const float* sp = sarea(buf);
-      const v4f sxp = *reinterpret_cast<const v4f*>(sp + wm * 64 + l16 * 4);
-      const v4f sxc = *reinterpret_cast<const v4f*>(sp + 128 + wm * 64 + l16 * 4);
-      v4f swv[4];
+        dequant(3, 2, p2);
+        dequant(3, 3, p1);
+        // the accumulators are complete here: keeps the compiler from deferring
+        // the dequant FMAs past the next barrier (which doubles the live registers)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) swv[i] = *reinterpret_cast<const v4f*>(sp + 256 + wn * 64 + 16 * i + 4 * lseg);
-      auto dequant = [&](int i, int j, const v4i acc) {
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          // element copied to a scalar first: a bit-cast applied directly to
-          // an ext-vector element is lowered as a cast of element 0
-          const int bits = acc[v];
-          const float t = fmaf(__int_as_float(bits), sxp[j], sxc[j]);
-          y[i][j][v] = fmaf(t, swv[i][v], y[i][j][v]);
+          for (int j = 0; j < 4; ++j) __asm__ volatile("" : "+v"(y[i][j]));
+        // keep the MFMA pipe fed while the VALU dequantizes: 1 MFMA, then 8 FMAs
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
         }
-      };
-      v4i prev = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[0], af[0], magic, 0, 0, 0);
-#pragma unroll
-      for (int idx = 1; idx < 16; ++idx) {
-        const int i = idx >> 2, j = idx & 3;
-        const v4i cur = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i], af[j], magic, 0, 0, 0);
-        dequant((idx - 1) >> 2, (idx - 1) & 3, prev);
-        prev = cur;
-      }
-      dequant(3, 3, prev);
-      // the accumulators are complete here: keeps the compiler from deferring
-      // the dequant FMAs past the next barrier (which doubles the live registers)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) __asm__ volatile("" : "+v"(y[i][j]));
-      // keep the MFMA pipe fed while the VALU dequantizes: 1 MFMA, then 8 FMAs
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
       }
     }
   };
 
-  // Prologue: raw scales of block 0 and stages 0..2 in flight; scales of group
-  // 0 staged once block 0 has landed.
-  dma_scales(0);
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) dma_group(min(s, G - 1), s);
-  wait_vm<2 * (kStages - 1), true>();
-  barrier();
+  // Prologue, in issue order: scales of pairs 0 and 1, pair 0, scales of pair
+  // 2, pair 1.  Iteration q then issues the scales of pair q+3 and, last, the
+  // 4 DMAs of pair q+2, so vmcnt(4) at the top of iteration q means that pair q
+  // and the scales of pairs up to q+2 have landed.
+  load_scales(0, 0);
+  load_scales(1, 1);
+  dma_pair(0, 0);
+  load_scales(2, 2);
+  dma_pair(min(1, P - 1), 1);
   put_scale(0, 0, 0);
 
-  // Iteration g: stage g complete (own loads: vmcnt, everyone's: barrier); group
-  // g+3 starts loading into the buffer freed by group g-1 (preceded, every 8
-  // groups, by the raw scales of the next block); scales of group g+1 are
-  // staged; group g is computed.  Each iteration issues 2 or 3 DMAs, so after
-  // the two later iterations at least 4 younger ones exist when stage g is
-  // waited for: vmcnt(4) guarantees stage g has landed.  The body is unrolled
-  // over 16 groups so every LDS buffer index is a compile-time constant.
-  for (int b2 = 0; 16 * b2 < G; ++b2) {
+  // Iteration q: stage q complete (own loads: vmcnt, everyone's: barrier); the
+  // scales of pair q+3 go into the ring slot pair q has freed; pair q+2 starts
+  // loading into the stage freed by pair q-1; the scales of pair q+1 are
+  // staged; pair q is computed.  The body is unrolled over the 3 stages so
+  // every LDS buffer and register-ring index is a compile-time constant.
+  for (int q0 = 0; q0 < P; q0 += 3) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int g = 16 * b2 + u;
+    for (int u = 0; u < 3; ++u) {
+      const int q = q0 + u;
       wait_vm<4, true>();
       barrier();
-      if ((u & 7) == 0) dma_scales(2 * b2 + (u >> 3) + 1);
-      dma_group(min(g + kStages - 1, G - 1), (u + kStages - 1) % kStages);
-      put_scale(g + 1, ((u + 1) >> 3) & 1, (u + 1) % kStages);
-      if (g < G) compute(u % kStages, g);
+      load_scales(min(q + 3, P - 1), u);
+      dma_pair(min(q + 2, P - 1), (u + 2) % 3);
+      put_scale(q + 1, (u + 1) % 3, (u + 1) % 3);
+      if (q < P) compute_pair(u, q);
     }
   }
   wait_vm<0, true>();
@@ -396,15 +431,14 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
   }
 }
 
-constexpr int kMainOcc = 2;
+constexpr int kMainOcc = 2;  // waves per SIMD the registers are sized for
 
 template <bool kDump>
 hipError_t launch(const GemmArgs<kDump>& a, hipStream_t stream) {
   const int tiles = ((a.N + kBN - 1) / kBN) * ((a.M + kBM - 1) / kBM);
   const size_t lds = kDump ? 0 : (size_t)2 * kBN * a.r * 2;   // dynamic part: lora tiles
-  auto kern = (a.K % 512 == 0) ? w4a4_gemm_kernel<kDump, kDump ? 1 : kMainOcc, true>
-                               : w4a4_gemm_kernel<kDump, kDump ? 1 : kMainOcc, false>;
-  if (lds + kLoraOff > 65536) {
+  auto kern = w4a4_gemm_kernel<kDump, kDump ? 1 : kMainOcc>;
+  if (lds + kStaticLds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;

@@ -161,7 +161,7 @@ def main():
     ap.add_argument("--config", default="mlp_up")
     ap.add_argument("--m", type=int, default=0, help="override the token count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=320)
     ap.add_argument("--extra", default="", help="write per-kernel details of extra shapes here (JSON)")
     ap.add_argument("--extra-configs", default="attn_out,qkv,mlp_down")
     ap.add_argument("--extra-m", default="64,256,1024")

@@ -186,7 +186,25 @@ __global__ __launch_bounds__(kWaves * 64) void quant_lora_down_kernel(
     const int g0 = k0 >> 6;
     const int gc = kc >> 6;
     __syncthreads();  // previous chunk's mu fully consumed
-    for (int i = threadIdx.x; i < kc; i += kWaves * 64) mu_s[i] = 1.0f / lam[k0 + i];
+    {
+      // all loads of lambda first (16 bytes per thread and step), then the
+      // divisions: one memory round trip instead of one per element
+      constexpr int kPer = (kMuChunk / 4 + kWaves * 64 - 1) / (kWaves * 64);
+      const float4* lam4 = reinterpret_cast<const float4*>(lam + k0);
+      float4 lv[kPer];
+#pragma unroll
+      for (int c = 0; c < kPer; ++c) {
+        const int i = threadIdx.x + c * kWaves * 64;
+        if (i < (kc >> 2)) lv[c] = lam4[i];
+      }
+#pragma unroll
+      for (int c = 0; c < kPer; ++c) {
+        const int i = threadIdx.x + c * kWaves * 64;
+        if (i < (kc >> 2))
+          reinterpret_cast<float4*>(mu_s)[i] =
+              float4{1.0f / lv[c].x, 1.0f / lv[c].y, 1.0f / lv[c].z, 1.0f / lv[c].w};
+      }
+    }
     __syncthreads();
 
     Slot<NT> ring[kDepth];
@@ -200,10 +218,12 @@ __global__ __launch_bounds__(kWaves * 64) void quant_lora_down_kernel(
       for (int s = 0; s < kDepth; ++s) {
         const int gl = base + kWaves * s;
         if (gl < gc) {
-          const Slot<NT> cur = ring[s];
+          // consume the slot in place, then refill it: refilling first would
+          // make the compiler copy the slot, and the copy waits for every load
+          // in flight (loads retire in issue order), draining the ring
+          quant_group<NT>(ring[s], mu_s + 64 * gl, g0 + gl, seg, row_ok, crow, srow, lacc);
           const int gn = gl + kWaves * kDepth;
           if (gn < gc) fetch<NT>(ring[s], xrow, lrow, K, g0 + gn);
-          quant_group<NT>(cur, mu_s + 64 * gl, g0 + gl, seg, row_ok, crow, srow, lacc);
         }
       }
     }

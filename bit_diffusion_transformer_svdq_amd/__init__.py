@@ -22,7 +22,8 @@ import numpy as np
 from ._lib import SvdqError, check, lib
 
 __all__ = ["SvdqError", "lib", "check_device", "quantize_act_lora_down", "w4a4_gemm_lora_up",
-           "w4a4_group_acc_debug", "smooth_from_absmax", "pack_weights", "GROUP_SIZE"]
+           "w4a4_group_acc_debug", "debug_set_quant_plan", "smooth_from_absmax", "pack_weights",
+           "GROUP_SIZE"]
 
 GROUP_SIZE = 64
 
@@ -85,6 +86,11 @@ def quantize_act_lora_down(x, smooth, lora_down=None, out=None, stream=None):
         _ptr(codes), _ptr(scales), _ptr(lora_act) if r else None, _stream(stream))
     check(st, "svdq_quantize_act_lora_down")
     return codes, scales, lora_act
+
+
+def debug_set_quant_plan(k_blocks: int = 0, tiles_per_wg: int = 0) -> None:
+    """Test hook: force call 1's work split for later calls (0 = automatic)."""
+    check(lib().svdq_debug_set_quant_plan(int(k_blocks), int(tiles_per_wg)), "svdq_debug_set_quant_plan")
 
 
 def w4a4_gemm_lora_up(act_codes, act_scales, w_codes, w_scales, lora_act=None, lora_up=None,

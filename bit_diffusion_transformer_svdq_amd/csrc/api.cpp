@@ -141,6 +141,14 @@ svdq_status svdq_quantize_act_lora_down(const void* x, const float* smooth, cons
   return ok();
 }
 
+svdq_status svdq_debug_set_quant_plan(int k_blocks, int tiles_per_wg) {
+  if (k_blocks < 0 || tiles_per_wg < 0 || tiles_per_wg > 12)
+    return fail(SVDQ_STATUS_INVALID_VALUE, "bad plan k_blocks=%d tiles_per_wg=%d (need >= 0, tiles <= 12)",
+                k_blocks, tiles_per_wg);
+  svdq::set_quant_plan_override(k_blocks, tiles_per_wg);
+  return ok();
+}
+
 static svdq_status validate_gemm(const void* act_codes, const void* w_codes, int64_t M, int64_t N,
                                  int64_t K, int64_t r, int64_t group_size) {
   if (M < 0 || N <= 0 || K <= 0 || r < 0 || group_size <= 0)

@@ -11,16 +11,30 @@
 // branch.  X is read from HBM once; x_hat feeds both the quantizer and the
 // bf16 MFMA of the down-projection from registers.
 //
-// Work split.  A workgroup owns 16 rows and the full K; its 4 waves take the
-// 64-wide groups round-robin (wave w: groups w, w+4, ...), each wave keeping
-// three groups (X and the matching lora_down fragments) in flight.  Lane l of a wave
-// covers row (l % 16) and, inside each group, the two 8-element runs
-// k = 8*(l/16) + {0..7} and 32 + 8*(l/16) + {0..7}: one global load of 16 bytes
-// per run, 64 contiguous bytes per row per load instruction, and exactly the
-// A-operand fragment of v_mfma_f32_16x16x32_bf16.  The group maximum combines
-// the four lanes of a row with two cross-lane exchanges.  The per-wave lora
-// partials are summed over the 4 waves in LDS in a fixed order, so results are
-// deterministic.
+// Work split.  The [M, K] problem is cut into cells of 16 rows (a row tile) by
+// one 64-wide group.  A workgroup owns a block of TB row tiles by GB
+// consecutive groups (one K-block); wave w of the workgroup owns row tile w of
+// the block and walks the block's groups with a ring of X loads in flight.
+// The host picks (TB, GB) so that the blocks spread evenly over the compute
+// units: at M = 4608, K = 3072 that is 7 tiles x 8 groups, 252 workgroups with
+// 56 cells each.  A row-only split (16 rows x all of K per workgroup) gives 288
+// equal workgroups on 256 CUs, and the 32 CUs that get two of them set the
+// kernel time.  The K-block's lora_down slice (GB groups x r ranks, in MFMA
+// B-fragment order) and its reciprocals mu sit in LDS and serve all TB waves,
+// so L1 is read once per workgroup instead of once per 16 rows.
+//
+// Lane l of a wave covers row (l % 16) and, inside each group, the two
+// 8-element runs k = 8*(l/16) + {0..7} and 32 + 8*(l/16) + {0..7}: one 16-byte
+// load per run, 64 contiguous bytes per row per load instruction, and exactly
+// the A-operand fragment of v_mfma_f32_16x16x32_bf16.  The group maximum
+// combines the four lanes of a row with two cross-lane exchanges.
+//
+// lora reduction over K-blocks.  With more than one K-block, each wave writes
+// its fp32 partial (16 rows x r) to a workspace slot of its own with
+// agent-coherent stores, waits for them to complete, then bumps the tile's
+// arrival counter.  The wave that arrives last reads the tile's partials with
+// agent-coherent loads, adds them in K-block order and writes lora_act, so the
+// result does not depend on timing; the counter wraps back to zero.
 //
 // Rounding (bit-exact by construction): mu = fl32(1/lambda) by IEEE division,
 // once per workgroup and channel, kept in LDS;
@@ -33,6 +47,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "svdq_internal.h"
 
 namespace svdq {
@@ -44,13 +63,19 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned int u32;
 typedef u32 v4u __attribute__((ext_vector_type(4)));
+typedef u32 v2u32 __attribute__((ext_vector_type(2)));
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kRows = 16;
-constexpr int kDepth = 3;      // groups in flight per wave (X and lora_down)
-constexpr int kMuChunk = 4096; // channels whose reciprocals are staged in LDS at a time
-constexpr int kRedSlots = kWaves < 4 ? kWaves : 4;  // LDS slots of the lora partial sums
+constexpr int kMaxTiles = 12;     // row tiles (= waves) per workgroup
+constexpr int kMaxGB = 64;        // groups per K-block (reciprocals held in LDS)
+constexpr int kLdsLimit = 160 * 1024;
+constexpr int kMuBytes = kMaxGB * 64 * 4;
 constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
+constexpr float kRcp7 = 1.0f / 7.0f;        // fl32(1/7)
+
+// groups of X in flight per wave; fewer for large ranks (more fragment registers)
+template <int NT>
+constexpr int depth_for() { return NT <= 2 ? 6 : (NT <= 4 ? 4 : 3); }
 
 __device__ __forceinline__ float lo_bf16(u32 w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float hi_bf16(u32 w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
@@ -61,46 +86,38 @@ __device__ __forceinline__ u32 pack_bf16(float a, float b) {
   return __builtin_bit_cast(u32, __builtin_convertvector(f, v2bf));
 }
 
-// Packed data of one group for one lane, fetched kDepth groups ahead: the two
-// 16-byte runs of X and the lane's lora_down fragments (B operand of the bf16
-// MFMA: rank 16t + l%16, the same k runs as X).
-template <int NT>
-struct Slot {
-  uint4 xa, xb;
-  v8bf lb[NT > 0 ? NT : 1][2];
+struct QuantArgs {
+  const uint16_t* x;
+  const float* lam;
+  const uint16_t* lora_down;
+  uint8_t* codes;
+  uint16_t* scales;
+  uint16_t* lora_act;
+  float* part;      // [KB][T][NT][4][64 lanes] partial sums (KB > 1 and r > 0)
+  u32* count;       // [T] arrival counters, zero between launches
+  int M, K, T, G;   // T = row tiles, G = groups of 64
+  int GB, TB, KB;   // groups per K-block, row tiles per workgroup, K-blocks
 };
 
-template <int NT>
-__device__ __forceinline__ void fetch(Slot<NT>& sl, const uint16_t* xrow, const uint16_t* lrow,
-                                      int K, int g) {
-  sl.xa = *reinterpret_cast<const uint4*>(xrow + 64 * g);
-  sl.xb = *reinterpret_cast<const uint4*>(xrow + 64 * g + 32);
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const uint16_t* l = lrow + (size_t)16 * t * K + 64 * g;
-    sl.lb[t][0] = *reinterpret_cast<const v8bf*>(l);
-    sl.lb[t][1] = *reinterpret_cast<const v8bf*>(l + 32);
-  }
-}
-
 // One 64-wide group of one wave: smooth, quantize, pack, store, and accumulate
-// the lora_down partial.  mu_g points at the 64 reciprocals of this group.
+// the lora_down partial.  mu_g points at the group's 64 reciprocals in LDS and
+// lf_g at its lora_down fragments in LDS ([NT][2 halves][64 lanes]).
 template <int NT>
-__device__ __forceinline__ void quant_group(const Slot<NT>& sl, const float* mu_g, int g, int seg,
-                                            bool row_ok, uint8_t* crow, uint16_t* srow_out,
-                                            v4f* lacc) {
+__device__ __forceinline__ void quant_group(const uint4& xa, const uint4& xb, const float* mu_g,
+                                            const v8bf* lf_g, int g, int lane, bool row_ok,
+                                            uint8_t* crow, uint16_t* srow, v4f* lacc) {
+  const int seg = lane >> 4;
   const v4f m0a = *reinterpret_cast<const v4f*>(mu_g + 8 * seg);
   const v4f m0b = *reinterpret_cast<const v4f*>(mu_g + 8 * seg + 4);
   const v4f m1a = *reinterpret_cast<const v4f*>(mu_g + 32 + 8 * seg);
   const v4f m1b = *reinterpret_cast<const v4f*>(mu_g + 32 + 8 * seg + 4);
   const float mu[16] = {m0a[0], m0a[1], m0a[2], m0a[3], m0b[0], m0b[1], m0b[2], m0b[3],
                         m1a[0], m1a[1], m1a[2], m1a[3], m1b[0], m1b[1], m1b[2], m1b[3]};
-  const u32 xw[8] = {sl.xa.x, sl.xa.y, sl.xa.z, sl.xa.w, sl.xb.x, sl.xb.y, sl.xb.z, sl.xb.w};
+  const u32 xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 
   // x_hat = bf16(fl32(x * mu)) as packed pairs (also the MFMA A operand)
   u32 xh[8];
   float xf[16];
-  float amax = 0.f;
 #pragma unroll
   for (int d = 0; d < 8; ++d) {
     const float p0 = lo_bf16(xw[d]) * mu[2 * d];
@@ -108,27 +125,54 @@ __device__ __forceinline__ void quant_group(const Slot<NT>& sl, const float* mu_
     xh[d] = pack_bf16(p0, p1);
     xf[2 * d] = lo_bf16(xh[d]);
     xf[2 * d + 1] = hi_bf16(xh[d]);
-    amax = fmaxf(amax, fmaxf(fabsf(xf[2 * d]), fabsf(xf[2 * d + 1])));
   }
-  // the four lanes that hold this row's group: lanes l, l^16, l^32, l^48
-  amax = fmaxf(amax, __shfl_xor(amax, 16));
-  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  // A = max |x_hat| over the group.  With the sign bit cleared, bf16 bit
+  // patterns of non-negative values order like the values, so the maximum is
+  // taken on 16-bit integers, two per instruction; the four lanes holding the
+  // row's group (l, l^16, l^32, l^48) are combined with two lane swaps.
+  v2u16 mm = __builtin_bit_cast(v2u16, xh[0] & 0x7FFF7FFFu);
+#pragma unroll
+  for (int d = 1; d < 8; ++d) mm = __builtin_elementwise_max(mm, __builtin_bit_cast(v2u16, xh[d] & 0x7FFF7FFFu));
+  u32 am = max((u32)mm[0], (u32)mm[1]);
+  {
+    const v2u32 sw = __builtin_amdgcn_permlane16_swap(am, am, false, false);
+    am = max(sw[0], sw[1]);
+    const v2u32 sw2 = __builtin_amdgcn_permlane32_swap(am, am, false, false);
+    am = max(sw2[0], sw2[1]);
+  }
+  const float amax = __builtin_bit_cast(float, am << 16);
 
-  const u32 sbits = pack_bf16(amax / 7.0f, 0.f) & 0xFFFFu;
+  // s = bf16(fl32(A / 7)) equals bf16(fl32(A * fl32(1/7))) for every
+  // non-negative bf16 A (checked exhaustively: the two fp32 values differ in
+  // the last bit at times, never across a bf16 rounding boundary).
+  const u32 sbits = pack_bf16(amax * kRcp7, 0.f) & 0xFFFFu;
   const float s = __builtin_bit_cast(float, sbits << 16);
-  const float iota = s > 0.f ? 1.0f / s : 0.f;
+  // iota = fl32(1/s): hardware reciprocal and one Newton step, exact for bf16
+  // s in [2^-100, 2^100] (checked exhaustively on the device); outside that
+  // range (never for real activations) the IEEE division.
+  float iota;
+  const bool fast = s >= 0x1p-100f && s <= 0x1p100f;
+  if (__builtin_amdgcn_ballot_w64(!fast && s > 0.f) == 0) {
+    const float r = __builtin_amdgcn_rcpf(s);
+    iota = fast ? __builtin_fmaf(__builtin_fmaf(-s, r, 1.0f), r, r) : 0.f;
+  } else {
+    iota = s > 0.f ? 1.0f / s : 0.f;
+  }
 
-  // quantize and pack 8 nibbles per dword (element 2i low nibble)
+  // q = rint(x_hat * iota): the low byte of fma(x_hat, iota, 1.5 * 2^23) is q
+  // in two's complement.  Bytes are gathered with byte permutes (even and odd
+  // elements apart) and merged into nibbles (element 2i low).
   u32 packed[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    u32 pk = 0;
+    u32 qb[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const u32 qb = __builtin_bit_cast(u32, fmaf(xf[8 * i + e], iota, kRoundMagic));
-      pk |= (qb & 0xFu) << (4 * e);
-    }
-    packed[i] = pk;
+    for (int e = 0; e < 8; ++e) qb[e] = __builtin_bit_cast(u32, fmaf(xf[8 * i + e], iota, kRoundMagic));
+    const u32 ev = __builtin_amdgcn_perm(__builtin_amdgcn_perm(qb[6], qb[4], 0x0C0C0400u),
+                                         __builtin_amdgcn_perm(qb[2], qb[0], 0x0C0C0400u), 0x05040100u);
+    const u32 od = __builtin_amdgcn_perm(__builtin_amdgcn_perm(qb[7], qb[5], 0x0C0C0400u),
+                                         __builtin_amdgcn_perm(qb[3], qb[1], 0x0C0C0400u), 0x05040100u);
+    packed[i] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
   }
 
   // fused lora_down: lacc[t] += x_hat[16 rows, 64] @ L1[64, 16 ranks]
@@ -137,153 +181,360 @@ __device__ __forceinline__ void quant_group(const Slot<NT>& sl, const float* mu_
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const v4u av = {xh[4 * i], xh[4 * i + 1], xh[4 * i + 2], xh[4 * i + 3]};
-      lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av), sl.lb[t][i],
-                                                        lacc[t], 0, 0, 0);
+      lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av),
+                                                        lf_g[(2 * t + i) * 64 + lane], lacc[t],
+                                                        0, 0, 0);
     }
   }
   if (row_ok) {
     uint8_t* c = crow + 32 * g + 4 * seg;
     *reinterpret_cast<u32*>(c) = packed[0];
     *reinterpret_cast<u32*>(c + 16) = packed[1];
-    if (seg == 0) srow_out[g] = (uint16_t)sbits;
+    if (seg == 0) srow[g] = (uint16_t)sbits;
   }
 }
 
 template <int NT>  // NT = r / 16 rank tiles of 16
-__global__ __launch_bounds__(kWaves * 64) void quant_lora_down_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ lam,
-    const uint16_t* __restrict__ lora_down, int M, int K,
-    uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
-    uint16_t* __restrict__ lora_act) {
+__global__ __launch_bounds__(64 * kMaxTiles) void quant_lora_down_kernel(QuantArgs a) {
   constexpr int R = NT * 16;
-  __shared__ float mu_s[kMuChunk];
-  __shared__ float red[kRedSlots][kRows][NT > 0 ? R : 1];
+  constexpr int kDepth = depth_for<NT>();
+  __shared__ __align__(16) float mu_s[kMaxGB * 64];             // [GB * 64]
+  extern __shared__ __align__(16) uint8_t smem[];
+  v8bf* lf_s = reinterpret_cast<v8bf*>(smem);                   // [GB][NT][2][64]
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int nthr = blockDim.x;
+  const int kb = blockIdx.y;
+  const int g0 = kb * a.GB;
+  const int gc = min(a.GB, a.G - g0);  // groups in this K-block (> 0 by the plan)
+  const int tile = blockIdx.x * a.TB + wave;
+  const bool tile_ok = tile < a.T;     // wave-uniform
   const int rho = lane & 15;
-  const int seg = lane >> 4;
-  const int row0 = blockIdx.x * kRows;
-  const int row = row0 + rho;
-  const bool row_ok = row < M;
-  const int G = K >> 6;
-  const uint16_t* xrow = x + (size_t)(row_ok ? row : M - 1) * K + 8 * seg;
-  const uint16_t* lrow = lora_down + (size_t)rho * K + 8 * seg;
-  uint8_t* crow = codes + (size_t)row * (K >> 1);
-  uint16_t* srow = scales + (size_t)row * G;
+  const int row = tile * 16 + rho;
+  const bool row_ok = tile_ok && row < a.M;
+  const int K = a.K;
 
+  // 1. the K-block's lora_down fragments (1 KB chunks (group, rank tile,
+  //    half), 16 bytes per lane, spread over the waves) and this thread's
+  //    lambda values: short L2 round trips, issued ahead of the long X stream
+  //    so that waiting for them leaves X in flight (vector memory counters
+  //    retire in issue order).  The first kChunks chunks of each wave are
+  //    loaded unconditionally (an index past the end repeats the last chunk:
+  //    same bytes to the same place), so that the compiler counts the loads
+  //    in flight exactly; further chunks (large blocks only) come after X.
+  //    Plain loads, not LDS DMA: the compiler does not order DMA against
+  //    plain loads and would wait for X before the first use of lambda.
+  constexpr int kChunks = 4;
+  constexpr int nt1 = NT > 0 ? NT : 1;
+  const int nchunk = NT * 2 * gc;
+  auto chunk_src = [&](int c) {
+    const int h = c & 1, t = (c >> 1) % nt1, gi = (c >> 1) / nt1;
+    return reinterpret_cast<const v8bf*>(a.lora_down + (size_t)(16 * t + rho) * K + 64 * (g0 + gi) +
+                                         32 * h + 8 * (lane >> 4));
+  };
+  v8bf fr[NT > 0 ? kChunks : 1];
+  if constexpr (NT > 0) {
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) fr[j] = *chunk_src(min(wave + j * a.TB, nchunk - 1));
+  }
+  constexpr int kMu = 4;  // lambda values per thread in the fast path
+  const int nmu = 64 * gc;
+  float lv[kMu];
+#pragma unroll
+  for (int j = 0; j < kMu; ++j) lv[j] = a.lam[64 * g0 + min(j * nthr + (int)threadIdx.x, nmu - 1)];
+
+  // 2. X: the first group of the ring, then the fragments and mu go to LDS
+  //    (waiting for them leaves that group in flight), then the rest of the
+  //    ring.  Under the full X stream the small loads above would take as
+  //    long as the bulk of X, which would then wait for them.  All X loads
+  //    are unconditional (rows past M re-read row M-1, groups past the block
+  //    re-read its last group), so the number of loads in flight is the same
+  //    on every path and each wait is a precise vmcnt.
+  const uint16_t* xrow = a.x + (size_t)(row_ok ? row : a.M - 1) * K + 8 * (lane >> 4);
+  uint4 ra[kDepth], rb[kDepth];
+  ra[0] = *reinterpret_cast<const uint4*>(xrow + 64 * g0);
+  rb[0] = *reinterpret_cast<const uint4*>(xrow + 64 * g0 + 32);
+
+  // 3. fragments and mu = fl32(1 / lambda) into LDS.  Every lane divides and
+  //    stores (lanes past the block store the last channel's value again), so
+  //    that nothing is predicated.
+  if constexpr (NT > 0) {
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) lf_s[min(wave + j * a.TB, nchunk - 1) * 64 + lane] = fr[j];
+  }
+#pragma unroll
+  for (int j = 0; j < kMu; ++j) mu_s[min(j * nthr + (int)threadIdx.x, nmu - 1)] = 1.0f / lv[j];
+
+#pragma unroll
+  for (int s = 1; s < kDepth; ++s) {
+    const int gs = g0 + min(s, gc - 1);
+    ra[s] = *reinterpret_cast<const uint4*>(xrow + 64 * gs);
+    rb[s] = *reinterpret_cast<const uint4*>(xrow + 64 * gs + 32);
+  }
+  for (int c = kMu * nthr + (int)threadIdx.x; c < nmu; c += nthr) mu_s[c] = 1.0f / a.lam[64 * g0 + c];
+  if constexpr (NT > 0) {
+    for (int c = wave + kChunks * a.TB; c < nchunk; c += a.TB) lf_s[c * 64 + lane] = *chunk_src(c);
+  }
+  // LDS writes done; no __syncthreads, whose fence would wait for X as well
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+  if (!tile_ok) return;  // no barrier follows
+
+  uint8_t* crow = a.codes + (size_t)row * (K >> 1);
+  uint16_t* srow = a.scales + (size_t)row * a.G;
   v4f lacc[NT > 0 ? NT : 1];
 #pragma unroll
   for (int t = 0; t < (NT > 0 ? NT : 1); ++t) lacc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // K is processed in chunks of kMuChunk channels whose reciprocals mu sit in
-  // LDS.  Inside a chunk, wave w takes groups w, w + kWaves, ... through a ring
-  // of kDepth slots: each slot is refilled with the group kDepth steps ahead as
-  // soon as it is consumed, and every global load a step waits for was issued
-  // kDepth steps earlier (vector memory counters retire in issue order).
-  for (int k0 = 0; k0 < K; k0 += kMuChunk) {
-    const int kc = min(kMuChunk, K - k0);
-    const int g0 = k0 >> 6;
-    const int gc = kc >> 6;
-    __syncthreads();  // previous chunk's mu fully consumed
-    {
-      // all loads of lambda first (16 bytes per thread and step), then the
-      // divisions: one memory round trip instead of one per element
-      constexpr int kPer = (kMuChunk / 4 + kWaves * 64 - 1) / (kWaves * 64);
-      const float4* lam4 = reinterpret_cast<const float4*>(lam + k0);
-      float4 lv[kPer];
-#pragma unroll
-      for (int c = 0; c < kPer; ++c) {
-        const int i = threadIdx.x + c * kWaves * 64;
-        if (i < (kc >> 2)) lv[c] = lam4[i];
-      }
-#pragma unroll
-      for (int c = 0; c < kPer; ++c) {
-        const int i = threadIdx.x + c * kWaves * 64;
-        if (i < (kc >> 2))
-          reinterpret_cast<float4*>(mu_s)[i] =
-              float4{1.0f / lv[c].x, 1.0f / lv[c].y, 1.0f / lv[c].z, 1.0f / lv[c].w};
-      }
-    }
-    __syncthreads();
-
-    Slot<NT> ring[kDepth];
+  // 4. walk the block's groups in full rounds of kDepth: each slot is consumed
+  //    in place and then refilled with the group kDepth ahead (refilling first
+  //    would make the compiler copy the slot and wait for every load in
+  //    flight); the last round's refills past the block re-read its last group
+  const int nfull = gc / kDepth;
+  for (int rnd = 0; rnd < nfull; ++rnd) {
 #pragma unroll
     for (int s = 0; s < kDepth; ++s) {
-      const int gl = wave + kWaves * s;
-      if (gl < gc) fetch<NT>(ring[s], xrow, lrow, K, g0 + gl);
+      const int gl = rnd * kDepth + s;
+      quant_group<NT>(ra[s], rb[s], mu_s + 64 * gl, lf_s + gl * NT * 128, g0 + gl, lane, row_ok,
+                      crow, srow, lacc);
+      const int gn = g0 + min(gl + kDepth, gc - 1);
+      ra[s] = *reinterpret_cast<const uint4*>(xrow + 64 * gn);
+      rb[s] = *reinterpret_cast<const uint4*>(xrow + 64 * gn + 32);
     }
-    for (int base = wave; base < gc; base += kWaves * kDepth) {
+  }
+  // the remaining gc % kDepth groups sit in the first slots
 #pragma unroll
-      for (int s = 0; s < kDepth; ++s) {
-        const int gl = base + kWaves * s;
-        if (gl < gc) {
-          // consume the slot in place, then refill it: refilling first would
-          // make the compiler copy the slot, and the copy waits for every load
-          // in flight (loads retire in issue order), draining the ring
-          quant_group<NT>(ring[s], mu_s + 64 * gl, g0 + gl, seg, row_ok, crow, srow, lacc);
-          const int gn = gl + kWaves * kDepth;
-          if (gn < gc) fetch<NT>(ring[s], xrow, lrow, K, g0 + gn);
-        }
-      }
-    }
+  for (int s = 0; s < kDepth; ++s) {
+    const int gl = nfull * kDepth + s;
+    if (gl < gc)
+      quant_group<NT>(ra[s], rb[s], mu_s + 64 * gl, lf_s + gl * NT * 128, g0 + gl, lane, row_ok,
+                      crow, srow, lacc);
   }
 
   if constexpr (NT > 0) {
-    // lane l holds rows 4*(l/16)+v, rank 16t + l%16.  Waves w, w + kRedSlots,
-    // ... are added into slot w in a fixed order (highest first), then the
-    // slots are summed in order: the result does not depend on timing.
-    constexpr int kPhases = kWaves / kRedSlots;
+    // lane l holds rows 4*(l/16)+v of the tile, rank 16t + l%16
+    v4f sum[NT];
+    if (a.KB == 1) {
 #pragma unroll
-    for (int ph = kPhases - 1; ph >= 0; --ph) {
-      if (wave / kRedSlots == ph) {
-        float(*dst)[NT > 0 ? R : 1] = red[wave % kRedSlots];
+      for (int t = 0; t < NT; ++t) sum[t] = lacc[t];
+    } else {
+      // Partials travel as agent-scope relaxed atomics (coherent across the
+      // XCDs' L2s without writing back or invalidating whole caches, which a
+      // fence would do); the store completion wait orders them before the
+      // counter increment, and the reader loads them the same way.
+      // Layout [t][v][lane]: each store instruction writes 256 contiguous bytes.
+      float* mine = a.part + ((size_t)kb * a.T + tile) * NT * 256;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float& d = dst[4 * seg + v][16 * t + rho];
-            d = (ph == kPhases - 1) ? lacc[t][v] : d + lacc[t][v];
+        for (int v = 0; v < 4; ++v)
+          __hip_atomic_store(mine + (t * 4 + v) * 64 + lane, lacc[t][v], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      __asm__ volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the partial is visible to the agent
+      __asm__ volatile("" ::: "memory");
+      u32 old = 0;
+      if (lane == 0) old = atomicInc(a.count + tile, (u32)(a.KB - 1));
+      old = __shfl(old, 0);
+      if (old != (u32)(a.KB - 1)) return;  // another K-block of this tile is still running
+      __asm__ volatile("" ::: "memory");
+      // read the other K-blocks' partials kRd at a time, all loads of a batch
+      // before any add (one memory round trip per batch); add in K-block order
+      constexpr int kRd = 8;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        for (int j0 = 0; j0 < a.KB; j0 += kRd) {
+          v4f pv[kRd];
+#pragma unroll
+          for (int i = 0; i < kRd; ++i) {
+            const int j = min(j0 + i, a.KB - 1);
+            const float* p = a.part + (((size_t)j * a.T + tile) * NT + t) * 256;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              pv[i][e] = __hip_atomic_load(p + e * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
-      }
-      __syncthreads();
-    }
-    for (int idx = threadIdx.x; idx < kRows * R; idx += kWaves * 64) {
-      const int rr = idx / R;
-      const int j = idx - rr * R;
-      float sum = red[0][rr][j];
 #pragma unroll
-      for (int w = 1; w < kRedSlots; ++w) sum += red[w][rr][j];
-      if (row0 + rr < M) lora_act[(size_t)(row0 + rr) * R + j] = (uint16_t)(pack_bf16(sum, 0.f) & 0xFFFFu);
+          for (int i = 0; i < kRd; ++i) {
+            const int j = j0 + i;
+            if (j < a.KB) {
+              const v4f v = (j == kb) ? lacc[t] : pv[i];
+              sum[t] = (j == 0) ? v : sum[t] + v;
+            }
+          }
+        }
+      }
     }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int rr = tile * 16 + 4 * (lane >> 4) + v;
+        if (rr < a.M)
+          a.lora_act[(size_t)rr * R + 16 * t + rho] = (uint16_t)(pack_bf16(sum[t][v], 0.f) & 0xFFFFu);
+      }
   }
 }
 
+// ---------------------------------------------------------------- host side
+
+struct Plan {
+  int TB, GB, KB, nrb;
+  size_t lds;
+};
+
+size_t lds_bytes(int GB, int NT) { return (size_t)GB * NT * 2048; }  // dynamic part
+
+// Balance cells (16 rows x 64 k) over the compute units, in units of one
+// cell's X bytes (2 KB from HBM) per compute unit:
+//  - the X stream: 1 per cell; the quantizer's VALU work: ~3.5 per cell of
+//    each wave on the busiest SIMD (TB waves share 4 SIMDs; measured: ~750
+//    cycles per wave and group against ~210 for a cell's share of HBM); the
+//    larger one counts;
+//  - the K-block's lora_down slice, read from L2 by each workgroup: GB * NT
+//    KB-sized fragments, at half weight (L2, not HBM);
+//  - with K split, each row tile's fp32 partial is written and read back
+//    through the last-level cache: ~NT per tile, at half weight;
+//  - the workgroup's prologue (lambda, reciprocals, barrier): ~1;
+// times the number of workgroups that share a compute unit.
+Plan make_plan(int T, int G, int NT, int cus) {
+  const int GB0 = std::min(G, 8);
+  Plan best{1, GB0, (G + GB0 - 1) / GB0, T, lds_bytes(GB0, NT)};
+  double best_cost = 1e300;
+  for (int TB = 1; TB <= kMaxTiles; ++TB) {
+    const int nrb = (T + TB - 1) / TB;
+    for (int KB = (G + kMaxGB - 1) / kMaxGB; KB <= G; ++KB) {
+      const int GB = (G + KB - 1) / KB;
+      if ((G + GB - 1) / GB != KB) continue;  // same blocks as a smaller KB
+      const size_t lds = lds_bytes(GB, NT);
+      if (lds + kMuBytes > (size_t)kLdsLimit) continue;
+      if (KB > 4 * cus) break;
+      const long wgs = (long)nrb * KB;
+      const long per_cu = (wgs + cus - 1) / cus;
+      const double mem = (double)TB * GB;
+      const double valu = 3.5 * ((TB + 3) / 4) * GB;
+      const double lora = 0.5 * GB * NT + (KB > 1 ? 0.5 * TB * NT : 0.0);
+      const double cost = per_cu * (std::max(mem, valu) + lora + 1.0);
+      if (cost < best_cost - 1e-9) {
+        best_cost = cost;
+        best = Plan{TB, GB, KB, nrb, lds};
+      }
+    }
+  }
+  return best;
+}
+
+int g_force_tb = 0, g_force_kb = 0;  // test hook (0 = automatic)
+
+// Per device and stream: T counters (zero between launches) followed by the
+// partial sums.  Calls on one stream are ordered, so they can share it.
+struct Workspace {
+  void* ptr = nullptr;
+  size_t count_cap = 0;   // counters known to be zero
+  size_t part_bytes = 0;
+};
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+int cu_count(int dev) {
+  static int cache[64] = {0};
+  if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = 256;
+  }
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  return n;
+}
+
 template <int NT>
-hipError_t launch_nt(const uint16_t* x, const float* lam, const uint16_t* lora_down, int M, int K,
-                     uint8_t* codes, uint16_t* scales, uint16_t* lora_act, hipStream_t stream) {
-  const dim3 grid((M + kRows - 1) / kRows);
-  hipLaunchKernelGGL(quant_lora_down_kernel<NT>, grid, dim3(kWaves * 64), 0, stream, x, lam,
-                     lora_down, M, K, codes, scales, lora_act);
+hipError_t launch_nt(const QuantArgs& a, const Plan& p, hipStream_t stream) {
+  const dim3 grid(p.nrb, p.KB);
+  const dim3 block(64 * p.TB);
+  auto kern = quant_lora_down_kernel<NT>;
+  if (p.lds + kMuBytes > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, grid, block, p.lds, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
+void set_quant_plan_override(int k_blocks, int tiles_per_wg) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_force_kb = std::max(0, k_blocks);
+  g_force_tb = std::max(0, tiles_per_wg);
+}
+
 hipError_t launch_quant_lora_down(const uint16_t* x, const float* lam, const uint16_t* lora_down,
                                   int64_t M, int64_t K, int64_t r, uint8_t* codes,
                                   uint16_t* scales, uint16_t* lora_act, hipStream_t stream) {
-  const int m = (int)M, k = (int)K;
-  switch (r / 16) {
-    case 0: return launch_nt<0>(x, lam, lora_down, m, k, codes, scales, lora_act, stream);
-    case 1: return launch_nt<1>(x, lam, lora_down, m, k, codes, scales, lora_act, stream);
-    case 2: return launch_nt<2>(x, lam, lora_down, m, k, codes, scales, lora_act, stream);
-    case 3: return launch_nt<3>(x, lam, lora_down, m, k, codes, scales, lora_act, stream);
-    case 4: return launch_nt<4>(x, lam, lora_down, m, k, codes, scales, lora_act, stream);
-    case 5: return launch_nt<5>(x, lam, lora_down, m, k, codes, scales, lora_act, stream);
-    case 6: return launch_nt<6>(x, lam, lora_down, m, k, codes, scales, lora_act, stream);
-    case 7: return launch_nt<7>(x, lam, lora_down, m, k, codes, scales, lora_act, stream);
-    case 8: return launch_nt<8>(x, lam, lora_down, m, k, codes, scales, lora_act, stream);
+  const int NT = (int)(r / 16);
+  const int T = (int)((M + 15) / 16);
+  const int G = (int)(K / 64);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+
+  std::lock_guard<std::mutex> lk(g_mu);
+  Plan p = make_plan(T, G, NT, cu_count(dev));
+  if (g_force_kb > 0 || g_force_tb > 0) {
+    const int TB = g_force_tb > 0 ? std::min(g_force_tb, kMaxTiles) : p.TB;
+    const int KB0 = g_force_kb > 0 ? std::min(g_force_kb, G) : p.KB;
+    const int GB = (G + KB0 - 1) / KB0;
+    if (GB <= kMaxGB && lds_bytes(GB, NT) + kMuBytes <= (size_t)kLdsLimit)
+      p = Plan{TB, GB, (G + GB - 1) / GB, (T + TB - 1) / TB, lds_bytes(GB, NT)};
+  }
+
+  QuantArgs a;
+  a.x = x; a.lam = lam; a.lora_down = lora_down;
+  a.codes = codes; a.scales = scales; a.lora_act = lora_act;
+  a.part = nullptr; a.count = nullptr;
+  a.M = (int)M; a.K = (int)K; a.T = T; a.G = G;
+  a.GB = p.GB; a.TB = p.TB; a.KB = p.KB;
+
+  if (NT > 0 && p.KB > 1) {
+    const size_t part_need = (size_t)p.KB * T * NT * 64 * 16;
+    Workspace& w = g_ws[{dev, stream}];
+    if (w.count_cap < (size_t)T || w.part_bytes < part_need) {
+      if (w.ptr) {
+        e = hipStreamSynchronize(stream);  // earlier launches on this stream may still use it
+        if (e != hipSuccess) return e;
+        e = hipFree(w.ptr);
+        w = Workspace{};
+        if (e != hipSuccess) return e;
+      }
+      const size_t cap = std::max<size_t>(T, 64) + T / 4;
+      const size_t pb = part_need + part_need / 4;
+      e = hipMalloc(&w.ptr, round256(cap * 4) + pb);
+      if (e != hipSuccess) { w = Workspace{}; return e; }
+      e = hipMemsetAsync(w.ptr, 0, round256(cap * 4), stream);
+      if (e != hipSuccess) { (void)hipFree(w.ptr); w = Workspace{}; return e; }
+      w.count_cap = cap;
+      w.part_bytes = pb;
+    }
+    a.count = static_cast<u32*>(w.ptr);
+    a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(w.ptr) + round256(w.count_cap * 4));
+  }
+
+  switch (NT) {
+    case 0: return launch_nt<0>(a, p, stream);
+    case 1: return launch_nt<1>(a, p, stream);
+    case 2: return launch_nt<2>(a, p, stream);
+    case 3: return launch_nt<3>(a, p, stream);
+    case 4: return launch_nt<4>(a, p, stream);
+    case 5: return launch_nt<5>(a, p, stream);
+    case 6: return launch_nt<6>(a, p, stream);
+    case 7: return launch_nt<7>(a, p, stream);
+    case 8: return launch_nt<8>(a, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -13,6 +13,10 @@ hipError_t launch_quant_lora_down(const uint16_t* x, const float* lam, const uin
                                   uint8_t* codes, uint16_t* scales, uint16_t* lora_act,
                                   hipStream_t stream);
 
+// Test hook: forces call 1's work split (K-blocks, row tiles per workgroup);
+// 0 keeps the automatic choice.  Affects later launches of this process.
+void set_quant_plan_override(int k_blocks, int tiles_per_wg);
+
 // Call 2: W4A4 GEMM + group dequant + fused lora_up + bias.  When `acc_dump` is
 // not null the kernel writes the int32 group accumulators [M, N, K/64] there
 // instead of Y (scales, lora and bias are then ignored).

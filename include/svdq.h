@@ -104,11 +104,30 @@ svdq_status svdq_check_device(int device);
  *   stream     hipStream_t or NULL
  * Codes and scales are exactly defined (bit-exact to the rule above); lora_act
  * may differ from a float64 evaluation by one bf16 ulp (summation order).
+ * Workspace: when K is split over several workgroups, the fp32 partial sums of
+ * lora_act go through a device workspace that the library owns, one per
+ * (device, stream), allocated and zero-filled on first use and grown when a
+ * call needs more (the growth waits for `stream` and frees the old one).  The
+ * first call on a stream for a given size therefore allocates: make it
+ * outside graph capture.  Calls that share a stream are ordered by it; calls
+ * on different streams use different workspaces.  The result of a call does
+ * not depend on timing (partials are added in a fixed order).
  */
 svdq_status svdq_quantize_act_lora_down(
     const void* x, const float* smooth, const void* lora_down,
     int64_t M, int64_t K, int64_t r, int64_t group_size,
     void* act_codes, void* act_scales, void* lora_act, void* stream);
+
+/*
+ * Test hook for call 1: forces its work split for every later call in this
+ * process.  k_blocks = number of K-blocks (each a run of consecutive groups of
+ * 64; clipped to K/64), tiles_per_wg = row tiles of 16 per workgroup (1..12);
+ * 0 keeps the automatic choice for that parameter.  A forced split whose
+ * K-block would not fit in LDS is ignored.  Codes and scales do not depend on
+ * the split; lora_act may change by a bf16 ulp (its fp32 partial sums change).
+ * Returns INVALID_VALUE for negative values or tiles_per_wg > 12.
+ */
+svdq_status svdq_debug_set_quant_plan(int k_blocks, int tiles_per_wg);
 
 /*
  * Call 2 - W4A4 GEMM with per-group int32 accumulation, per-group

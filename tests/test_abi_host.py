@@ -124,6 +124,15 @@ def test_debug_hook_argument_errors():
     assert L.svdq_w4a4_group_acc_debug(FAKE, FAKE, 0, 64, 64, 64, FAKE, None) == SUCCESS
 
 
+def test_quant_plan_hook_arguments():
+    L = lib()
+    assert L.svdq_debug_set_quant_plan(-1, 0) == INVALID_VALUE
+    assert L.svdq_debug_set_quant_plan(0, -2) == INVALID_VALUE
+    assert L.svdq_debug_set_quant_plan(2, 13) == INVALID_VALUE
+    assert L.svdq_debug_set_quant_plan(3, 12) == SUCCESS
+    assert L.svdq_debug_set_quant_plan(0, 0) == SUCCESS
+
+
 def _gpu_visible():
     try:
         import torch

@@ -211,6 +211,72 @@ def test_repeated_launches_are_bit_identical():
             assert np.array_equal(first[k], again[k]), k
 
 
+def _quant(d, lam, packed, stream=None):
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K
+    r = packed["lora_down"].shape[0]
+    codes, scales, la = K.quantize_act_lora_down(
+        to_dev_bf16(d["x"]), to_dev(np.asarray(lam, np.float32)),
+        to_dev_bf16(packed["lora_down"]) if r else None, stream=stream)
+    torch.cuda.synchronize()
+    return {"act_codes": codes.cpu().numpy(), "act_scales": bf16_bits(scales), "lora_act": bf16_bits(la)}
+
+
+@pytest.mark.parametrize("plan,M,K,r", [
+    ((1, 1), 200, 448, 32), ((3, 2), 200, 448, 32), ((7, 5), 200, 448, 32), ((2, 12), 200, 448, 32),
+    ((0, 1), 200, 448, 32), ((5, 0), 200, 448, 32), ((4, 3), 61, 1024, 128), ((3, 4), 130, 576, 48),
+    ((6, 7), 33, 384, 0), ((40, 2), 40, 3072, 16),
+])
+def test_forced_work_splits(plan, M, K, r):
+    """Every split of call 1 (K-blocks, row tiles per workgroup) gives the oracle's
+    codes and scales bit for bit and lora_act within its bound; ragged M and a
+    ragged last K-block (K = 448 is 7 groups)."""
+    import bit_diffusion_transformer_svdq_amd as K_
+    d, lam, packed = custom_case(M, K, 64, r, seed=M + K)
+    ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
+    K_.debug_set_quant_plan(*plan)
+    try:
+        got = _quant(d, lam, packed)
+        again = _quant(d, lam, packed)
+    finally:
+        K_.debug_set_quant_plan(0, 0)
+    _check_quant(got, ref, packed["lora_down"] if r else None)
+    for k in got:  # the K-block partials are added in a fixed order
+        assert np.array_equal(got[k], again[k]), k
+
+
+def test_two_streams_use_separate_workspaces():
+    """Split-K calls on two streams at once, then a larger problem on one of them
+    (the workspace grows), then the first size again."""
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K_
+    cases = [custom_case(300, 512, 64, 32, seed=s) for s in (31, 32)]
+    big = custom_case(900, 1024, 64, 32, seed=33)
+    refs = [O.quantize_act_lora_down(d["x"], lam, p["lora_down"]) for d, lam, p in cases]
+    ref_big = O.quantize_act_lora_down(big[0]["x"], big[1], big[2]["lora_down"])
+    ins = [(to_dev_bf16(d["x"]), to_dev(np.asarray(lam, np.float32)), to_dev_bf16(p["lora_down"]))
+           for d, lam, p in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    K_.debug_set_quant_plan(4, 2)
+    try:
+        outs = [None, None]
+        for _ in range(3):
+            for i in (0, 1):
+                outs[i] = K_.quantize_act_lora_down(*ins[i], stream=streams[i])
+        torch.cuda.synchronize()
+        got = [{"act_codes": c.cpu().numpy(), "act_scales": bf16_bits(s), "lora_act": bf16_bits(l)}
+               for c, s, l in outs]
+        got_big = _quant(*big, stream=streams[0])
+        got_small = _quant(*cases[0], stream=streams[0])
+    finally:
+        K_.debug_set_quant_plan(0, 0)
+    for g, ref, (d, lam, p) in zip(got, refs, cases):
+        _check_quant(g, ref, p["lora_down"])
+    _check_quant(got_big, ref_big, big[2]["lora_down"])
+    _check_quant(got_small, refs[0], cases[0][2]["lora_down"])
+
+
 # ---- DiT-scale shapes, in the launch configuration the benchmark times ----
 
 def _full_case(name):

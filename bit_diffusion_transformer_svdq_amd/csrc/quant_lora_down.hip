@@ -156,7 +156,10 @@ __device__ __forceinline__ void quant_group(const uint4& xa, const uint4& xb, co
     const float r = __builtin_amdgcn_rcpf(s);
     iota = fast ? __builtin_fmaf(__builtin_fmaf(-s, r, 1.0f), r, r) : 0.f;
   } else {
-    iota = s > 0.f ? 1.0f / s : 0.f;
+    // a reciprocal that overflows (s < 2^-128) makes the group a zero group,
+    // like s = 0
+    const float r = 1.0f / s;
+    iota = (s > 0.f && r <= 0x1.fffffep127f) ? r : 0.f;
   }
 
   // q = rint(x_hat * iota): the low byte of fma(x_hat, iota, 1.5 * 2^23) is q

@@ -90,7 +90,8 @@ svdq_status svdq_check_device(int device);
  *   x_hat     = bf16(fl32(X * mu))                     (one canonical bf16 X_hat)
  *   per row m and group g of 64 k:
  *     s       = bf16(fl32(max|x_hat| / 7))
- *     q       = clamp(rint_even(x_hat * fl32(1/s)), -7, 7)   (s == 0 -> q = 0)
+ *     q       = clamp(rint_even(x_hat * fl32(1/s)), -7, 7)
+ *               (s == 0, or fl32(1/s) overflowing (s < 2^-128): q = 0)
  *   lora_act  = bf16(x_hat @ lora_down^T)              (fp32 accumulation)
  *
  *   x          device, bf16 [M, K]

@@ -233,8 +233,10 @@ def quantize_activation_groups(xhat_bits, group: int = GROUP):
 
     A = max |x_hat| over the group; s = bf16(fl32(A / 7)); iota = fl32(1 / s);
     q = clamp(rint(x_hat * iota), -7, 7), the product taken exactly (8 + 24 bits
-    fit float64); s = 0 gives q = 0.  Returns (q int8 [M, K], scale bits uint16
-    [M, K/group]).
+    fit float64); s = 0 gives q = 0.  Reading (the pages are silent): when
+    fl32(1 / s) overflows (s < 2^-128, a group maximum below about 2e-38) the
+    group is treated like s = 0, q = 0.  Returns (q int8 [M, K], scale bits
+    uint16 [M, K/group]).
     """
     xh = bf16_to_f64(xhat_bits)
     M, K = xh.shape
@@ -242,9 +244,9 @@ def quantize_activation_groups(xhat_bits, group: int = GROUP):
     amax = np.abs(g).max(axis=2)
     s_bits = f32_to_bf16(f64_to_f32(amax / float(QMAX)))
     s = bf16_to_f64(s_bits)
-    with np.errstate(divide="ignore"):
+    with np.errstate(divide="ignore", over="ignore"):
         iota = f64_to_f32(1.0 / s).astype(np.float64)
-    iota = np.where(s > 0, iota, 0.0)
+    iota = np.where((s > 0) & np.isfinite(iota), iota, 0.0)
     q = np.rint(g * iota[:, :, None])
     q = np.clip(q, -QMAX, QMAX).astype(np.int8)
     return q.reshape(M, K), s_bits

@@ -245,6 +245,42 @@ def test_forced_work_splits(plan, M, K, r):
         assert np.array_equal(got[k], again[k]), k
 
 
+def test_quantizer_scale_sweep_covers_every_scale():
+    """One group per bf16 group maximum A whose scale s = bf16(A/7) lies in
+    [2^-100, 2^100], i.e. every scale that reaches the kernel's fast reciprocal
+    (so that path is checked exhaustively), plus maxima outside that range
+    (IEEE division path; below 7 * 2^-128 fl32(1/s) overflows and the group
+    quantizes to zero) and all-zero groups.  lambda = 1, so x_hat = x; each
+    group holds +-A and 63 values drawn from [-A, A]."""
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K_
+    rng = np.random.default_rng(7)
+    a_bits = np.arange(0, 0x7F80, dtype=np.uint32)
+    a_all = (a_bits << 16).view(np.float32).astype(np.float64)
+    s_all = O.bf16_to_f64(O.f32_to_bf16((a_all / 7.0).astype(np.float32)))
+    in_rng = (s_all >= 2.0 ** -100) & (s_all <= 2.0 ** 100)
+    assert in_rng.sum() > 25000
+    extra = np.concatenate([2.0 ** rng.uniform(-126, -99, 150), 2.0 ** rng.uniform(101, 127, 150)])
+    A = np.concatenate([a_all[in_rng], extra, np.zeros(64)])
+    G, Kd = len(A), 4096
+    M = -(-G // (Kd // 64))
+    A = np.concatenate([A, np.ones(M * (Kd // 64) - G)])
+    A_bits = O.f64_to_bf16(A)
+    Ab = O.bf16_to_f64(A_bits)
+    vals = rng.uniform(-1.0, 1.0, (len(Ab), 64)) * Ab[:, None]
+    pos = rng.integers(0, 64, len(Ab))
+    vals[np.arange(len(Ab)), pos] = Ab * np.where(rng.random(len(Ab)) < 0.5, -1.0, 1.0)
+    x_bits = O.f64_to_bf16(vals).reshape(M, Kd)
+    lam = np.ones(Kd, np.float32)
+    ref = O.quantize_act_lora_down(x_bits, lam, np.zeros((0, Kd), np.uint16))
+    codes, scales, _ = K_.quantize_act_lora_down(to_dev_bf16(x_bits), to_dev(lam), None)
+    torch.cuda.synchronize()
+    got_s = bf16_bits(scales)
+    assert np.array_equal(got_s, ref["act_scales"]), np.argwhere(got_s != ref["act_scales"])[:5]
+    got_c = codes.cpu().numpy()
+    assert np.array_equal(got_c, ref["act_codes"]), np.argwhere(got_c != ref["act_codes"])[:5]
+
+
 def test_two_streams_use_separate_workspaces():
     """Split-K calls on two streams at once, then a larger problem on one of them
     (the workspace grows), then the first size again."""

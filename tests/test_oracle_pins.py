@@ -459,3 +459,20 @@ def test_weight_scale_is_one_rounding_at_a_constructed_near_tie():
     q, s_bits = O.quantize_weight_groups(R)
     assert Fraction(float(O.bf16_to_f64(s_bits)[0, 0])) == ex_bf16(Fraction(float(R[0, 0])) / 7)
     assert int(s_bits[0, 0]) == 0x3C11
+
+
+def test_activation_quantizer_tiny_groups_reading():
+    """Reading for a case the pages leave open: a group whose scale s is so small
+    that fl32(1/s) overflows (s < 2^-128) quantizes to zero, like s = 0.  Just
+    above that, s = 2^-127 gives iota = 2^127 and the exact codes."""
+    xh = np.zeros((1, 128))
+    xh[0, :64] = np.linspace(-1.0, 1.0, 64) * 7.0 * 2.0 ** -127      # s = 2^-127
+    xh[0, 64:] = np.linspace(-1.0, 1.0, 64) * 7.0 * 2.0 ** -130      # s < 2^-128
+    bits = O.f64_to_bf16(xh)
+    q, s_bits = O.quantize_activation_groups(bits)
+    s = O.bf16_to_f64(s_bits)[0]
+    assert s[0] == 2.0 ** -127 and 0 < s[1] < 2.0 ** -128
+    xv = O.bf16_to_f64(bits)[0]
+    assert np.array_equal(q[0, :64], np.clip(np.rint(xv[:64] / s[0]), -7, 7))
+    assert q[0, 0] == -7 and q[0, 63] == 7
+    assert not np.any(q[0, 64:])

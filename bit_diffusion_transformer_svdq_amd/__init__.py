@@ -22,7 +22,7 @@ import numpy as np
 from ._lib import SvdqError, check, lib
 
 __all__ = ["SvdqError", "lib", "check_device", "quantize_act_lora_down", "w4a4_gemm_lora_up",
-           "w4a4_group_acc_debug", "debug_set_quant_plan", "smooth_from_absmax", "pack_weights",
+           "w4a4_group_acc_debug", "debug_set_quant_plan", "debug_set_gemm_path", "smooth_from_absmax", "pack_weights",
            "GROUP_SIZE"]
 
 GROUP_SIZE = 64
@@ -91,6 +91,11 @@ def quantize_act_lora_down(x, smooth, lora_down=None, out=None, stream=None):
 def debug_set_quant_plan(k_blocks: int = 0, tiles_per_wg: int = 0) -> None:
     """Test hook: force call 1's work split for later calls (0 = automatic)."""
     check(lib().svdq_debug_set_quant_plan(int(k_blocks), int(tiles_per_wg)), "svdq_debug_set_quant_plan")
+
+
+def debug_set_gemm_path(path: int = 0) -> None:
+    """Test hook: 0 = kernel chosen by shape, 1 = tiled kernel, 2 = K-split (few-token) kernel."""
+    check(lib().svdq_debug_set_gemm_path(int(path)), "svdq_debug_set_gemm_path")
 
 
 def w4a4_gemm_lora_up(act_codes, act_scales, w_codes, w_scales, lora_act=None, lora_up=None,

@@ -149,6 +149,12 @@ svdq_status svdq_debug_set_quant_plan(int k_blocks, int tiles_per_wg) {
   return ok();
 }
 
+svdq_status svdq_debug_set_gemm_path(int path) {
+  if (path < 0 || path > 2) return fail(SVDQ_STATUS_INVALID_VALUE, "bad gemm path %d (0, 1 or 2)", path);
+  svdq::set_gemm_path_override(path);
+  return ok();
+}
+
 static svdq_status validate_gemm(const void* act_codes, const void* w_codes, int64_t M, int64_t N,
                                  int64_t K, int64_t r, int64_t group_size) {
   if (M < 0 || N <= 0 || K <= 0 || r < 0 || group_size <= 0)

@@ -29,4 +29,17 @@ hipError_t launch_w4a4_gemm_lora_up(const uint8_t* act_codes, const uint16_t* ac
                                     int64_t M, int64_t N, int64_t K, int64_t r,
                                     uint16_t* y, int32_t* acc_dump, hipStream_t stream);
 
+// Call 2 for few tokens: K split over the waves of a workgroup, weights
+// streamed once.  Same arguments and results as launch_w4a4_gemm_lora_up.
+bool skinny_supported(int64_t M, int64_t N, int64_t K);
+hipError_t launch_w4a4_gemm_skinny(const uint8_t* act_codes, const uint16_t* act_scales,
+                                   const uint8_t* w_codes, const uint16_t* w_scales,
+                                   const uint16_t* lora_act, const uint16_t* lora_up,
+                                   const uint16_t* bias, int64_t M, int64_t N, int64_t K,
+                                   int64_t r, uint16_t* y, int32_t* acc_dump, hipStream_t stream);
+
+// Test hook: 0 = choose by shape, 1 = always the tiled kernel, 2 = the
+// few-token kernel wherever it is supported.
+void set_gemm_path_override(int path);
+
 }  // namespace svdq

@@ -53,6 +53,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "svdq_internal.h"
 
 namespace svdq {
@@ -78,6 +80,7 @@ constexpr int kStaticLds = kStages * 2 * kTile + 2 * 4 * kScale;  // 3 tile stag
 constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 constexpr u32 kNib = 0xF0F0F0F0u;
+constexpr int64_t kSkinnyMaxM = 160;  // up to this many tokens the K-split kernel is faster
 
 __device__ __forceinline__ u32 pack_bf16(float a, float b) {
   v2f f = {a, b};
@@ -501,12 +504,24 @@ hipError_t launch(const GemmArgs<kDump>& a, hipStream_t stream) {
 
 }  // namespace
 
+namespace {
+std::atomic<int> g_path{0};
+}  // namespace
+
+void set_gemm_path_override(int path) { g_path.store(path, std::memory_order_relaxed); }
+
 hipError_t launch_w4a4_gemm_lora_up(const uint8_t* act_codes, const uint16_t* act_scales,
                                     const uint8_t* w_codes, const uint16_t* w_scales,
                                     const uint16_t* lora_act, const uint16_t* lora_up,
                                     const uint16_t* bias, int64_t M, int64_t N, int64_t K,
                                     int64_t r, uint16_t* y, int32_t* acc_dump,
                                     hipStream_t stream) {
+  // Few tokens: the 128 x 128 tile grid leaves most CUs idle; the K-split
+  // kernel streams the weights with every CU instead.
+  const int path = g_path.load(std::memory_order_relaxed);
+  if (path != 1 && skinny_supported(M, N, K) && (path == 2 || M <= kSkinnyMaxM))
+    return launch_w4a4_gemm_skinny(act_codes, act_scales, w_codes, w_scales, lora_act, lora_up,
+                                   bias, M, N, K, r, y, acc_dump, stream);
   if (acc_dump != nullptr) {
     GemmArgs<true> a{act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,
                      y, acc_dump, (int)M, (int)N, (int)K, 0};

@@ -131,6 +131,15 @@ svdq_status svdq_quantize_act_lora_down(
 svdq_status svdq_debug_set_quant_plan(int k_blocks, int tiles_per_wg);
 
 /*
+ * Test hook for call 2 (and svdq_w4a4_group_acc_debug): 0 chooses the kernel
+ * by shape (the K-split kernel for up to 160 tokens, the tiled kernel above),
+ * 1 forces the tiled kernel, 2 the K-split kernel wherever it is supported.
+ * Both compute the same integers and the same dequantization; Y may differ in
+ * fp32 rounding order.  Returns INVALID_VALUE for other values.
+ */
+svdq_status svdq_debug_set_gemm_path(int path);
+
+/*
  * Call 2 - W4A4 GEMM with per-group int32 accumulation, per-group
  * dequantization, the fused low-rank up-projection and the bias
  * (mind-verse.de, section "Nunchaku und SVDQuant": fused kernels for the 4-bit

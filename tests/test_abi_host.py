@@ -133,6 +133,14 @@ def test_quant_plan_hook_arguments():
     assert L.svdq_debug_set_quant_plan(0, 0) == SUCCESS
 
 
+def test_gemm_path_hook_arguments():
+    L = lib()
+    assert L.svdq_debug_set_gemm_path(-1) == INVALID_VALUE
+    assert L.svdq_debug_set_gemm_path(3) == INVALID_VALUE
+    for p in (1, 2, 0):
+        assert L.svdq_debug_set_gemm_path(p) == SUCCESS
+
+
 def _gpu_visible():
     try:
         import torch

@@ -112,6 +112,29 @@ def test_edge_shapes(M, K, N, r):
     _check_y(got["y"], d, lam, packed, ref)
 
 
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("M,K,N,r", [
+    (1, 64, 64, 16), (37, 448, 192, 32), (64, 3072, 1024, 32), (130, 640, 448, 48), (256, 256, 256, 128),
+    (300, 192, 320, 16),
+])
+def test_both_gemm_kernels_parity(path, M, K, N, r):
+    """The tiled kernel (path 1) and the K-split few-token kernel (path 2) on the
+    same shapes: same codes, accumulators and Y within the bar."""
+    import bit_diffusion_transformer_svdq_amd as K_
+    d, lam, packed = custom_case(M, K, N, r, seed=M + K + N)
+    ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
+    K_.debug_set_gemm_path(path)
+    try:
+        got = _run(d, lam, packed)
+        acc = K_.w4a4_group_acc_debug(to_dev(ref["act_codes"]), to_dev(packed["w_codes"])).cpu().numpy()
+    finally:
+        K_.debug_set_gemm_path(0)
+    _check_quant(got, ref)
+    _check_y(got["y"], d, lam, packed, ref)
+    want = O.group_accumulators(ref["act_codes"], packed["w_codes"])
+    assert np.array_equal(acc, want), np.argwhere(acc != want)[:5]
+
+
 @pytest.mark.parametrize("M,K,N", [(37, 192, 320), (200, 128, 64)])
 def test_group_accumulators_bit_exact_ragged(M, K, N):
     import bit_diffusion_transformer_svdq_amd as K_

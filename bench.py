@@ -32,7 +32,8 @@ sys.path.insert(0, ROOT)
 METRIC = "effective TOPS + % int8-MFMA peak, W4A4+LoRA linear M=4608 K=3072 N=12288"
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
-NSETS = 4
+NSETS = 4          # at least this many rotating input/weight/output sets ...
+ROTATE_BYTES = 512e6  # ... and enough of them to exceed the 256 MB last-level cache twice
 GEMM_SRC = os.path.join(ROOT, "bit_diffusion_transformer_svdq_amd", "csrc", "w4a4_gemm_lora_up.hip")
 QUANT_SRC = os.path.join(ROOT, "bit_diffusion_transformer_svdq_amd", "csrc", "quant_lora_down.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mlp_up.json")
@@ -75,8 +76,11 @@ def measure_gpu(spec_name, M, steps, warmup, seed=0):
 
     dev = torch.device("cuda:0")
     K.check_device(0)
+    per_set = (2 * Mv * Kd + 4 * Kd + 2 * r * Kd + 2 * r * N + N * Kd // 2 + 2 * N * Kd // 64 + 2 * N
+               + Mv * Kd // 2 + 2 * Mv * Kd // 64 + 2 * Mv * r + 2 * Mv * N)
+    nsets = int(min(32, max(NSETS, -(-ROTATE_BYTES // per_set))))
     sets = []
-    for _ in range(NSETS):
+    for _ in range(nsets):
         sets.append(dict(
             x=_bf(d["x"], dev), lam=torch.from_numpy(lam).to(dev),
             down=_bf(packed["lora_down"], dev), up=_bf(packed["lora_up"], dev),
@@ -101,23 +105,23 @@ def measure_gpu(spec_name, M, steps, warmup, seed=0):
             evs[2].record(stream)
 
     for i in range(warmup):
-        step(sets[i % NSETS])
+        step(sets[i % nsets])
     torch.cuda.synchronize()
     # wall clock over exactly `steps` steps
     t0 = time.perf_counter()
     for i in range(steps):
-        step(sets[i % NSETS])
+        step(sets[i % nsets])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # per-kernel durations with HIP events on the launch stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for i in range(steps):
-        step(sets[i % NSETS], evs[i])
+        step(sets[i % nsets], evs[i])
     torch.cuda.synchronize()
     tq = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
     tg = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
     return dict(spec=spec, M=Mv, K=Kd, N=N, r=r, wall_s=wall, steps=steps, t_quant=tq, t_gemm=tg,
-                pack_s=pack_s)
+                pack_s=pack_s, nsets=nsets)
 
 
 def cpu_baseline(spec_name, rows=64):
@@ -157,7 +161,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="mlp_up")
     ap.add_argument("--m", type=int, default=0, help="override the token count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -165,6 +169,8 @@ def main():
     ap.add_argument("--extra", default="", help="write per-kernel details of extra shapes here (JSON)")
     ap.add_argument("--extra-configs", default="attn_out,qkv,mlp_down")
     ap.add_argument("--extra-m", default="64,256,1024")
+    ap.add_argument("--small-m", default="64,256",
+                    help="token counts of the same linear reported in the JSON line (HBM-bound regime)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -208,7 +214,7 @@ def main():
         "data": "synthetic (seeded; shapes and value distributions of a 12B-class DiT linear)",
         "config": {"workload": f"{res['spec'].name}: SVDQuant W4A4 linear M={M} K={Kd} N={N} rank={r} "
                                f"group=64 (one 1024x1024 image: 4096 image + 512 text tokens)",
-                   "M": M, "K": Kd, "N": N, "rank": r, "group_size": 64, "buffer_sets": NSETS},
+                   "M": M, "K": Kd, "N": N, "rank": r, "group_size": 64, "buffer_sets": res["nsets"]},
         "pct_int8_peak": 100.0 * ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS,
         "roofline": {"bound": "mfma", "achieved": gemm_tops, "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                      "frac": gemm_tops / INT8_PEAK_TOPS,
@@ -223,6 +229,21 @@ def main():
         },
         "offline_pack_s": res["pack_s"],
     }
+    if args.small_m:
+        # the same linear with few tokens: K-B streams the 18.9 MB of packed
+        # weights, so its figure of merit is HBM bandwidth, not MFMA rate
+        small = []
+        for m in [int(v) for v in args.small_m.split(",") if v]:
+            e = measure_gpu(args.config, m, 100, 50)
+            tq_, tg_ = float(np.mean(e["t_quant"])), float(np.mean(e["t_gemm"]))
+            gb = gemm_min_bytes(e["M"], e["N"], e["K"], e["r"])
+            qb = quant_min_bytes(e["M"], e["K"], e["r"])
+            small.append({"M": e["M"], "buffer_sets": e["nsets"], "us_quant": tq_ * 1e6, "us_gemm": tg_ * 1e6,
+                          "gemm_min_bytes": gb, "gemm_GB/s": gb / tg_ / 1e9,
+                          "gemm_hbm_frac": gb / tg_ / 1e9 / HBM_PEAK_GBS,
+                          "linear_GB/s": (gb + qb) / (tq_ + tg_) / 1e9,
+                          "gemm_TOP/s": 2.0 * e["M"] * e["N"] * e["K"] / tg_ / 1e12})
+        out["small_m"] = small
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_rows)
 

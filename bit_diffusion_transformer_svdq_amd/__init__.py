@@ -22,8 +22,8 @@ import numpy as np
 from ._lib import SvdqError, check, lib
 
 __all__ = ["SvdqError", "lib", "check_device", "quantize_act_lora_down", "w4a4_gemm_lora_up",
-           "w4a4_group_acc_debug", "debug_set_quant_plan", "debug_set_gemm_path", "smooth_from_absmax", "pack_weights",
-           "GROUP_SIZE"]
+           "mlp_pair", "w4a4_group_acc_debug", "debug_set_quant_plan", "debug_set_gemm_path",
+           "EPILOGUES", "smooth_from_absmax", "pack_weights", "GROUP_SIZE"]
 
 GROUP_SIZE = 64
 
@@ -98,9 +98,15 @@ def debug_set_gemm_path(path: int = 0) -> None:
     check(lib().svdq_debug_set_gemm_path(int(path)), "svdq_debug_set_gemm_path")
 
 
+EPILOGUES = {"none": 0, "gelu_tanh": 1}
+
+
 def w4a4_gemm_lora_up(act_codes, act_scales, w_codes, w_scales, lora_act=None, lora_up=None,
-                      bias=None, out=None, stream=None):
-    """Call 2: W4A4 GEMM + per-group dequant + fused lora_up + bias -> Y bf16 [M, N]."""
+                      bias=None, out=None, stream=None, epilogue="none"):
+    """Call 2: W4A4 GEMM + per-group dequant + fused lora_up + bias -> Y bf16 [M, N].
+
+    epilogue "gelu_tanh" applies GELU (tanh form) to y + b before the rounding.
+    """
     torch = _torch()
     M = act_codes.shape[0]
     K = act_codes.shape[1] * 2
@@ -116,12 +122,30 @@ def w4a4_gemm_lora_up(act_codes, act_scales, w_codes, w_scales, lora_act=None, l
     if bias is not None:
         _need(bias, torch.bfloat16, (N,), "bias")
     y = torch.empty((M, N), dtype=torch.bfloat16, device=act_codes.device) if out is None else out
-    st = lib().svdq_w4a4_gemm_lora_up(
+    st = lib().svdq_w4a4_gemm_lora_up_ex(
         _ptr(act_codes), _ptr(act_scales), _ptr(w_codes), _ptr(w_scales),
         _ptr(lora_act) if r else None, _ptr(lora_up) if r else None, _ptr(bias),
-        M, N, K, r, GROUP_SIZE, _ptr(y), _stream(stream))
-    check(st, "svdq_w4a4_gemm_lora_up")
+        M, N, K, r, GROUP_SIZE, EPILOGUES[epilogue], _ptr(y), _stream(stream))
+    check(st, "svdq_w4a4_gemm_lora_up_ex")
     return y
+
+
+def mlp_pair(x, up: dict, down: dict, h_out=None, out=None, stream=None):
+    """An MLP pair on one stream: the up-projection (calls 1 and 2) with the GELU
+    epilogue writes H bf16 [M, N_up], which stays in device memory as the input
+    of the down-projection (calls 1 and 2 again).
+
+    ``up`` and ``down`` hold the packed layer as device tensors: smooth,
+    lora_down (or None), w_codes, w_scales, lora_up (or None), bias (or None).
+    Returns (y bf16 [M, N_down], h)."""
+    codes, scales, la = quantize_act_lora_down(x, up["smooth"], up["lora_down"], stream=stream)
+    h = w4a4_gemm_lora_up(codes, scales, up["w_codes"], up["w_scales"], la if up["lora_up"] is not None
+                          else None, up["lora_up"], up["bias"], out=h_out, stream=stream,
+                          epilogue="gelu_tanh")
+    codes, scales, la = quantize_act_lora_down(h, down["smooth"], down["lora_down"], stream=stream)
+    y = w4a4_gemm_lora_up(codes, scales, down["w_codes"], down["w_scales"], la if down["lora_up"] is not None
+                          else None, down["lora_up"], down["bias"], out=out, stream=stream)
+    return y, h
 
 
 def w4a4_group_acc_debug(act_codes, w_codes, stream=None):

@@ -174,13 +174,15 @@ static svdq_status validate_gemm(const void* act_codes, const void* w_codes, int
   return SVDQ_STATUS_SUCCESS;
 }
 
-svdq_status svdq_w4a4_gemm_lora_up(const void* act_codes, const void* act_scales,
-                                   const void* w_codes, const void* w_scales,
-                                   const void* lora_act, const void* lora_up, const void* bias,
-                                   int64_t M, int64_t N, int64_t K, int64_t r, int64_t group_size,
-                                   void* y, void* stream) {
+svdq_status svdq_w4a4_gemm_lora_up_ex(const void* act_codes, const void* act_scales,
+                                      const void* w_codes, const void* w_scales,
+                                      const void* lora_act, const void* lora_up, const void* bias,
+                                      int64_t M, int64_t N, int64_t K, int64_t r, int64_t group_size,
+                                      int epilogue, void* y, void* stream) {
   svdq_status s = validate_gemm(act_codes, w_codes, M, N, K, r, group_size);
   if (s != SVDQ_STATUS_SUCCESS) return s;
+  if (epilogue != SVDQ_EPILOGUE_NONE && epilogue != SVDQ_EPILOGUE_GELU_TANH)
+    return fail(SVDQ_STATUS_INVALID_VALUE, "unknown epilogue %d", epilogue);
   if (M == 0) return ok();
   if (!act_scales || !w_scales || !y) return fail(SVDQ_STATUS_INVALID_VALUE, "null act_scales/w_scales/y");
   if (r > 0 && (!lora_act || !lora_up))
@@ -194,10 +196,19 @@ svdq_status svdq_w4a4_gemm_lora_up(const void* act_codes, const void* act_scales
       static_cast<const uint8_t*>(act_codes), static_cast<const uint16_t*>(act_scales),
       static_cast<const uint8_t*>(w_codes), static_cast<const uint16_t*>(w_scales),
       static_cast<const uint16_t*>(lora_act), static_cast<const uint16_t*>(lora_up),
-      static_cast<const uint16_t*>(bias), M, N, K, r, static_cast<uint16_t*>(y), nullptr,
+      static_cast<const uint16_t*>(bias), M, N, K, r, epilogue, static_cast<uint16_t*>(y), nullptr,
       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SVDQ_STATUS_HIP_ERROR, "gemm launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+svdq_status svdq_w4a4_gemm_lora_up(const void* act_codes, const void* act_scales,
+                                   const void* w_codes, const void* w_scales,
+                                   const void* lora_act, const void* lora_up, const void* bias,
+                                   int64_t M, int64_t N, int64_t K, int64_t r, int64_t group_size,
+                                   void* y, void* stream) {
+  return svdq_w4a4_gemm_lora_up_ex(act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,
+                                   M, N, K, r, group_size, SVDQ_EPILOGUE_NONE, y, stream);
 }
 
 svdq_status svdq_w4a4_group_acc_debug(const void* act_codes, const void* w_codes, int64_t M,
@@ -212,7 +223,8 @@ svdq_status svdq_w4a4_group_acc_debug(const void* act_codes, const void* w_codes
   if (s != SVDQ_STATUS_SUCCESS) return s;
   hipError_t e = svdq::launch_w4a4_gemm_lora_up(
       static_cast<const uint8_t*>(act_codes), nullptr, static_cast<const uint8_t*>(w_codes), nullptr,
-      nullptr, nullptr, nullptr, M, N, K, 0, nullptr, acc, static_cast<hipStream_t>(stream));
+      nullptr, nullptr, nullptr, M, N, K, 0, SVDQ_EPILOGUE_NONE, nullptr, acc,
+      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SVDQ_STATUS_HIP_ERROR, "gemm debug launch: %s", hipGetErrorString(e));
   return ok();
 }

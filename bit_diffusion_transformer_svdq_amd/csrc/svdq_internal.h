@@ -6,6 +6,19 @@
 
 namespace svdq {
 
+// Output epilogue of call 2: GELU with the tanh approximation (Hendrycks and
+// Gimpel, 2016), 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), for the MLP
+// projections the W4A4 layer serves (mind-verse.de, "Effiziente Optimierung
+// von Diffusionsmodellen durch Nunchaku 4-Bit-Quantisierung", section "Nunchaku
+// Lite: Nahtlose Integration in Diffusers").  With e = exp(2u) the identity
+// 0.5 x (1 + tanh u) = x - x / (e + 1) needs one exponential and one
+// reciprocal, and gives x for e = inf and 0 for e = 0.
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float u = 0.7978845608028654f * __builtin_fmaf(0.044715f * x, x * x, x);
+  const float e = __expf(2.0f * u);
+  return x - __fdividef(x, e + 1.0f);
+}
+
 // Call 1: smoothing + int4 group quantization + packing + fused lora_down.
 // Shapes are validated by the caller: M > 0, K % 64 == 0, r % 16 == 0, r <= 128.
 hipError_t launch_quant_lora_down(const uint16_t* x, const float* lam, const uint16_t* lora_down,
@@ -26,7 +39,7 @@ hipError_t launch_w4a4_gemm_lora_up(const uint8_t* act_codes, const uint16_t* ac
                                     const uint8_t* w_codes, const uint16_t* w_scales,
                                     const uint16_t* lora_act, const uint16_t* lora_up,
                                     const uint16_t* bias,
-                                    int64_t M, int64_t N, int64_t K, int64_t r,
+                                    int64_t M, int64_t N, int64_t K, int64_t r, int epilogue,
                                     uint16_t* y, int32_t* acc_dump, hipStream_t stream);
 
 // Call 2 for few tokens: K split over the waves of a workgroup, weights
@@ -36,7 +49,8 @@ hipError_t launch_w4a4_gemm_skinny(const uint8_t* act_codes, const uint16_t* act
                                    const uint8_t* w_codes, const uint16_t* w_scales,
                                    const uint16_t* lora_act, const uint16_t* lora_up,
                                    const uint16_t* bias, int64_t M, int64_t N, int64_t K,
-                                   int64_t r, uint16_t* y, int32_t* acc_dump, hipStream_t stream);
+                                   int64_t r, int epilogue, uint16_t* y, int32_t* acc_dump,
+                                   hipStream_t stream);
 
 // Test hook: 0 = choose by shape, 1 = always the tiled kernel, 2 = the
 // few-token kernel wherever it is supported.

@@ -130,6 +130,7 @@ struct GemmArgs {
   uint16_t* y;
   int32_t* acc;
   int M, N, K, r;
+  int epilogue;  // 0: none, 1: GELU (tanh form) after the bias
 };
 
 // Workgroup id -> (tile_m, tile_n).  Workgroups are dispatched round-robin over
@@ -459,9 +460,16 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
       for (int j = 0; j < 4; ++j) {
         const int m = m0 + wm * 64 + 16 * j + l16;
         if (m < M && n < N) {
+          float o4[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o4[v] = y[i][j][v] + bb4[v];
+          if (p.epilogue == 1) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) o4[v] = gelu_tanh(o4[v]);
+          }
           uint2 o;
-          o.x = pack_bf16(y[i][j][0] + bb4[0], y[i][j][1] + bb4[1]);
-          o.y = pack_bf16(y[i][j][2] + bb4[2], y[i][j][3] + bb4[3]);
+          o.x = pack_bf16(o4[0], o4[1]);
+          o.y = pack_bf16(o4[2], o4[3]);
           *reinterpret_cast<uint2*>(p.y + (size_t)m * N + n) = o;
         }
       }
@@ -514,21 +522,21 @@ hipError_t launch_w4a4_gemm_lora_up(const uint8_t* act_codes, const uint16_t* ac
                                     const uint8_t* w_codes, const uint16_t* w_scales,
                                     const uint16_t* lora_act, const uint16_t* lora_up,
                                     const uint16_t* bias, int64_t M, int64_t N, int64_t K,
-                                    int64_t r, uint16_t* y, int32_t* acc_dump,
+                                    int64_t r, int epilogue, uint16_t* y, int32_t* acc_dump,
                                     hipStream_t stream) {
   // Few tokens: the 128 x 128 tile grid leaves most CUs idle; the K-split
   // kernel streams the weights with every CU instead.
   const int path = g_path.load(std::memory_order_relaxed);
   if (path != 1 && skinny_supported(M, N, K) && (path == 2 || M <= kSkinnyMaxM))
     return launch_w4a4_gemm_skinny(act_codes, act_scales, w_codes, w_scales, lora_act, lora_up,
-                                   bias, M, N, K, r, y, acc_dump, stream);
+                                   bias, M, N, K, r, epilogue, y, acc_dump, stream);
   if (acc_dump != nullptr) {
     GemmArgs<true> a{act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,
-                     y, acc_dump, (int)M, (int)N, (int)K, 0};
+                     y, acc_dump, (int)M, (int)N, (int)K, 0, 0};
     return launch<true>(a, stream);
   }
   GemmArgs<false> a{act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,
-                    y, nullptr, (int)M, (int)N, (int)K, (int)r};
+                    y, nullptr, (int)M, (int)N, (int)K, (int)r, epilogue};
   return launch<false>(a, stream);
 }
 

@@ -80,6 +80,7 @@ struct SkinnyArgs {
   uint16_t* y;            // [M, N] bf16
   int32_t* dump;          // [M, N, G] int32 (debug variant)
   int M, N, K, G, r;
+  int epilogue;           // 0: none, 1: GELU (tanh form) after the bias
 };
 
 // LDS: [G][16*N16] weight scales and [G][16][4] token scales (bf16), then the
@@ -358,6 +359,7 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkinnyArgs<kDump> a
         const size_t off = (size_t)(((j * 4 + i) * 4 + v) * kSlotStride) + ln;
         o[h] = ((red[off] + red[kSlot + off]) + red[2 * kSlot + off]) + red[3 * kSlot + off];
         if (a.bias) o[h] += __builtin_bit_cast(float, (u32)a.bias[gn + h] << 16);
+        if (a.epilogue == 1) o[h] = gelu_tanh(o[h]);
       }
       *reinterpret_cast<u32*>(a.y + (size_t)gm * a.N + gn) = pack_bf16(o[0], o[1]);
     }
@@ -447,14 +449,15 @@ hipError_t launch_w4a4_gemm_skinny(const uint8_t* act_codes, const uint16_t* act
                                    const uint8_t* w_codes, const uint16_t* w_scales,
                                    const uint16_t* lora_act, const uint16_t* lora_up,
                                    const uint16_t* bias, int64_t M, int64_t N, int64_t K,
-                                   int64_t r, uint16_t* y, int32_t* acc_dump, hipStream_t stream) {
+                                   int64_t r, int epilogue, uint16_t* y, int32_t* acc_dump,
+                                   hipStream_t stream) {
   if (acc_dump != nullptr) {
     SkinnyArgs<true> a{act_codes, act_scales, w_codes, w_scales, nullptr, nullptr, nullptr,
-                       nullptr, acc_dump, (int)M, (int)N, (int)K, (int)(K / 64), 0};
+                       nullptr, acc_dump, (int)M, (int)N, (int)K, (int)(K / 64), 0, 0};
     return launch_skinny<true>(a, stream);
   }
   SkinnyArgs<false> a{act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,
-                      y, nullptr, (int)M, (int)N, (int)K, (int)(K / 64), (int)r};
+                      y, nullptr, (int)M, (int)N, (int)K, (int)(K / 64), (int)r, epilogue};
   return launch_skinny<false>(a, stream);
 }
 

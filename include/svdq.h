@@ -167,6 +167,35 @@ svdq_status svdq_w4a4_gemm_lora_up(
     void* y, void* stream);
 
 /*
+ * Output epilogues of call 2, applied to y + b before the bf16 rounding.
+ * SVDQ_EPILOGUE_GELU_TANH is GELU with the tanh approximation (Hendrycks and
+ * Gimpel, 2016): 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))), as in the MLP
+ * up-projection of a diffusion transformer block; the W4A4 layer serves the
+ * attention and MLP projections (mind-verse.de, "Effiziente Optimierung von
+ * Diffusionsmodellen durch Nunchaku 4-Bit-Quantisierung", section "Nunchaku
+ * Lite: Nahtlose Integration in Diffusers").  Evaluated in fp32 from
+ * exp(2u): relative error a few fp32 ulp, far below the bf16 output rounding.
+ */
+typedef enum {
+  SVDQ_EPILOGUE_NONE = 0,
+  SVDQ_EPILOGUE_GELU_TANH = 1
+} svdq_epilogue;
+
+/*
+ * Call 2 with an output epilogue (svdq_epilogue); arguments and errors as for
+ * svdq_w4a4_gemm_lora_up, plus INVALID_VALUE for an unknown epilogue.  With
+ * SVDQ_EPILOGUE_NONE it is svdq_w4a4_gemm_lora_up.  An MLP pair chains
+ * call 2 (GELU) -> call 1 on its bf16 output -> call 2 of the down-projection
+ * on one stream, with no host round trip.
+ */
+svdq_status svdq_w4a4_gemm_lora_up_ex(
+    const void* act_codes, const void* act_scales,
+    const void* w_codes, const void* w_scales,
+    const void* lora_act, const void* lora_up, const void* bias,
+    int64_t M, int64_t N, int64_t K, int64_t r, int64_t group_size,
+    int epilogue, void* y, void* stream);
+
+/*
  * Test hook for call 2: runs the same main loop as svdq_w4a4_gemm_lora_up and
  * writes the int32 group accumulators acc_g[m,n] (the exact integer sums
  * sum_{k in g} q_x q_w, with any internal scaling removed) instead of Y.

@@ -308,11 +308,12 @@ def group_accumulators(act_codes, w_codes, group: int = GROUP, rows=None, cols=N
 
 
 def linear_output(act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,
-                  group: int = GROUP, rows=None):
+                  group: int = GROUP, rows=None, epilogue=None):
     """Y* = sum_g s_x[m,g] s_w[n,g] acc_g[m,n] + lora_act @ lora_up^T + b (float64).
 
     Returns (Y* float64 [m, N], bf16(Y*) uint16 [m, N]); ``rows`` selects rows.
-    ``bias`` may be None.
+    ``bias`` may be None.  ``epilogue="gelu_tanh"`` applies gelu_tanh to Y*
+    before the rounding.
     """
     rows_idx = np.arange(np.asarray(act_codes).shape[0]) if rows is None else np.asarray(rows)
     acc = group_accumulators(act_codes, w_codes, group, rows=rows_idx)
@@ -326,6 +327,10 @@ def linear_output(act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, b
         y += bf16_to_f64(la[rows_idx]) @ bf16_to_f64(lora_up).T
     if bias is not None:
         y += bf16_to_f64(bias)[None, :]
+    if epilogue == "gelu_tanh":
+        y = gelu_tanh(y)
+    elif epilogue is not None:
+        raise ValueError(f"unknown epilogue {epilogue!r}")
     return y, f64_to_bf16(y)
 
 
@@ -336,3 +341,55 @@ def forward(x_bits, lam, packed: dict, bias, group: int = GROUP, rows=None):
                               packed["w_scales"], a["lora_act"], packed["lora_up"],
                               bias, group, rows=rows)
     return a, y, y_bits
+
+
+# ---------------------------------------------------------------------------
+# Output epilogue and the MLP pair.  The W4A4 layer serves the attention and
+# MLP projections of the transformer (mind-verse.de, "Effiziente Optimierung
+# von Diffusionsmodellen durch Nunchaku 4-Bit-Quantisierung", section "Nunchaku
+# Lite: Nahtlose Integration in Diffusers"); in an MLP the up-projection's
+# output goes through GELU before the down-projection.
+# ---------------------------------------------------------------------------
+
+GELU_C = 0.7978845608028654   # sqrt(2 / pi)
+GELU_A = 0.044715
+
+
+def gelu_tanh(v):
+    """GELU, tanh approximation (Hendrycks and Gimpel, 2016), float64:
+    0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))."""
+    v = np.asarray(v, dtype=np.float64)
+    return 0.5 * v * (1.0 + np.tanh(GELU_C * (v + GELU_A * v ** 3)))
+
+
+def float_mlp_hidden(x_bits, w_bits, bias_bits, rows=None):
+    """bf16(gelu_tanh(X W^T + b)) of the unquantized up-projection, float64.
+
+    The smoothing factors of a layer are calibrated on the activations that
+    reach it; for the down-projection of an MLP these are the GELU outputs of
+    the floating-point model, so its lambda comes from this array's absmax."""
+    x = bf16_to_f64(x_bits)
+    if rows is not None:
+        x = x[np.asarray(rows)]
+    y = x @ bf16_to_f64(w_bits).T + bf16_to_f64(bias_bits)[None, :]
+    return f64_to_bf16(gelu_tanh(y))
+
+
+def mlp_pair(x_bits, lam_up, packed_up: dict, bias_up, lam_down, packed_down: dict, bias_down,
+             group: int = GROUP, rows=None):
+    """Up-projection with the GELU epilogue, its bf16 output H as the input of
+    the down-projection (call 1 then call 2 again).  Every step is local to a
+    token row once lambda is fixed, so ``rows`` computes just those rows.
+
+    Returns dict(h uint16 [m, N_up], y float64 [m, N_down], y_bits uint16, and
+    the intermediates a_up, a_down of call 1)."""
+    x = np.asarray(x_bits) if rows is None else np.asarray(x_bits)[np.asarray(rows)]
+    a_up = quantize_act_lora_down(x, lam_up, packed_up["lora_down"], group)
+    _, h = linear_output(a_up["act_codes"], a_up["act_scales"], packed_up["w_codes"],
+                         packed_up["w_scales"], a_up["lora_act"], packed_up["lora_up"], bias_up,
+                         group, epilogue="gelu_tanh")
+    a_dn = quantize_act_lora_down(h, lam_down, packed_down["lora_down"], group)
+    y, y_bits = linear_output(a_dn["act_codes"], a_dn["act_scales"], packed_down["w_codes"],
+                              packed_down["w_scales"], a_dn["lora_act"], packed_down["lora_up"],
+                              bias_down, group)
+    return {"h": h, "y": y, "y_bits": y_bits, "a_up": a_up, "a_down": a_dn}

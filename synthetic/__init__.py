@@ -13,7 +13,11 @@ tensors with the shapes of a 12B-class DiT linear stand in for them:
 * X ~ N(0, 1) with a fraction of whole input channels carrying outliers;
 * W ~ N(0, 0.02) (standard deviation), optionally with a 0.1 % share of
   entries replaced by 0.02 * t(3) (heavy tails);
-* bias ~ N(0, 0.01).
+* bias ~ N(0, 0.01);
+* for the up-projection of a chained MLP pair, a fraction of whole output
+  channels (rows of W and entries of the bias) scaled by the outlier factor, so
+  that the GELU output feeding the down-projection carries outlier channels of
+  its own.
 
 All values are drawn in float64 from ``numpy.random.default_rng(SeedSequence(
 [config_id, layer_id, tensor_id]))`` and rounded to bfloat16 once (through
@@ -26,11 +30,11 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["LinearSpec", "SPECS", "make_linear", "stack_specs", "to_bf16_bits",
-           "bf16_bits_to_f32"]
+__all__ = ["LinearSpec", "SPECS", "PAIRS", "make_linear", "make_w", "make_bias", "stack_specs",
+           "to_bf16_bits", "bf16_bits_to_f32"]
 
 # tensor ids inside one (config, layer) seed sequence
-_T_X, _T_XOUT, _T_W, _T_WTAIL, _T_BIAS = 0, 1, 2, 3, 4
+_T_X, _T_XOUT, _T_W, _T_WTAIL, _T_BIAS, _T_WROW = 0, 1, 2, 3, 4, 5
 
 
 @dataclass(frozen=True)
@@ -46,6 +50,7 @@ class LinearSpec:
     outlier_scale: float = 1.0
     heavy_tail: bool = False
     gelu_input: bool = False
+    row_outlier_frac: float = 0.0         # fraction of N output channels scaled (rounded)
     layer_id: int = 0
     note: str = field(default="", compare=False)
 
@@ -76,7 +81,15 @@ SPECS = {
     # MLP down-projection; its input is a GELU(tanh) output with its own outliers
     "mlp_down": LinearSpec("mlp_down", 3, 4608, 12288, 3072, 32, outlier_frac=0.01,
                            outlier_scale=30.0, heavy_tail=True, gelu_input=True, layer_id=1),
+    # chained MLP pair: up 3072 -> 12288 whose GELU output (123 channels x30 from
+    # scaled rows of W_up) is the input of down 12288 -> 3072
+    "pair_up": LinearSpec("pair_up", 3, 4608, 3072, 12288, 32, outlier_frac=0.01,
+                          outlier_scale=30.0, heavy_tail=True, row_outlier_frac=0.01, layer_id=2),
+    "pair_down": LinearSpec("pair_down", 3, 4608, 12288, 3072, 32, heavy_tail=True, layer_id=3),
 }
+
+# chained pairs: name -> (up spec, down spec)
+PAIRS = {"mlp_pair": ("pair_up", "pair_down")}
 
 
 def stack_specs(batch: int = 1):
@@ -140,6 +153,11 @@ def make_x(spec: LinearSpec) -> np.ndarray:
     return to_bf16_bits(x)
 
 
+def _outlier_rows(spec: LinearSpec) -> np.ndarray:
+    cnt = int(round(spec.row_outlier_frac * spec.N))
+    return _rng(spec, _T_WROW).choice(spec.N, size=cnt, replace=False) if cnt else np.zeros(0, np.int64)
+
+
 def make_w(spec: LinearSpec) -> np.ndarray:
     """Weights [N, K] as bf16 bits."""
     w = _rng(spec, _T_W).standard_normal((spec.N, spec.K)) * 0.02
@@ -148,11 +166,14 @@ def make_w(spec: LinearSpec) -> np.ndarray:
         cnt = int(round(0.001 * spec.N * spec.K))
         idx = g.choice(spec.N * spec.K, size=cnt, replace=False)
         w.reshape(-1)[idx] = 0.02 * g.standard_t(3.0, size=cnt)
+    w[_outlier_rows(spec)] *= spec.outlier_scale
     return to_bf16_bits(w)
 
 
 def make_bias(spec: LinearSpec) -> np.ndarray:
-    return to_bf16_bits(_rng(spec, _T_BIAS).standard_normal(spec.N) * 0.01)
+    b = _rng(spec, _T_BIAS).standard_normal(spec.N) * 0.01
+    b[_outlier_rows(spec)] *= spec.outlier_scale
+    return to_bf16_bits(b)
 
 
 def make_linear(spec: LinearSpec | str, M: int | None = None) -> dict:

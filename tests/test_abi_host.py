@@ -117,6 +117,26 @@ def test_gemm_argument_errors(kw, status):
     assert _gemm(**kw) == status
 
 
+def test_gemm_epilogue_argument():
+    """The _ex entry point accepts the declared epilogues and rejects others
+    before any device call; the plain entry point is the no-epilogue case."""
+    L = lib()
+
+    def ex(ep, **kw):
+        a = dict(M=64)
+        a.update(kw)
+        return L.svdq_w4a4_gemm_lora_up_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["M"], 256, 256,
+                                           16, 64, ep, FAKE, None)
+    for bad in (-1, 2, 7):
+        assert ex(bad) == INVALID_VALUE
+        assert b"epilogue" in L.svdq_last_error()
+        assert ex(bad, M=0) == INVALID_VALUE
+    for good in (0, 1):
+        assert ex(good, M=0) == SUCCESS
+        if not _gpu_visible():
+            assert ex(good) == NO_DEVICE
+
+
 def test_debug_hook_argument_errors():
     L = lib()
     assert L.svdq_w4a4_group_acc_debug(FAKE, FAKE, 4, 64, 64, 64, None, None) == INVALID_VALUE

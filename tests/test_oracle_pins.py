@@ -476,3 +476,72 @@ def test_activation_quantizer_tiny_groups_reading():
     assert np.array_equal(q[0, :64], np.clip(np.rint(xv[:64] / s[0]), -7, 7))
     assert q[0, 0] == -7 and q[0, 63] == 7
     assert not np.any(q[0, 64:])
+
+
+def test_gelu_tanh_pins():
+    """The tanh-form GELU against closed forms: g(x) - g(-x) = x exactly (the
+    tanh terms cancel), g(0) = 0, g -> x for large x and -> 0 for large -x, and
+    the exact GELU x*Phi(x) (math.erf) within the approximation's error."""
+    import math
+    x = np.linspace(-8, 8, 4001)
+    g = O.gelu_tanh(x)
+    assert np.allclose(g - O.gelu_tanh(-x), x, rtol=0, atol=1e-13)
+    assert O.gelu_tanh(0.0) == 0.0
+    assert abs(O.gelu_tanh(12.0) - 12.0) < 1e-12 and abs(O.gelu_tanh(-12.0)) < 1e-12
+    exact = np.array([v * 0.5 * (1.0 + math.erf(v / math.sqrt(2.0))) for v in x])
+    err = np.abs(g - exact).max()
+    assert 1e-5 < err < 1e-3, err
+
+
+def test_mlp_pair_chains_the_two_calls():
+    """mlp_pair is call 1 + call 2 (GELU) on the up weights, then call 1 + call 2
+    on the bf16 GELU output with the down weights, each step as defined above;
+    a row subset gives the same rows (every step is per token once lambda is fixed)."""
+    up = S.LinearSpec("pair_up", 9, 48, 128, 192, 16, outlier_channels=3, outlier_scale=20.0,
+                      row_outlier_frac=0.05)
+    dn = S.LinearSpec("pair_dn", 9, 48, 192, 128, 16, layer_id=1)
+    du = S.make_linear(up)
+    wd, bd = S.make_w(dn), S.make_bias(dn)
+    lam_u = O.smooth_factors(O.activation_absmax(du["x"]), du["w"])
+    pu = O.pack_weights(du["w"], lam_u, 16)
+    a_u, y_u, _ = O.forward(du["x"], lam_u, pu, du["bias"])
+    h = O.f64_to_bf16(O.gelu_tanh(y_u))
+    lam_d = O.smooth_factors(O.activation_absmax(O.float_mlp_hidden(du["x"], du["w"], du["bias"])), wd)
+    pd = O.pack_weights(wd, lam_d, 16)
+    res = O.mlp_pair(du["x"], lam_u, pu, du["bias"], lam_d, pd, bd)
+    assert np.array_equal(res["h"], h)
+    _, y_d, yb_d = O.forward(h, lam_d, pd, bd)
+    assert np.array_equal(res["y_bits"], yb_d) and np.array_equal(res["y"], y_d)
+    rows = [0, 5, 47]
+    sub = O.mlp_pair(du["x"], lam_u, pu, du["bias"], lam_d, pd, bd, rows=rows)
+    assert np.array_equal(sub["y_bits"], res["y_bits"][rows]) and np.array_equal(sub["h"], h[rows])
+
+
+def test_float_mlp_hidden_brute_force():
+    """The calibration activations against scalar loops in exact rationals on a
+    tiny case (the tanh itself in float64)."""
+    import math
+    from fractions import Fraction
+    rng = np.random.default_rng(3)
+    x = S.to_bf16_bits(rng.standard_normal((3, 5)))
+    w = S.to_bf16_bits(rng.standard_normal((4, 5)) * 0.5)
+    b = S.to_bf16_bits(rng.standard_normal(4) * 0.1)
+    got = O.float_mlp_hidden(x, w, b)
+    xf, wf, bf = (S.bf16_bits_to_f32(a).astype(np.float64) for a in (x, w, b))
+    for m in range(3):
+        for n in range(4):
+            z = float(sum(Fraction(xf[m, k]) * Fraction(wf[n, k]) for k in range(5)) + Fraction(bf[n]))
+            g = 0.5 * z * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z ** 3)))
+            want = O.f64_to_bf16(np.array([g]))[0]
+            assert abs(int(got[m, n]) - int(want)) <= 1, (m, n, got[m, n], want)
+
+
+def test_pair_up_rows_carry_outliers():
+    """The synthetic up-projection of the chained pair scales round(1 % of N)
+    output channels by 30 (rows of W and the bias), the rest as the plain spec."""
+    spec = S.LinearSpec("rows", 9, 8, 64, 300, 16, row_outlier_frac=0.01, outlier_scale=30.0)
+    plain = S.LinearSpec("rows", 9, 8, 64, 300, 16, outlier_scale=30.0)
+    w, w0 = S.bf16_bits_to_f32(S.make_w(spec)), S.bf16_bits_to_f32(S.make_w(plain))
+    ratio = np.abs(w).max(axis=1) / np.abs(w0).max(axis=1)
+    big = np.flatnonzero(np.abs(ratio - 30.0) < 0.5)
+    assert big.size == 3 and np.all(np.abs(ratio[np.setdiff1d(np.arange(300), big)] - 1.0) < 1e-6)

@@ -124,6 +124,93 @@ def measure_gpu(spec_name, M, steps, warmup, seed=0):
                 pack_s=pack_s, nsets=nsets)
 
 
+def _pack_dev(K, w, lam, bias, r, dev, seed=0):
+    import torch
+    packed = K.pack_weights(w, lam, r, seed=seed)
+    return {"smooth": torch.from_numpy(lam).to(dev),
+            "lora_down": _bf(packed["lora_down"], dev) if r else None,
+            "lora_up": _bf(packed["lora_up"], dev) if r else None,
+            "w_codes": torch.from_numpy(packed["w_codes"]).to(dev), "w_scales": _bf(packed["w_scales"], dev),
+            "bias": _bf(bias, dev)}
+
+
+def measure_pair(pair_name, steps, warmup):
+    """The chained MLP pair: up-projection with the GELU epilogue, H [M, N_up] bf16
+    left in HBM, down-projection on H; four launches on one stream per step."""
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K
+    import synthetic as S
+
+    su, sd = (S.SPECS[n] for n in S.PAIRS[pair_name])
+    du = S.make_linear(su)
+    wd, bd = S.make_w(sd), S.make_bias(sd)
+    dev = torch.device("cuda:0")
+    K.check_device(0)
+    absmax = np.abs(S.bf16_bits_to_f32(du["x"])).max(axis=0).astype(np.float32)
+    up = _pack_dev(K, du["w"], K.smooth_from_absmax(absmax, du["w"]), du["bias"], su.r, dev)
+    # the down-projection's smoothing is calibrated on the float model's GELU
+    # output (offline set-up, outside the timed region)
+    x = _bf(du["x"], dev)
+    with torch.no_grad():
+        hf = torch.nn.functional.gelu(x.float() @ _bf(du["w"], dev).float().T + _bf(du["bias"], dev).float(),
+                                      approximate="tanh")
+        habs = hf.abs().amax(dim=0).cpu().numpy().astype(np.float32)
+    del hf
+    down = _pack_dev(K, wd, K.smooth_from_absmax(habs, wd), bd, sd.r, dev)
+    M, N_up, N_dn = su.M, su.N, sd.N
+    per_set = 2 * M * su.K + 2 * M * N_up + 2 * M * N_dn
+    nsets = int(min(16, max(2, -(-ROTATE_BYTES // per_set))))
+    sets = [dict(x=x.clone(), h=torch.empty((M, N_up), dtype=torch.bfloat16, device=dev),
+                 y=torch.empty((M, N_dn), dtype=torch.bfloat16, device=dev)) for _ in range(nsets)]
+    stream = torch.cuda.current_stream()
+    bufs = dict(cu=torch.empty((M, su.K // 2), dtype=torch.uint8, device=dev),
+                su=torch.empty((M, su.K // 64), dtype=torch.bfloat16, device=dev),
+                lu=torch.empty((M, su.r), dtype=torch.bfloat16, device=dev),
+                cd=torch.empty((M, sd.K // 2), dtype=torch.uint8, device=dev),
+                sd=torch.empty((M, sd.K // 64), dtype=torch.bfloat16, device=dev),
+                ld=torch.empty((M, sd.r), dtype=torch.bfloat16, device=dev))
+
+    def step(s, evs=None):
+        rec = (lambda i: evs[i].record(stream)) if evs is not None else (lambda i: None)
+        rec(0)
+        K.quantize_act_lora_down(s["x"], up["smooth"], up["lora_down"], out=(bufs["cu"], bufs["su"], bufs["lu"]),
+                                 stream=stream)
+        rec(1)
+        K.w4a4_gemm_lora_up(bufs["cu"], bufs["su"], up["w_codes"], up["w_scales"], bufs["lu"], up["lora_up"],
+                            up["bias"], out=s["h"], stream=stream, epilogue="gelu_tanh")
+        rec(2)
+        K.quantize_act_lora_down(s["h"], down["smooth"], down["lora_down"], out=(bufs["cd"], bufs["sd"], bufs["ld"]),
+                                 stream=stream)
+        rec(3)
+        K.w4a4_gemm_lora_up(bufs["cd"], bufs["sd"], down["w_codes"], down["w_scales"], bufs["ld"],
+                            down["lora_up"], down["bias"], out=s["y"], stream=stream)
+        rec(4)
+
+    for i in range(warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for i in range(steps):
+        step(sets[i % nsets], evs[i])
+    torch.cuda.synchronize()
+    t = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e-3 for j in range(4)]
+    ops = 2.0 * M * su.K * N_up + 2.0 * M * sd.K * N_dn
+    return {"workload": f"{pair_name}: up M={M} K={su.K} N={N_up} + GELU-tanh epilogue, H bf16 in HBM, "
+                        f"down K={sd.K} N={N_dn}, rank {su.r}, group 64",
+            "buffer_sets": nsets, "us_per_pair": wall * 1e6, "eff_TOPS": ops / wall / 1e12,
+            "pct_int8_peak": 100.0 * ops / wall / 1e12 / INT8_PEAK_TOPS,
+            "us_quant_up": t[0] * 1e6, "us_gemm_up_gelu": t[1] * 1e6,
+            "us_quant_down": t[2] * 1e6, "us_gemm_down": t[3] * 1e6,
+            "quant_down_GB/s": quant_min_bytes(M, sd.K, sd.r) / t[2] / 1e9,
+            "gemm_up_TOP/s": 2.0 * M * su.K * N_up / t[1] / 1e12,
+            "gemm_down_TOP/s": 2.0 * M * sd.K * N_dn / t[3] / 1e12}
+
+
 def cpu_baseline(spec_name, rows=64):
     """The oracle as written, single-threaded, on a bounded row sample of the workload."""
     from threadpoolctl import threadpool_limits
@@ -171,6 +258,8 @@ def main():
     ap.add_argument("--extra-m", default="64,256,1024")
     ap.add_argument("--small-m", default="64,256",
                     help="token counts of the same linear reported in the JSON line (HBM-bound regime)")
+    ap.add_argument("--pair", default="mlp_pair",
+                    help="chained pair reported in the JSON line ('' to skip)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -244,6 +333,8 @@ def main():
                           "linear_GB/s": (gb + qb) / (tq_ + tg_) / 1e9,
                           "gemm_TOP/s": 2.0 * e["M"] * e["N"] * e["K"] / tg_ / 1e12})
         out["small_m"] = small
+    if args.pair:
+        out["mlp_pair"] = measure_pair(args.pair, 50, 20)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_rows)
 

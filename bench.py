@@ -211,6 +211,111 @@ def measure_pair(pair_name, steps, warmup):
             "gemm_down_TOP/s": 2.0 * M * sd.K * N_dn / t[3] / 1e12}
 
 
+def measure_stack(batch, steps, warmup):
+    """One denoising step's linear stack of a FLUX-like 12B DiT: 228 SVDQuant
+    linears (456 launches), each layer with its own device buffers of packed
+    weights, run back to back on one stream, eagerly and as one captured HIP
+    graph.  Packing all 228 layers on the host would take minutes and the
+    timing does not depend on the values, so each of the 6 distinct weight
+    shapes is packed once and copied into every layer's own buffers; the MLP
+    up-projections of the double-stream blocks carry the GELU epilogue."""
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K
+    import synthetic as S
+
+    specs = S.stack_specs(batch)
+    dev = torch.device("cuda:0")
+    K.check_device(0)
+    first_kn, first_mk = {}, {}
+    for sp in specs:
+        first_kn.setdefault((sp.K, sp.N), sp)
+        first_mk.setdefault((sp.M, sp.K), sp)
+    xs = {mk: _bf(S.make_x(sp), dev) for mk, sp in first_mk.items()}
+    shape_pack = {}
+    for kn, sp in first_kn.items():
+        w = S.make_w(sp)
+        # smoothing from the activations of the first layer with this K
+        xm = next(v for (m, k), v in xs.items() if k == kn[0])
+        absmax = xm.float().abs().amax(dim=0).cpu().numpy().astype(np.float32)
+        shape_pack[kn] = _pack_dev(K, w, K.smooth_from_absmax(absmax, w), S.make_bias(sp), sp.r, dev)
+    layers = []
+    for sp in specs:
+        src = shape_pack[(sp.K, sp.N)]
+        layers.append(dict(spec=sp, w={k: (None if v is None else v.clone()) for k, v in src.items()},
+                           gelu=sp.name.startswith("double") and sp.N == 12288))
+    quant = {mk: (torch.empty((mk[0], mk[1] // 2), dtype=torch.uint8, device=dev),
+                  torch.empty((mk[0], mk[1] // 64), dtype=torch.bfloat16, device=dev),
+                  torch.empty((mk[0], 32), dtype=torch.bfloat16, device=dev)) for mk in first_mk}
+    ys = {}
+    for sp in specs:
+        ys.setdefault((sp.M, sp.N), torch.empty((sp.M, sp.N), dtype=torch.bfloat16, device=dev))
+    stream = torch.cuda.Stream()
+
+    def step():
+        for L in layers:
+            sp, w = L["spec"], L["w"]
+            q = quant[(sp.M, sp.K)]
+            K.quantize_act_lora_down(xs[(sp.M, sp.K)], w["smooth"], w["lora_down"], out=q, stream=stream)
+            K.w4a4_gemm_lora_up(q[0], q[1], w["w_codes"], w["w_scales"], q[2], w["lora_up"], w["bias"],
+                                out=ys[(sp.M, sp.N)], stream=stream,
+                                epilogue="gelu_tanh" if L["gelu"] else "none")
+
+    def timed(fn):
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                fn()
+            torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    ops = sum(2.0 * sp.M * sp.N * sp.K for sp in specs)
+    t_eager = timed(step)
+    # per-shape breakdown from HIP events around every launch of one more eager step
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers]
+    with torch.cuda.stream(stream):
+        for L, e in zip(layers, evs):
+            sp, w = L["spec"], L["w"]
+            q = quant[(sp.M, sp.K)]
+            e[0].record(stream)
+            K.quantize_act_lora_down(xs[(sp.M, sp.K)], w["smooth"], w["lora_down"], out=q, stream=stream)
+            e[1].record(stream)
+            K.w4a4_gemm_lora_up(q[0], q[1], w["w_codes"], w["w_scales"], q[2], w["lora_up"], w["bias"],
+                                out=ys[(sp.M, sp.N)], stream=stream,
+                                epilogue="gelu_tanh" if L["gelu"] else "none")
+            e[2].record(stream)
+    torch.cuda.synchronize()
+    by = {}
+    for L, e in zip(layers, evs):
+        sp = L["spec"]
+        b = by.setdefault((sp.M, sp.K, sp.N), [0, 0.0, 0.0])
+        b[0] += 1
+        b[1] += e[0].elapsed_time(e[1]) * 1e3
+        b[2] += e[1].elapsed_time(e[2]) * 1e3
+    by_shape = [{"M": m, "K": k, "N": n, "count": c, "us_quant": tq / c, "us_gemm": tg / c,
+                 "gemm_TOP/s": 2.0 * m * n * k / (tg / c) / 1e6, "share_of_step": (tq + tg) / (t_eager * 1e6)}
+                for (m, k, n), (c, tq, tg) in sorted(by.items())]
+    out = {"workload": f"denoising-step linear stack, batch {batch}: 19 double-stream blocks (image "
+                       f"{4096 * batch} and text {512 * batch} tokens; QKV, out, MLP up with GELU, MLP down) "
+                       f"+ 38 single-stream blocks ({4608 * batch} tokens; 3072->21504, 15360->3072), r=32",
+           "layers": len(specs), "launches": 2 * len(specs), "ops_per_step": ops,
+           "weight_bytes": int(sum(v.numel() * v.element_size() for L in layers for v in L["w"].values()
+                                   if v is not None)),
+           "ms_eager": t_eager * 1e3, "eff_TOPS_eager": ops / t_eager / 1e12, "by_shape": by_shape}
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step()
+        t_graph = timed(g.replay)
+        out.update({"ms_graph": t_graph * 1e3, "eff_TOPS_graph": ops / t_graph / 1e12,
+                    "pct_int8_peak_graph": 100.0 * ops / t_graph / 1e12 / INT8_PEAK_TOPS})
+    except Exception as e:  # capture problems are reported, not fatal to the bench
+        out["graph_error"] = f"{type(e).__name__}: {e}"
+    return out
+
+
 def cpu_baseline(spec_name, rows=64):
     """The oracle as written, single-threaded, on a bounded row sample of the workload."""
     from threadpoolctl import threadpool_limits
@@ -260,6 +365,8 @@ def main():
                     help="token counts of the same linear reported in the JSON line (HBM-bound regime)")
     ap.add_argument("--pair", default="mlp_pair",
                     help="chained pair reported in the JSON line ('' to skip)")
+    ap.add_argument("--stack", type=int, default=1,
+                    help="batch of the denoising-step stack reported in the JSON line (0 to skip)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -335,6 +442,8 @@ def main():
         out["small_m"] = small
     if args.pair:
         out["mlp_pair"] = measure_pair(args.pair, 50, 20)
+    if args.stack:
+        out["step_stack"] = measure_stack(args.stack, 5, 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_rows)
 

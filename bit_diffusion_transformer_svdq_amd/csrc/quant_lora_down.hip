@@ -49,6 +49,7 @@
 
 #include <algorithm>
 #include <map>
+#include <vector>
 #include <mutex>
 #include <utility>
 
@@ -432,7 +433,10 @@ Plan make_plan(int T, int G, int NT, int cus) {
 int g_force_tb = 0, g_force_kb = 0;  // test hook (0 = automatic)
 
 // Per device and stream: T counters (zero between launches) followed by the
-// partial sums.  Calls on one stream are ordered, so they can share it.
+// partial sums.  Calls on one stream are ordered, so they can share it.  A
+// workspace that is outgrown is kept, not freed: a graph captured earlier on
+// that stream still holds its address, and its counters are still zero
+// whenever no launch that uses them is running.
 struct Workspace {
   void* ptr = nullptr;
   size_t count_cap = 0;   // counters known to be zero
@@ -440,6 +444,7 @@ struct Workspace {
 };
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::vector<void*> g_retired;  // outgrown workspaces, alive until the process ends
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -508,12 +513,14 @@ hipError_t launch_quant_lora_down(const uint16_t* x, const float* lam, const uin
     const size_t part_need = (size_t)p.KB * T * NT * 64 * 16;
     Workspace& w = g_ws[{dev, stream}];
     if (w.count_cap < (size_t)T || w.part_bytes < part_need) {
+      // allocating is not allowed while the stream is being captured into a graph
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      e = hipStreamIsCapturing(stream, &cs);
+      if (e != hipSuccess) return e;
+      if (cs != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
       if (w.ptr) {
-        e = hipStreamSynchronize(stream);  // earlier launches on this stream may still use it
-        if (e != hipSuccess) return e;
-        e = hipFree(w.ptr);
+        g_retired.push_back(w.ptr);
         w = Workspace{};
-        if (e != hipSuccess) return e;
       }
       const size_t cap = std::max<size_t>(T, 64) + T / 4;
       const size_t pb = part_need + part_need / 4;

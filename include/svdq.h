@@ -108,11 +108,16 @@ svdq_status svdq_check_device(int device);
  * Workspace: when K is split over several workgroups, the fp32 partial sums of
  * lora_act go through a device workspace that the library owns, one per
  * (device, stream), allocated and zero-filled on first use and grown when a
- * call needs more (the growth waits for `stream` and frees the old one).  The
- * first call on a stream for a given size therefore allocates: make it
- * outside graph capture.  Calls that share a stream are ordered by it; calls
- * on different streams use different workspaces.  The result of a call does
- * not depend on timing (partials are added in a fixed order).
+ * call needs more.  An outgrown workspace is kept until the process ends, so a
+ * graph captured before the growth stays valid.  The first call on a stream
+ * for a given size therefore allocates: make it outside graph capture; a call
+ * that would allocate while `stream` is capturing returns HIP_ERROR
+ * (hipErrorStreamCaptureUnsupported) and enqueues nothing.  Calls that share a
+ * stream are ordered by it; calls on different streams use different
+ * workspaces.  A graph captured on a stream uses that stream's workspace:
+ * replay it on the same stream (or make sure no other launch using that
+ * workspace runs at the same time).  The result of a call does not depend on timing (partials are
+ * added in a fixed order).
  */
 svdq_status svdq_quantize_act_lora_down(
     const void* x, const float* smooth, const void* lora_down,

@@ -1,0 +1,118 @@
+"""The two calls inside a captured HIP graph.  Needs an MI355X.
+
+A chain of layers (an MLP pair and a third linear whose call 1 splits K over
+workgroups, so the library's per-stream workspace is used) is run eagerly,
+then captured on the same stream and replayed several times with eager work in
+between; every replay must reproduce the eager outputs bit for bit (the
+kernels are the same and deterministic).  A call that would have to allocate
+its workspace during capture fails cleanly instead.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from tests.gpu_util import custom_case, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    from bit_diffusion_transformer_svdq_amd import check_device
+    check_device(0)
+
+
+def _layer(case):
+    d, lam, packed = case
+    r = packed["lora_down"].shape[0]
+    return {"smooth": to_dev(np.asarray(lam, np.float32)),
+            "lora_down": to_dev_bf16(packed["lora_down"]) if r else None,
+            "lora_up": to_dev_bf16(packed["lora_up"]) if r else None,
+            "w_codes": to_dev(packed["w_codes"]), "w_scales": to_dev_bf16(packed["w_scales"]),
+            "bias": to_dev_bf16(d["bias"])}
+
+
+def test_graph_replays_match_eager():
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K
+    M = 200
+    up_c, dn_c, third_c = custom_case(M, 256, 512, 16, seed=71), custom_case(M, 512, 256, 16, seed=72), \
+        custom_case(M, 1024, 192, 32, seed=73)
+    up, dn, third = _layer(up_c), _layer(dn_c), _layer(third_c)
+    x = to_dev_bf16(up_c[0]["x"])
+    x3 = to_dev_bf16(third_c[0]["x"])
+    h = torch.empty((M, 512), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((M, 256), dtype=torch.bfloat16, device="cuda")
+    y3 = torch.empty((M, 192), dtype=torch.bfloat16, device="cuda")
+    q3 = (torch.empty((M, 512), dtype=torch.uint8, device="cuda"),
+          torch.empty((M, 16), dtype=torch.bfloat16, device="cuda"),
+          torch.empty((M, 32), dtype=torch.bfloat16, device="cuda"))
+    s = torch.cuda.Stream()
+
+    def chain():
+        K.mlp_pair(x, up, dn, h_out=h, out=y)
+        c, sc, la = K.quantize_act_lora_down(x3, third["smooth"], third["lora_down"], out=q3)
+        K.w4a4_gemm_lora_up(c, sc, third["w_codes"], third["w_scales"], la, third["lora_up"], third["bias"],
+                            out=y3)
+
+    K.debug_set_quant_plan(3, 0)   # call 1 splits K into 3 blocks: partials go through the workspace
+    try:
+        with torch.cuda.stream(s):
+            chain()                  # eager, on the capture stream (allocates its workspace)
+        torch.cuda.synchronize()
+        want = [t.clone() for t in (h, y, y3, *q3)]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            chain()
+        torch.cuda.synchronize()
+        for rep in range(3):
+            # everything on the capture stream: the graph's launches use that
+            # stream's workspace, like the eager calls on it
+            with torch.cuda.stream(s):
+                for t in (h, y, y3, *q3):
+                    t.zero_()
+                chain()              # eager work on the same stream between replays
+                for t in (h, y, y3, *q3):
+                    t.fill_(7)
+                g.replay()
+            torch.cuda.synchronize()
+            for got, w in zip((h, y, y3, *q3), want):
+                assert torch.equal(got, w), rep
+    finally:
+        K.debug_set_quant_plan(0, 0)
+    # the chain's codes of the third layer are still the oracle's
+    ref = O.quantize_act_lora_down(third_c[0]["x"], third_c[1], third_c[2]["lora_down"])
+    assert np.array_equal(q3[0].cpu().numpy(), ref["act_codes"])
+
+
+def test_workspace_growth_during_capture_is_refused():
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K
+    d, lam, packed = custom_case(64, 1024, 64, 16, seed=74)
+    L = _layer((d, lam, packed))
+    x = to_dev_bf16(d["x"])
+    out = (torch.empty((64, 512), dtype=torch.uint8, device="cuda"),
+           torch.empty((64, 16), dtype=torch.bfloat16, device="cuda"),
+           torch.empty((64, 16), dtype=torch.bfloat16, device="cuda"))
+    s = torch.cuda.Stream()        # fresh stream: no workspace yet
+    K.debug_set_quant_plan(4, 0)
+    g = torch.cuda.CUDAGraph()
+    err = None
+    try:
+        with torch.cuda.graph(g, stream=s):
+            try:
+                K.quantize_act_lora_down(x, L["smooth"], L["lora_down"], out=out)
+            except K.SvdqError as e:
+                err = str(e)
+    finally:
+        K.debug_set_quant_plan(0, 0)
+    torch.cuda.synchronize()
+    assert err is not None and "captur" in err.lower(), err
+    # outside capture the same call allocates and works
+    with torch.cuda.stream(s):
+        c, _, _ = K.quantize_act_lora_down(x, L["smooth"], L["lora_down"], out=out)
+    torch.cuda.synchronize()
+    ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
+    assert np.array_equal(c.cpu().numpy(), ref["act_codes"])

@@ -393,3 +393,61 @@ def mlp_pair(x_bits, lam_up, packed_up: dict, bias_up, lam_down, packed_down: di
                               packed_down["w_scales"], a_dn["lora_act"], packed_down["lora_up"],
                               bias_down, group)
     return {"h": h, "y": y, "y_bits": y_bits, "a_up": a_up, "a_down": a_dn}
+
+
+# ---------------------------------------------------------------------------
+# Fused QKV epilogue.  For FLUX.1-dev the engine merges the Q, K and V
+# projections into one quantized to_qkv module because its fused operator
+# handles the QKV projection, the Q/K normalization and the rotary embeddings
+# together (mind-verse.de, "Effiziente Optimierung von Diffusionsmodellen durch
+# Nunchaku 4-Bit-Quantisierung", section "Quantisierung von Modellen mit
+# strukturellen Umschreibungen").  The page names the three steps only; their
+# definitions here are the textbook ones: RMSNorm (Zhang and Sennrich, 2019)
+# over each head's channels with a learned scale, then the rotary position
+# embedding of RoFormer (Su et al., 2021), which turns each pair of adjacent
+# channels (2i, 2i+1) of a head by a per-token angle.  Y = [Q | K | V] along N.
+# ---------------------------------------------------------------------------
+
+def rms_norm_heads(y, head_dim: int, weight_bits, eps: float):
+    """z = y / sqrt(mean over the head's channels of y^2 + eps) * w, float64."""
+    y = np.asarray(y, dtype=np.float64)
+    m, n = y.shape
+    h = y.reshape(m, n // head_dim, head_dim)
+    ms = (h * h).mean(axis=-1, keepdims=True)
+    w = bf16_to_f64(weight_bits)[None, None, :]
+    return (h / np.sqrt(ms + eps) * w).reshape(m, n)
+
+
+def rope_pairs(z, head_dim: int, cos, sin):
+    """Rotate each adjacent pair (2i, 2i+1) of every head by the token's angle i:
+    (a, b) -> (a cos - b sin, a sin + b cos).  cos, sin: [m, head_dim/2]."""
+    z = np.asarray(z, dtype=np.float64)
+    m, n = z.shape
+    h = z.reshape(m, n // head_dim, head_dim // 2, 2)
+    c = np.asarray(cos, dtype=np.float64)[:, None, :]
+    s_ = np.asarray(sin, dtype=np.float64)[:, None, :]
+    a, b = h[..., 0], h[..., 1]
+    out = np.stack([a * c - b * s_, a * s_ + b * c], axis=-1)
+    return out.reshape(m, n)
+
+
+def qkv_norm_rope(y_star, head_dim: int, q_norm_bits, k_norm_bits, eps: float, cos, sin):
+    """Q and K thirds of Y*: RMSNorm per head, then the rotary embedding; the V
+    third unchanged.  Returns (float64 [m, N], bf16 bits)."""
+    y = np.asarray(y_star, dtype=np.float64)
+    sec = y.shape[1] // 3
+    q = rope_pairs(rms_norm_heads(y[:, :sec], head_dim, q_norm_bits, eps), head_dim, cos, sin)
+    k = rope_pairs(rms_norm_heads(y[:, sec:2 * sec], head_dim, k_norm_bits, eps), head_dim, cos, sin)
+    out = np.concatenate([q, k, y[:, 2 * sec:]], axis=1)
+    return out, f64_to_bf16(out)
+
+
+def qkv_output(act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias, head_dim: int,
+               q_norm_bits, k_norm_bits, eps: float, cos, sin, group: int = GROUP, rows=None):
+    """Call 2 with the fused QKV epilogue: linear_output, then qkv_norm_rope on
+    the unrounded Y* (the fused operator rounds once, at the end)."""
+    y, _ = linear_output(act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias, group,
+                         rows=rows)
+    sel = slice(None) if rows is None else np.asarray(rows)
+    return qkv_norm_rope(y, head_dim, q_norm_bits, k_norm_bits, eps, np.asarray(cos)[sel],
+                         np.asarray(sin)[sel])

@@ -31,10 +31,10 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = ["LinearSpec", "SPECS", "PAIRS", "make_linear", "make_w", "make_bias", "stack_specs",
-           "to_bf16_bits", "bf16_bits_to_f32"]
+           "make_rope_tables", "make_norm_weight", "to_bf16_bits", "bf16_bits_to_f32"]
 
 # tensor ids inside one (config, layer) seed sequence
-_T_X, _T_XOUT, _T_W, _T_WTAIL, _T_BIAS, _T_WROW = 0, 1, 2, 3, 4, 5
+_T_X, _T_XOUT, _T_W, _T_WTAIL, _T_BIAS, _T_WROW, _T_NORM = 0, 1, 2, 3, 4, 5, 6
 
 
 @dataclass(frozen=True)
@@ -183,3 +183,30 @@ def make_linear(spec: LinearSpec | str, M: int | None = None) -> dict:
     if M is not None:
         spec = spec.with_m(M)
     return {"spec": spec, "x": make_x(spec), "w": make_w(spec), "bias": make_bias(spec)}
+
+
+def make_rope_tables(M: int, head_dim: int = 128, n_text: int = 512, grid_w: int = 64,
+                     axes=(16, 56, 56), theta: float = 10000.0):
+    """Per-token rotary tables cos, sin (fp32 [M, head_dim/2]) of a FLUX-like
+    DiT: the first n_text tokens (text) sit at position (0, 0, 0), image token t
+    at (0, t // grid_w, t % grid_w); the head's channel pairs are split over the
+    three position axes (16 + 56 + 56 = 128 channels), pair i of an axis of
+    d channels turning at pos * theta^(-2i/d).  Positions and frequencies are
+    inputs of the rotary step, not part of it."""
+    assert sum(axes) == head_dim
+    t = np.arange(M)
+    img = np.maximum(t - n_text, 0)
+    pos = np.stack([np.zeros(M), np.where(t < n_text, 0, img // grid_w),
+                    np.where(t < n_text, 0, img % grid_w)], axis=1).astype(np.float64)
+    ang = []
+    for a, d in enumerate(axes):
+        freq = theta ** (-np.arange(0, d, 2, dtype=np.float64) / d)
+        ang.append(pos[:, a:a + 1] * freq[None, :])
+    ang = np.concatenate(ang, axis=1)
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def make_norm_weight(spec: LinearSpec, which: int, head_dim: int = 128) -> np.ndarray:
+    """Learned RMSNorm scale of Q (which=0) or K (which=1): 1 + 0.1 N(0,1), bf16 bits."""
+    g = np.random.default_rng(np.random.SeedSequence([spec.config_id, spec.layer_id, _T_NORM, which]))
+    return to_bf16_bits(1.0 + 0.1 * g.standard_normal(head_dim))

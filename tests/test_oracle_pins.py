@@ -545,3 +545,82 @@ def test_pair_up_rows_carry_outliers():
     ratio = np.abs(w).max(axis=1) / np.abs(w0).max(axis=1)
     big = np.flatnonzero(np.abs(ratio - 30.0) < 0.5)
     assert big.size == 3 and np.all(np.abs(ratio[np.setdiff1d(np.arange(300), big)] - 1.0) < 1e-6)
+
+
+def test_rms_norm_heads_closed_forms():
+    """With unit scales each head row of the output has mean square ms/(ms+eps)
+    (exactly 1 for eps = 0) and the direction of the input; a positive factor on
+    the input cancels when eps = 0; the scale multiplies channel-wise."""
+    rng = np.random.default_rng(5)
+    y = rng.standard_normal((7, 3 * 16)) * rng.uniform(0.1, 10, size=(7, 1))
+    ones = O.f64_to_bf16(np.ones(16))
+    for eps in (0.0, 1e-6, 0.5):
+        z = O.rms_norm_heads(y, 16, ones, eps).reshape(7, 3, 16)
+        h = y.reshape(7, 3, 16)
+        ms = (h * h).mean(-1)
+        assert np.allclose((z * z).mean(-1), ms / (ms + eps), rtol=1e-12, atol=0)
+        cosang = (z * h).sum(-1) / np.linalg.norm(z, axis=-1) / np.linalg.norm(h, axis=-1)
+        assert np.allclose(cosang, 1.0, rtol=0, atol=1e-12)
+    assert np.allclose(O.rms_norm_heads(37.5 * y, 16, ones, 0.0), O.rms_norm_heads(y, 16, ones, 0.0),
+                       rtol=1e-12, atol=1e-14)
+    w = O.f64_to_bf16(rng.uniform(0.5, 2, 16))
+    ratio = O.rms_norm_heads(y, 16, w, 1e-6) / O.rms_norm_heads(y, 16, ones, 1e-6)
+    assert np.allclose(ratio, np.tile(O.bf16_to_f64(w), 3)[None, :], rtol=1e-12)
+
+
+def test_rope_pairs_rotation_properties():
+    """Each channel pair is turned by its angle: zero angle is the identity, a
+    quarter turn maps (a, b) to (-b, a), pair norms are kept, and turns compose:
+    <R(t1) q, R(t2) k> = <R(t1 - t2) q, k> per pair (the relative-position
+    property of the rotary embedding)."""
+    rng = np.random.default_rng(6)
+    m, hd = 5, 8
+    q, k = rng.standard_normal((m, 2 * hd)), rng.standard_normal((m, 2 * hd))
+    zero = np.zeros((m, hd // 2))
+    assert np.array_equal(O.rope_pairs(q, hd, np.cos(zero), np.sin(zero)), q)
+    quarter = O.rope_pairs(q, hd, np.zeros((m, hd // 2)), np.ones((m, hd // 2)))
+    qp = q.reshape(m, 2, hd // 2, 2)
+    assert np.array_equal(quarter.reshape(m, 2, hd // 2, 2), np.stack([-qp[..., 1], qp[..., 0]], -1))
+    t1, t2 = rng.uniform(-7, 7, (m, hd // 2)), rng.uniform(-7, 7, (m, hd // 2))
+    r1 = O.rope_pairs(q, hd, np.cos(t1), np.sin(t1)).reshape(m, 2, hd // 2, 2)
+    r2 = O.rope_pairs(k, hd, np.cos(t2), np.sin(t2)).reshape(m, 2, hd // 2, 2)
+    assert np.allclose(np.linalg.norm(r1, axis=-1), np.linalg.norm(qp, axis=-1), rtol=1e-13)
+    d = O.rope_pairs(q, hd, np.cos(t1 - t2), np.sin(t1 - t2)).reshape(m, 2, hd // 2, 2)
+    kp = k.reshape(m, 2, hd // 2, 2)
+    assert np.allclose((r1 * r2).sum(-1), (d * kp).sum(-1), rtol=1e-10, atol=1e-12)
+
+
+def test_qkv_output_composition():
+    """qkv_output is call 2's Y* followed by the per-third epilogue: the V third
+    is Y* itself (bit for bit after rounding), Q and K are norm-then-rotate of
+    their thirds with their own scales; rows select token rows and table rows."""
+    spec = S.LinearSpec("qkvpin", 9, 24, 128, 3 * 32, 16, outlier_channels=2, outlier_scale=20.0)
+    d = S.make_linear(spec)
+    lam = O.smooth_factors(O.activation_absmax(d["x"]), d["w"])
+    pk = O.pack_weights(d["w"], lam, 16)
+    a = O.quantize_act_lora_down(d["x"], lam, pk["lora_down"])
+    cos, sin = S.make_rope_tables(24, 16, n_text=4, grid_w=4, axes=(4, 6, 6))
+    qn, kn = S.make_norm_weight(spec, 0, 16), S.make_norm_weight(spec, 1, 16)
+    args = (a["act_codes"], a["act_scales"], pk["w_codes"], pk["w_scales"], a["lora_act"], pk["lora_up"],
+            d["bias"])
+    y, yb = O.linear_output(*args)
+    out, ob = O.qkv_output(*args, 16, qn, kn, 1e-6, cos, sin)
+    assert np.array_equal(ob[:, 64:], yb[:, 64:])
+    assert np.allclose(out[:, :32], O.rope_pairs(O.rms_norm_heads(y[:, :32], 16, qn, 1e-6), 16, cos, sin),
+                       rtol=0, atol=0)
+    assert np.allclose(out[:, 32:64], O.rope_pairs(O.rms_norm_heads(y[:, 32:64], 16, kn, 1e-6), 16, cos, sin),
+                       rtol=0, atol=0)
+    rows = [3, 0, 23]
+    sub, subb = O.qkv_output(*args, 16, qn, kn, 1e-6, cos, sin, rows=rows)
+    assert np.array_equal(subb, ob[rows])
+
+
+def test_rope_tables_positions():
+    """Text tokens get zero angles; image token t turns its height-axis pairs by
+    t // grid_w and its width-axis pairs by t % grid_w times the pair frequency."""
+    cos, sin = S.make_rope_tables(10, 16, n_text=2, grid_w=3, axes=(4, 6, 6))
+    assert np.all(cos[:2] == 1) and np.all(sin[:2] == 0) and np.all(cos[:, :2] == 1)
+    t = 2 + 7   # image token 7: row 2, col 1
+    f6 = 10000.0 ** (-np.arange(0, 6, 2) / 6)
+    assert np.allclose(np.arctan2(sin[t, 2:5], cos[t, 2:5]), np.angle(np.exp(1j * 2 * f6)), atol=1e-6)
+    assert np.allclose(np.arctan2(sin[t, 5:8], cos[t, 5:8]), np.angle(np.exp(1j * 1 * f6)), atol=1e-6)

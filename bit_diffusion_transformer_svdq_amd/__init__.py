@@ -22,7 +22,7 @@ import numpy as np
 from ._lib import SvdqError, check, lib
 
 __all__ = ["SvdqError", "lib", "check_device", "quantize_act_lora_down", "w4a4_gemm_lora_up",
-           "mlp_pair", "w4a4_group_acc_debug", "debug_set_quant_plan", "debug_set_gemm_path",
+           "mlp_pair", "w4a4_gemm_qkv_norm_rope", "w4a4_group_acc_debug", "debug_set_quant_plan", "debug_set_gemm_path",
            "EPILOGUES", "smooth_from_absmax", "pack_weights", "GROUP_SIZE"]
 
 GROUP_SIZE = 64
@@ -127,6 +127,41 @@ def w4a4_gemm_lora_up(act_codes, act_scales, w_codes, w_scales, lora_act=None, l
         _ptr(lora_act) if r else None, _ptr(lora_up) if r else None, _ptr(bias),
         M, N, K, r, GROUP_SIZE, EPILOGUES[epilogue], _ptr(y), _stream(stream))
     check(st, "svdq_w4a4_gemm_lora_up_ex")
+    return y
+
+
+def w4a4_gemm_qkv_norm_rope(act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,
+                            q_norm, k_norm, rope_cos, rope_sin, eps=1e-6, head_dim=128, out=None,
+                            stream=None):
+    """Call 2 with the fused QKV epilogue -> bf16 [M, N] = [Q | K | V]: per-head
+    RMSNorm (scales q_norm / k_norm, bf16 [head_dim]) and the rotary turn of
+    adjacent channel pairs (rope_cos / rope_sin fp32 [M, head_dim/2]) on Q and
+    K; V as in call 2."""
+    torch = _torch()
+    M = act_codes.shape[0]
+    K = act_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    r = 0 if lora_up is None else lora_up.shape[1]
+    _need(act_codes, torch.uint8, (M, K // 2), "act_codes")
+    _need(act_scales, torch.bfloat16, (M, K // GROUP_SIZE), "act_scales")
+    _need(w_codes, torch.uint8, (N, K // 2), "w_codes")
+    _need(w_scales, torch.bfloat16, (N, K // GROUP_SIZE), "w_scales")
+    if r:
+        _need(lora_act, torch.bfloat16, (M, r), "lora_act")
+        _need(lora_up, torch.bfloat16, (N, r), "lora_up")
+    if bias is not None:
+        _need(bias, torch.bfloat16, (N,), "bias")
+    _need(q_norm, torch.bfloat16, (head_dim,), "q_norm")
+    _need(k_norm, torch.bfloat16, (head_dim,), "k_norm")
+    _need(rope_cos, torch.float32, (M, head_dim // 2), "rope_cos")
+    _need(rope_sin, torch.float32, (M, head_dim // 2), "rope_sin")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=act_codes.device) if out is None else out
+    st = lib().svdq_w4a4_gemm_qkv_norm_rope(
+        _ptr(act_codes), _ptr(act_scales), _ptr(w_codes), _ptr(w_scales),
+        _ptr(lora_act) if r else None, _ptr(lora_up) if r else None, _ptr(bias),
+        M, N, K, r, GROUP_SIZE, int(head_dim), _ptr(q_norm), _ptr(k_norm), float(eps),
+        _ptr(rope_cos), _ptr(rope_sin), _ptr(y), _stream(stream))
+    check(st, "svdq_w4a4_gemm_qkv_norm_rope")
     return y
 
 

@@ -35,6 +35,10 @@ SIGNATURES = {
     "svdq_w4a4_gemm_lora_up_ex": (ctypes.c_int, [
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
         _i64, _i64, _i64, _i64, _i64, ctypes.c_int, _c_void_p, _c_void_p]),
+    "svdq_w4a4_gemm_qkv_norm_rope": (ctypes.c_int, [
+        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+        _i64, _i64, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p, ctypes.c_float,
+        _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "svdq_w4a4_group_acc_debug": (ctypes.c_int, [
         _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p]),
     "svdq_smooth_from_absmax": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p]),

@@ -7,6 +7,7 @@
 // Diffusionsmodellen durch Nunchaku 4-Bit-Quantisierung", section
 // "Hardware-Unterstützung"): unsupported GPU generations are refused.
 
+#include <cmath>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -174,6 +175,29 @@ static svdq_status validate_gemm(const void* act_codes, const void* w_codes, int
   return SVDQ_STATUS_SUCCESS;
 }
 
+// pointer checks and launch shared by the call-2 entry points (dims validated)
+static svdq_status gemm_launch(const void* act_codes, const void* act_scales, const void* w_codes,
+                               const void* w_scales, const void* lora_act, const void* lora_up,
+                               const void* bias, int64_t M, int64_t N, int64_t K, int64_t r,
+                               int epilogue, const svdq::QkvEpilogue* qkv, void* y, void* stream) {
+  if (!act_scales || !w_scales || !y) return fail(SVDQ_STATUS_INVALID_VALUE, "null act_scales/w_scales/y");
+  if (r > 0 && (!lora_act || !lora_up))
+    return fail(SVDQ_STATUS_INVALID_VALUE, "r=%lld needs lora_act and lora_up", (long long)r);
+  if (!aligned16(act_scales) || !aligned16(w_scales) || !aligned16(y) ||
+      (bias && !aligned16(bias)) || (r > 0 && (!aligned16(lora_act) || !aligned16(lora_up))))
+    return fail(SVDQ_STATUS_INVALID_VALUE, "device pointers must be 16-byte aligned");
+  svdq_status s = check_current_device();
+  if (s != SVDQ_STATUS_SUCCESS) return s;
+  hipError_t e = svdq::launch_w4a4_gemm_lora_up(
+      static_cast<const uint8_t*>(act_codes), static_cast<const uint16_t*>(act_scales),
+      static_cast<const uint8_t*>(w_codes), static_cast<const uint16_t*>(w_scales),
+      static_cast<const uint16_t*>(lora_act), static_cast<const uint16_t*>(lora_up),
+      static_cast<const uint16_t*>(bias), M, N, K, r, epilogue, qkv, static_cast<uint16_t*>(y),
+      nullptr, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SVDQ_STATUS_HIP_ERROR, "gemm launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 svdq_status svdq_w4a4_gemm_lora_up_ex(const void* act_codes, const void* act_scales,
                                       const void* w_codes, const void* w_scales,
                                       const void* lora_act, const void* lora_up, const void* bias,
@@ -184,22 +208,32 @@ svdq_status svdq_w4a4_gemm_lora_up_ex(const void* act_codes, const void* act_sca
   if (epilogue != SVDQ_EPILOGUE_NONE && epilogue != SVDQ_EPILOGUE_GELU_TANH)
     return fail(SVDQ_STATUS_INVALID_VALUE, "unknown epilogue %d", epilogue);
   if (M == 0) return ok();
-  if (!act_scales || !w_scales || !y) return fail(SVDQ_STATUS_INVALID_VALUE, "null act_scales/w_scales/y");
-  if (r > 0 && (!lora_act || !lora_up))
-    return fail(SVDQ_STATUS_INVALID_VALUE, "r=%lld needs lora_act and lora_up", (long long)r);
-  if (!aligned16(act_scales) || !aligned16(w_scales) || !aligned16(y) ||
-      (bias && !aligned16(bias)) || (r > 0 && (!aligned16(lora_act) || !aligned16(lora_up))))
-    return fail(SVDQ_STATUS_INVALID_VALUE, "device pointers must be 16-byte aligned");
-  s = check_current_device();
+  return gemm_launch(act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, r,
+                     epilogue, nullptr, y, stream);
+}
+
+svdq_status svdq_w4a4_gemm_qkv_norm_rope(const void* act_codes, const void* act_scales,
+                                         const void* w_codes, const void* w_scales,
+                                         const void* lora_act, const void* lora_up, const void* bias,
+                                         int64_t M, int64_t N, int64_t K, int64_t r,
+                                         int64_t group_size, int64_t head_dim, const void* q_norm,
+                                         const void* k_norm, float eps, const float* rope_cos,
+                                         const float* rope_sin, void* y, void* stream) {
+  svdq_status s = validate_gemm(act_codes, w_codes, M, N, K, r, group_size);
   if (s != SVDQ_STATUS_SUCCESS) return s;
-  hipError_t e = svdq::launch_w4a4_gemm_lora_up(
-      static_cast<const uint8_t*>(act_codes), static_cast<const uint16_t*>(act_scales),
-      static_cast<const uint8_t*>(w_codes), static_cast<const uint16_t*>(w_scales),
-      static_cast<const uint16_t*>(lora_act), static_cast<const uint16_t*>(lora_up),
-      static_cast<const uint16_t*>(bias), M, N, K, r, epilogue, static_cast<uint16_t*>(y), nullptr,
-      static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(SVDQ_STATUS_HIP_ERROR, "gemm launch: %s", hipGetErrorString(e));
-  return ok();
+  if (head_dim != 128) return fail(SVDQ_STATUS_NOT_SUPPORTED, "head_dim %lld (only 128)", (long long)head_dim);
+  if (N % (3 * head_dim) != 0)
+    return fail(SVDQ_STATUS_NOT_SUPPORTED, "N=%lld is not 3 x a multiple of head_dim", (long long)N);
+  if (!std::isfinite(eps) || eps < 0.0f) return fail(SVDQ_STATUS_INVALID_VALUE, "eps must be finite and >= 0");
+  if (M == 0) return ok();
+  if (!q_norm || !k_norm || !rope_cos || !rope_sin)
+    return fail(SVDQ_STATUS_INVALID_VALUE, "null q_norm/k_norm/rope_cos/rope_sin");
+  if (!aligned16(q_norm) || !aligned16(k_norm) || !aligned16(rope_cos) || !aligned16(rope_sin))
+    return fail(SVDQ_STATUS_INVALID_VALUE, "device pointers must be 16-byte aligned");
+  const svdq::QkvEpilogue qkv{static_cast<const uint16_t*>(q_norm), static_cast<const uint16_t*>(k_norm),
+                              rope_cos, rope_sin, eps};
+  return gemm_launch(act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, r,
+                     svdq::kEpilogueQkv, &qkv, y, stream);
 }
 
 svdq_status svdq_w4a4_gemm_lora_up(const void* act_codes, const void* act_scales,
@@ -223,7 +257,7 @@ svdq_status svdq_w4a4_group_acc_debug(const void* act_codes, const void* w_codes
   if (s != SVDQ_STATUS_SUCCESS) return s;
   hipError_t e = svdq::launch_w4a4_gemm_lora_up(
       static_cast<const uint8_t*>(act_codes), nullptr, static_cast<const uint8_t*>(w_codes), nullptr,
-      nullptr, nullptr, nullptr, M, N, K, 0, SVDQ_EPILOGUE_NONE, nullptr, acc,
+      nullptr, nullptr, nullptr, M, N, K, 0, SVDQ_EPILOGUE_NONE, nullptr, nullptr, acc,
       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SVDQ_STATUS_HIP_ERROR, "gemm debug launch: %s", hipGetErrorString(e));
   return ok();

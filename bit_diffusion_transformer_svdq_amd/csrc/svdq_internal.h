@@ -19,6 +19,23 @@ __device__ __forceinline__ float gelu_tanh(float x) {
   return x - __fdividef(x, e + 1.0f);
 }
 
+// Epilogue codes of call 2 (values of the C ABI's svdq_epilogue, plus the
+// fused QKV epilogue of svdq_w4a4_gemm_qkv_norm_rope).
+constexpr int kEpilogueNone = 0;
+constexpr int kEpilogueGelu = 1;
+constexpr int kEpilogueQkv = 2;
+
+// Operands of the fused QKV epilogue: Y = [Q | K | V] along N, heads of 128
+// channels; per-head RMSNorm with learned scales on Q and K, then the rotary
+// turn of each adjacent channel pair by the token's angle.
+struct QkvEpilogue {
+  const uint16_t* q_norm;  // bf16 [128]
+  const uint16_t* k_norm;  // bf16 [128]
+  const float* cos;        // fp32 [M, 64]
+  const float* sin;        // fp32 [M, 64]
+  float eps;
+};
+
 // Call 1: smoothing + int4 group quantization + packing + fused lora_down.
 // Shapes are validated by the caller: M > 0, K % 64 == 0, r % 16 == 0, r <= 128.
 hipError_t launch_quant_lora_down(const uint16_t* x, const float* lam, const uint16_t* lora_down,
@@ -35,12 +52,15 @@ void set_quant_plan_override(int k_blocks, int tiles_per_wg);
 // instead of Y (scales, lora and bias are then ignored).
 // Shapes are validated by the caller: M > 0, N % 64 == 0, K % 64 == 0,
 // r % 16 == 0, r <= 128.
+// `qkv` is read only for epilogue == kEpilogueQkv (then N % 384 == 0), which
+// always runs on the tiled kernel.
 hipError_t launch_w4a4_gemm_lora_up(const uint8_t* act_codes, const uint16_t* act_scales,
                                     const uint8_t* w_codes, const uint16_t* w_scales,
                                     const uint16_t* lora_act, const uint16_t* lora_up,
                                     const uint16_t* bias,
                                     int64_t M, int64_t N, int64_t K, int64_t r, int epilogue,
-                                    uint16_t* y, int32_t* acc_dump, hipStream_t stream);
+                                    const QkvEpilogue* qkv, uint16_t* y, int32_t* acc_dump,
+                                    hipStream_t stream);
 
 // Call 2 for few tokens: K split over the waves of a workgroup, weights
 // streamed once.  Same arguments and results as launch_w4a4_gemm_lora_up.

@@ -130,7 +130,8 @@ struct GemmArgs {
   uint16_t* y;
   int32_t* acc;
   int M, N, K, r;
-  int epilogue;  // 0: none, 1: GELU (tanh form) after the bias
+  int epilogue;  // kEpilogueNone, kEpilogueGelu (after the bias) or kEpilogueQkv
+  QkvEpilogue qkv;
 };
 
 // Workgroup id -> (tile_m, tile_n).  Workgroups are dispatched round-robin over
@@ -444,6 +445,85 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
           for (int j = 0; j < 4; ++j) y[i][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fu[i], fa[j], y[i][j], 0, 0, 0);
       }
     }
+    // Fused QKV epilogue on a Q or K tile.  The 128 columns of the tile are one
+    // head (tiles and thirds are 128-aligned), held by the two waves of a wave
+    // row: sum of squares per token over the lane's 16 channels, then over the
+    // 4 lanes of the token (lane xor 16, 32), then over the two waves through
+    // the free scale area; then scale, learned weight and the pair rotation.
+    const int third = (p.epilogue == kEpilogueQkv) ? n0 / (N / 3) : 2;  // workgroup-uniform
+    if (p.epilogue == kEpilogueQkv && third < 2) {
+      const uint16_t* nw = third == 0 ? p.qkv.q_norm : p.qkv.k_norm;
+      float wgt[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + wn * 64 + 16 * i + 4 * lseg;
+        const int nl = wn * 64 + 16 * i + 4 * lseg;
+        float bb4[4] = {0.f, 0.f, 0.f, 0.f};
+        if (p.bias != nullptr) {
+          const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n);
+          bb4[0] = __builtin_bit_cast(float, bb.x << 16);
+          bb4[1] = __builtin_bit_cast(float, bb.x & 0xFFFF0000u);
+          bb4[2] = __builtin_bit_cast(float, bb.y << 16);
+          bb4[3] = __builtin_bit_cast(float, bb.y & 0xFFFF0000u);
+        }
+        const uint2 ww = *reinterpret_cast<const uint2*>(nw + nl);
+        wgt[i][0] = __builtin_bit_cast(float, ww.x << 16);
+        wgt[i][1] = __builtin_bit_cast(float, ww.x & 0xFFFF0000u);
+        wgt[i][2] = __builtin_bit_cast(float, ww.y << 16);
+        wgt[i][3] = __builtin_bit_cast(float, ww.y & 0xFFFF0000u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) y[i][j][v] += bb4[v];
+      }
+      float ss[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) a = fmaf(y[i][j][v], y[i][j][v], a);
+        a += __shfl_xor(a, 16);
+        a += __shfl_xor(a, 32);
+        ss[j] = a;
+      }
+      float* red = s0;  // the scale areas are free once every wave has left the loop
+      barrier();
+      if (lseg == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red[wn * 128 + wm * 64 + 16 * j + l16] = ss[j];
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+      barrier();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float tot = ss[j] + red[(1 - wn) * 128 + wm * 64 + 16 * j + l16];
+        ss[j] = 1.0f / sqrtf(tot * (1.0f / 128.0f) + p.qkv.eps);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + wn * 64 + 16 * i + 4 * lseg;
+        const int pair = (wn * 64 + 16 * i + 4 * lseg) >> 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int m = m0 + wm * 64 + 16 * j + l16;
+          const size_t t = (size_t)min(m, M - 1) * 64 + pair;
+          const float2 c = *reinterpret_cast<const float2*>(p.qkv.cos + t);
+          const float2 sn = *reinterpret_cast<const float2*>(p.qkv.sin + t);
+          float z[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) z[v] = y[i][j][v] * ss[j] * wgt[i][v];
+          if (m < M) {
+            uint2 o;
+            o.x = pack_bf16(z[0] * c.x - z[1] * sn.x, z[0] * sn.x + z[1] * c.x);
+            o.y = pack_bf16(z[2] * c.y - z[3] * sn.y, z[2] * sn.y + z[3] * c.y);
+            *reinterpret_cast<uint2*>(p.y + (size_t)m * N + n) = o;
+          }
+        }
+      }
+      return;
+    }
     // bias and store: lane owns Y[m, n .. n+3]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -463,7 +543,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
           float o4[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) o4[v] = y[i][j][v] + bb4[v];
-          if (p.epilogue == 1) {
+          if (p.epilogue == kEpilogueGelu) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) o4[v] = gelu_tanh(o4[v]);
           }
@@ -522,12 +602,13 @@ hipError_t launch_w4a4_gemm_lora_up(const uint8_t* act_codes, const uint16_t* ac
                                     const uint8_t* w_codes, const uint16_t* w_scales,
                                     const uint16_t* lora_act, const uint16_t* lora_up,
                                     const uint16_t* bias, int64_t M, int64_t N, int64_t K,
-                                    int64_t r, int epilogue, uint16_t* y, int32_t* acc_dump,
-                                    hipStream_t stream) {
+                                    int64_t r, int epilogue, const QkvEpilogue* qkv, uint16_t* y,
+                                    int32_t* acc_dump, hipStream_t stream) {
   // Few tokens: the 128 x 128 tile grid leaves most CUs idle; the K-split
   // kernel streams the weights with every CU instead.
   const int path = g_path.load(std::memory_order_relaxed);
-  if (path != 1 && skinny_supported(M, N, K) && (path == 2 || M <= kSkinnyMaxM))
+  if (epilogue != kEpilogueQkv && path != 1 && skinny_supported(M, N, K) &&
+      (path == 2 || M <= kSkinnyMaxM))
     return launch_w4a4_gemm_skinny(act_codes, act_scales, w_codes, w_scales, lora_act, lora_up,
                                    bias, M, N, K, r, epilogue, y, acc_dump, stream);
   if (acc_dump != nullptr) {
@@ -536,7 +617,11 @@ hipError_t launch_w4a4_gemm_lora_up(const uint8_t* act_codes, const uint16_t* ac
     return launch<true>(a, stream);
   }
   GemmArgs<false> a{act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,
-                    y, nullptr, (int)M, (int)N, (int)K, (int)r, epilogue};
+                    y, nullptr, (int)M, (int)N, (int)K, (int)r, epilogue, QkvEpilogue{}};
+  if (epilogue == kEpilogueQkv) {
+    if (qkv == nullptr || N % 384 != 0) return hipErrorInvalidValue;
+    a.qkv = *qkv;
+  }
   return launch<false>(a, stream);
 }
 

@@ -201,6 +201,39 @@ svdq_status svdq_w4a4_gemm_lora_up_ex(
     int epilogue, void* y, void* stream);
 
 /*
+ * Call 2 with the fused QKV epilogue of a diffusion transformer's attention:
+ * for FLUX.1-dev the Q, K and V projections are one quantized to_qkv linear
+ * whose fused operator also does the Q/K normalization and the rotary
+ * embeddings (mind-verse.de, "Effiziente Optimierung von Diffusionsmodellen
+ * durch Nunchaku 4-Bit-Quantisierung", section "Quantisierung von Modellen mit
+ * strukturellen Umschreibungen").  With v = Y*[m, :] + b (Y* as in call 2) and
+ * Y = [Q | K | V] along N (thirds of N/3 columns, heads of head_dim channels):
+ *   Q, K heads:  z = v_h / sqrt(mean(v_h^2) + eps) * w     (RMSNorm, per head;
+ *                w = q_norm for Q, k_norm for K)
+ *                (z[2i], z[2i+1]) -> (z[2i] c - z[2i+1] s, z[2i] s + z[2i+1] c)
+ *                with c = rope_cos[m, i], s = rope_sin[m, i] (RoFormer rotation
+ *                of adjacent channel pairs, the same angles for every head)
+ *   V:           v
+ * all in fp32 from the unrounded v, rounded to bf16 once.
+ *
+ *   head_dim   == 128; N must be a multiple of 3 * head_dim
+ *   q_norm, k_norm   device, bf16 [head_dim]
+ *   eps        finite, >= 0 (FLUX uses 1e-6)
+ *   rope_cos, rope_sin   device, fp32 [M, head_dim/2]
+ *   y          device out, bf16 [M, N]
+ * Other arguments, errors and the M == 0 rule as for svdq_w4a4_gemm_lora_up;
+ * NOT_SUPPORTED for another head_dim or N, INVALID_VALUE for a bad eps or a
+ * null or misaligned table.  Runs on the tiled kernel for every M.
+ */
+svdq_status svdq_w4a4_gemm_qkv_norm_rope(
+    const void* act_codes, const void* act_scales,
+    const void* w_codes, const void* w_scales,
+    const void* lora_act, const void* lora_up, const void* bias,
+    int64_t M, int64_t N, int64_t K, int64_t r, int64_t group_size,
+    int64_t head_dim, const void* q_norm, const void* k_norm, float eps,
+    const float* rope_cos, const float* rope_sin, void* y, void* stream);
+
+/*
  * Test hook for call 2: runs the same main loop as svdq_w4a4_gemm_lora_up and
  * writes the int32 group accumulators acc_g[m,n] (the exact integer sums
  * sum_{k in g} q_x q_w, with any internal scaling removed) instead of Y.

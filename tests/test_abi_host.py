@@ -137,6 +137,25 @@ def test_gemm_epilogue_argument():
             assert ex(good) == NO_DEVICE
 
 
+def test_qkv_entry_point_argument_errors():
+    L = lib()
+
+    def qkv(M=64, N=768, head_dim=128, eps=1e-6, qn=FAKE, cos=FAKE):
+        return L.svdq_w4a4_gemm_qkv_norm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, M, N, 256, 16, 64,
+                                              head_dim, qn, FAKE, eps, cos, FAKE, FAKE, None)
+    assert qkv(head_dim=64) == NOT_SUPPORTED
+    assert qkv(N=512) == NOT_SUPPORTED
+    assert qkv(N=96) == NOT_SUPPORTED
+    assert qkv(eps=float("nan")) == INVALID_VALUE
+    assert qkv(eps=-1.0) == INVALID_VALUE
+    assert qkv(qn=None) == INVALID_VALUE
+    assert qkv(cos=FAKE_ODD) == INVALID_VALUE
+    assert qkv(M=0, qn=None, cos=None) == SUCCESS
+    assert qkv(M=0, N=512) == NOT_SUPPORTED
+    if not _gpu_visible():
+        assert qkv() == NO_DEVICE
+
+
 def test_debug_hook_argument_errors():
     L = lib()
     assert L.svdq_w4a4_group_acc_debug(FAKE, FAKE, 4, 64, 64, 64, None, None) == INVALID_VALUE

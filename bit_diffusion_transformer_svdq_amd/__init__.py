@@ -22,7 +22,7 @@ import numpy as np
 from ._lib import SvdqError, check, lib
 
 __all__ = ["SvdqError", "lib", "check_device", "quantize_act_lora_down", "w4a4_gemm_lora_up",
-           "mlp_pair", "w4a4_gemm_qkv_norm_rope", "w4a4_group_acc_debug", "debug_set_quant_plan", "debug_set_gemm_path",
+           "mlp_pair", "w4a4_gemm_qkv_norm_rope", "w4a4_group_acc_debug", "debug_set_quant_plan", "debug_set_gemm_path", "debug_set_gemm_splits",
            "EPILOGUES", "smooth_from_absmax", "pack_weights", "GROUP_SIZE"]
 
 GROUP_SIZE = 64
@@ -96,6 +96,11 @@ def debug_set_quant_plan(k_blocks: int = 0, tiles_per_wg: int = 0) -> None:
 def debug_set_gemm_path(path: int = 0) -> None:
     """Test hook: 0 = kernel chosen by shape, 1 = tiled kernel, 2 = K-split (few-token) kernel."""
     check(lib().svdq_debug_set_gemm_path(int(path)), "svdq_debug_set_gemm_path")
+
+
+def debug_set_gemm_splits(splits: int = 0) -> None:
+    """Test hook: K-splits per tile of the tiled kernel (0 = chosen by shape)."""
+    check(lib().svdq_debug_set_gemm_splits(int(splits)), "svdq_debug_set_gemm_splits")
 
 
 EPILOGUES = {"none": 0, "gelu_tanh": 1}

@@ -29,6 +29,7 @@ SIGNATURES = {
         _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "svdq_debug_set_quant_plan": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     "svdq_debug_set_gemm_path": (ctypes.c_int, [ctypes.c_int]),
+    "svdq_debug_set_gemm_splits": (ctypes.c_int, [ctypes.c_int]),
     "svdq_w4a4_gemm_lora_up": (ctypes.c_int, [
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
         _i64, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p]),

@@ -63,10 +63,11 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
             cmd[2] = "-save-temps=obj"
         _run(cmd, verbose)
         objs.append(obj)
-    api_obj = os.path.join(BUILD_DIR, "api.o")
-    _run([hipcc, "-c", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC,
-          os.path.join(CSRC, "api.cpp"), "-o", api_obj], verbose)
-    objs.append(api_obj)
+    for host_src in ("api.cpp", "workspace.cpp"):
+        obj = os.path.join(BUILD_DIR, host_src.replace(".cpp", ".o"))
+        _run([hipcc, "-c", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC,
+              os.path.join(CSRC, host_src), "-o", obj], verbose)
+        objs.append(obj)
     packer_obj = os.path.join(BUILD_DIR, "packer.o")
     _run(["g++", "-c", "-O3", "-march=x86-64-v3", "-std=c++17", "-fPIC", "-Wall", "-fno-fast-math",
           "-ffp-contract=off", "-I", INCLUDE, os.path.join(CSRC, "packer.cpp"), "-o", packer_obj], verbose)

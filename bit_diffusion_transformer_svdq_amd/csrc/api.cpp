@@ -156,6 +156,12 @@ svdq_status svdq_debug_set_gemm_path(int path) {
   return ok();
 }
 
+svdq_status svdq_debug_set_gemm_splits(int splits) {
+  if (splits < 0 || splits > 64) return fail(SVDQ_STATUS_INVALID_VALUE, "bad split count %d (0..64)", splits);
+  svdq::set_gemm_splits_override(splits);
+  return ok();
+}
+
 static svdq_status validate_gemm(const void* act_codes, const void* w_codes, int64_t M, int64_t N,
                                  int64_t K, int64_t r, int64_t group_size) {
   if (M < 0 || N <= 0 || K <= 0 || r < 0 || group_size <= 0)

@@ -48,10 +48,7 @@
 #include <stdint.h>
 
 #include <algorithm>
-#include <map>
-#include <vector>
-#include <mutex>
-#include <utility>
+#include <atomic>
 
 #include "svdq_internal.h"
 
@@ -430,23 +427,8 @@ Plan make_plan(int T, int G, int NT, int cus) {
   return best;
 }
 
-int g_force_tb = 0, g_force_kb = 0;  // test hook (0 = automatic)
+std::atomic<int> g_force_tb{0}, g_force_kb{0};  // test hook (0 = automatic)
 
-// Per device and stream: T counters (zero between launches) followed by the
-// partial sums.  Calls on one stream are ordered, so they can share it.  A
-// workspace that is outgrown is kept, not freed: a graph captured earlier on
-// that stream still holds its address, and its counters are still zero
-// whenever no launch that uses them is running.
-struct Workspace {
-  void* ptr = nullptr;
-  size_t count_cap = 0;   // counters known to be zero
-  size_t part_bytes = 0;
-};
-std::mutex g_mu;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
-std::vector<void*> g_retired;  // outgrown workspaces, alive until the process ends
-
-size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 int cu_count(int dev) {
   static int cache[64] = {0};
@@ -477,9 +459,8 @@ hipError_t launch_nt(const QuantArgs& a, const Plan& p, hipStream_t stream) {
 }  // namespace
 
 void set_quant_plan_override(int k_blocks, int tiles_per_wg) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  g_force_kb = std::max(0, k_blocks);
-  g_force_tb = std::max(0, tiles_per_wg);
+  g_force_kb.store(std::max(0, k_blocks));
+  g_force_tb.store(std::max(0, tiles_per_wg));
 }
 
 hipError_t launch_quant_lora_down(const uint16_t* x, const float* lam, const uint16_t* lora_down,
@@ -492,11 +473,11 @@ hipError_t launch_quant_lora_down(const uint16_t* x, const float* lam, const uin
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
 
-  std::lock_guard<std::mutex> lk(g_mu);
   Plan p = make_plan(T, G, NT, cu_count(dev));
-  if (g_force_kb > 0 || g_force_tb > 0) {
-    const int TB = g_force_tb > 0 ? std::min(g_force_tb, kMaxTiles) : p.TB;
-    const int KB0 = g_force_kb > 0 ? std::min(g_force_kb, G) : p.KB;
+  const int force_kb = g_force_kb.load(), force_tb = g_force_tb.load();
+  if (force_kb > 0 || force_tb > 0) {
+    const int TB = force_tb > 0 ? std::min(force_tb, kMaxTiles) : p.TB;
+    const int KB0 = force_kb > 0 ? std::min(force_kb, G) : p.KB;
     const int GB = (G + KB0 - 1) / KB0;
     if (GB <= kMaxGB && lds_bytes(GB, NT) + kMuBytes <= (size_t)kLdsLimit)
       p = Plan{TB, GB, (G + GB - 1) / GB, (T + TB - 1) / TB, lds_bytes(GB, NT)};
@@ -510,29 +491,12 @@ hipError_t launch_quant_lora_down(const uint16_t* x, const float* lam, const uin
   a.GB = p.GB; a.TB = p.TB; a.KB = p.KB;
 
   if (NT > 0 && p.KB > 1) {
+    // T arrival counters and the fp32 partials [KB][T][NT][4][64]
     const size_t part_need = (size_t)p.KB * T * NT * 64 * 16;
-    Workspace& w = g_ws[{dev, stream}];
-    if (w.count_cap < (size_t)T || w.part_bytes < part_need) {
-      // allocating is not allowed while the stream is being captured into a graph
-      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-      e = hipStreamIsCapturing(stream, &cs);
-      if (e != hipSuccess) return e;
-      if (cs != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
-      if (w.ptr) {
-        g_retired.push_back(w.ptr);
-        w = Workspace{};
-      }
-      const size_t cap = std::max<size_t>(T, 64) + T / 4;
-      const size_t pb = part_need + part_need / 4;
-      e = hipMalloc(&w.ptr, round256(cap * 4) + pb);
-      if (e != hipSuccess) { w = Workspace{}; return e; }
-      e = hipMemsetAsync(w.ptr, 0, round256(cap * 4), stream);
-      if (e != hipSuccess) { (void)hipFree(w.ptr); w = Workspace{}; return e; }
-      w.count_cap = cap;
-      w.part_bytes = pb;
-    }
-    a.count = static_cast<u32*>(w.ptr);
-    a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(w.ptr) + round256(w.count_cap * 4));
+    void* part = nullptr;
+    e = stream_workspace(stream, (size_t)T, part_need, &a.count, &part);
+    if (e != hipSuccess) return e;
+    a.part = static_cast<float*>(part);
   }
 
   switch (NT) {

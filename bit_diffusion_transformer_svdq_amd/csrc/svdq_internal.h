@@ -36,6 +36,14 @@ struct QkvEpilogue {
   float eps;
 };
 
+// The library's device scratch for `stream` on the current device: at least
+// `counters` u32 counters, zero between launches (every kernel that uses one
+// leaves it at zero), and at least `bytes` of scratch after them.  Allocates
+// or grows on demand (never while the stream is capturing: then
+// hipErrorStreamCaptureUnsupported); outgrown buffers stay allocated.
+hipError_t stream_workspace(hipStream_t stream, size_t counters, size_t bytes, uint32_t** counter_ptr,
+                            void** scratch_ptr);
+
 // Call 1: smoothing + int4 group quantization + packing + fused lora_down.
 // Shapes are validated by the caller: M > 0, K % 64 == 0, r % 16 == 0, r <= 128.
 hipError_t launch_quant_lora_down(const uint16_t* x, const float* lam, const uint16_t* lora_down,
@@ -75,5 +83,9 @@ hipError_t launch_w4a4_gemm_skinny(const uint8_t* act_codes, const uint16_t* act
 // Test hook: 0 = choose by shape, 1 = always the tiled kernel, 2 = the
 // few-token kernel wherever it is supported.
 void set_gemm_path_override(int path);
+
+// Test hook: K-splits per tile of the tiled kernel (0 = choose by shape;
+// clipped to the number of group pairs; ignored for the QKV epilogue).
+void set_gemm_splits_override(int splits);
 
 }  // namespace svdq

@@ -53,6 +53,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "svdq_internal.h"
@@ -132,6 +133,9 @@ struct GemmArgs {
   int M, N, K, r;
   int epilogue;  // kEpilogueNone, kEpilogueGelu (after the bias) or kEpilogueQkv
   QkvEpilogue qkv;
+  int splits;         // K-splits per tile (gridDim.y); > 1 needs part and count
+  float* part;        // fp32 partial sub-tiles [tiles][splits][4 waves][16][4][64]
+  uint32_t* count;    // arrival counters [tiles][4 waves], zero between launches
 };
 
 // Workgroup id -> (tile_m, tile_n).  Workgroups are dispatched round-robin over
@@ -174,6 +178,11 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
   const int M = p.M, N = p.N, K = p.K, r = p.r;
   const int G = K >> 6;
   const int P = (G + 1) >> 1;  // group pairs
+  // K-split: workgroup (tile, split) runs pairs [qb, qb + Pl) of the tile
+  // (splits == 1: the whole K); pair indices below are local to the split.
+  const int split = blockIdx.y;
+  const int qb = (int)(((long)split * P) / p.splits);
+  const int Pl = (int)(((long)(split + 1) * P) / p.splits) - qb;
   const int KB = K >> 1;       // bytes per packed row
   int tm, tn;
   tile_of(blockIdx.x, (M + kBM - 1) / kBM, (N + kBN - 1) / kBN, tm, tn);
@@ -205,7 +214,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
   auto dma_pair = [&](int q, int buf) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const u32 col = 32u * (u32)min(2 * q + (int)(gsel[k] >> 1), G - 1);
+      const u32 col = 32u * (u32)min(2 * (qb + q) + (int)(gsel[k] >> 1), G - 1);
       dma16(p.w_codes + (woff[k] + col), wtile(buf) + 4096 * k + 1024 * wave);
       dma16(p.act_codes + (aoff[k] + col), atile(buf) + 4096 * k + 1024 * wave);
     }
@@ -228,8 +237,8 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
   u32 slo[3], shi[3];
   auto load_scales = [&](int q, int k) {
     if (kDump) return;
-    slo[k] = sbase[soff + (u32)min(2 * q, G - 1)];
-    shi[k] = sbase[soff + (u32)min(2 * q + 1, G - 1)];
+    slo[k] = sbase[soff + (u32)min(2 * (qb + q), G - 1)];
+    shi[k] = sbase[soff + (u32)min(2 * (qb + q) + 1, G - 1)];
   };
   // converted scales of pair q (ring slot k) -> stage buffer `buf`: per group
   // h, s_x/256 of the token slot (floats 256h + 0..127) or s_w of the weight
@@ -356,20 +365,21 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
   // reads are issued up front, so the second group's land during the first
   // one's compute; under the 3-per-CU register budget each group reads its own.
   auto compute_pair = [&](int buf, int sbuf, int q) {
-    const bool two = 2 * q + 1 < G;
+    const int g0 = 2 * (qb + q);
+    const bool two = g0 + 1 < G;
     if constexpr (kOcc <= 2) {
       GroupRegs d0, d1;
       read_group(d0, buf, sbuf, 0);
       if (two) read_group(d1, buf, sbuf, 1);
-      compute(d0, 2 * q);
-      if (two) compute(d1, 2 * q + 1);
+      compute(d0, g0);
+      if (two) compute(d1, g0 + 1);
     } else {
       GroupRegs d;
       read_group(d, buf, sbuf, 0);
-      compute(d, 2 * q);
+      compute(d, g0);
       if (two) {
         read_group(d, buf, sbuf, 1);
-        compute(d, 2 * q + 1);
+        compute(d, g0 + 1);
       }
     }
   };
@@ -382,7 +392,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
   load_scales(1, 1);
   dma_pair(0, 0);
   load_scales(2, 2);
-  dma_pair(min(1, P - 1), 1);
+  dma_pair(min(1, Pl - 1), 1);
   put_scale(0, 0, 0);
 
   // Iteration q: stage q complete (own loads: vmcnt, everyone's: barrier); the
@@ -391,21 +401,87 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
   // staged into the scale area pair q-1 has freed; pair q is computed.  The
   // body is unrolled over 6 pairs (3 tile stages x 2 scale areas) so every LDS
   // buffer and register-ring index is a compile-time constant.
-  for (int q0 = 0; q0 < P; q0 += 6) {
+  for (int q0 = 0; q0 < Pl; q0 += 6) {
 #pragma unroll
     for (int u = 0; u < 6; ++u) {
       const int q = q0 + u;
       wait_vm<4, true>();
       barrier();
-      load_scales(min(q + 3, P - 1), u % 3);
-      dma_pair(min(q + 2, P - 1), (u + 2) % 3);
+      load_scales(min(q + 3, Pl - 1), u % 3);
+      dma_pair(min(q + 2, Pl - 1), (u + 2) % 3);
       put_scale(q + 1, (u + 1) % 3, (u + 1) % 2);
-      if (q < P) compute_pair(u % 3, u % 2, q);
+      if (q < Pl) compute_pair(u % 3, u % 2, q);
     }
   }
   wait_vm<0, true>();
 
   if constexpr (!kDump) {
+    // K-split: each wave reduces its own 64 x 64 sub-tile.  It stores its fp32
+    // partial with agent-coherent stores (visible across the XCDs' L2s without
+    // a cache-wide write-back), waits for them, and bumps the sub-tile's
+    // counter; the wave that arrives last loads the other partials the same
+    // way, adds all of them in split order (the result does not depend on
+    // timing) and runs the epilogue.  The counter wraps back to zero.
+    if (p.splits > 1) {
+      const size_t sub = (size_t)blockIdx.x * 4 + wave;
+      float* mine = p.part + ((sub * p.splits + split) << 12);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            __hip_atomic_store(mine + (((i * 4 + j) * 4 + v) << 6) + lane, y[i][j][v], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      __asm__ volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the partial is visible to the agent
+      __asm__ volatile("" ::: "memory");
+      u32 old = 0;
+      if (lane == 0) old = atomicInc(p.count + sub, (u32)(p.splits - 1));
+      old = __shfl(old, 0);
+      if (old != (u32)(p.splits - 1)) return;  // another split of this sub-tile is still running
+      __asm__ volatile("" ::: "memory");
+      // two halves of the sub-tile (n tiles i = 2h, 2h + 1); per half, the
+      // partials of two splits are loaded together (64 loads in flight) and
+      // added in split order
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        v4f acc[2][4];
+        for (int s0 = 0; s0 < p.splits; s0 += 2) {
+          v4f t[2][2][4];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int s2 = min(s0 + e, p.splits - 1);
+            const float* src = p.part + ((sub * p.splits + s2) << 12);
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                  t[e][ii][j][v] = __hip_atomic_load(src + ((((2 * h + ii) * 4 + j) * 4 + v) << 6) + lane,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int s2 = s0 + e;
+            if (s2 < p.splits) {
+#pragma unroll
+              for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  const v4f v = (s2 == split) ? y[2 * h + ii][j] : t[e][ii][j];
+                  acc[ii][j] = (s2 == 0) ? v : acc[ii][j] + v;
+                }
+            }
+          }
+        }
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[2 * h + ii][j] = acc[ii][j];
+      }
+    }
     // fused lora_up: Y^T[n, m] += lora_up[n, :] . lora_act[m, :], fragments
     // from the LDS tiles, or else straight from memory (L2), all loads of a
     // 32-wide rank chunk first
@@ -568,16 +644,62 @@ int pick_occupancy(int tiles, int cus) {
   return (r3 * 260 < r2 * 200) ? 3 : 2;
 }
 
+// K-splits per tile.  A launch runs in rounds of 3 workgroups per CU; a last,
+// partial round with r workgroups takes a fraction of a full round that
+// depends on how many share a CU (1: 0.45, 2: 0.8, 3: 1).  A workgroup costs
+// its group pairs plus a fixed overhead (pipeline fill and epilogue, about 2
+// pairs; with splits also the fp32 partial write and the in-order reduction,
+// about 3 + S/2 pairs).  The split count with the least estimated time wins
+// (fitted to measured times on MI355X: few-tile shapes gain up to 2.4x, and
+// 864 tiles with long K gain about 15 % from S = 2).
+int pick_splits(int tiles, int pairs, int cus) {
+  const int slots = 3 * cus;
+  auto est = [&](int S) {
+    const long W = (long)tiles * S;
+    const long full = W / slots;
+    const long rest = W - full * slots;
+    const long load = (rest + cus - 1) / cus;
+    const double part = load == 0 ? 0.0 : load == 1 ? 0.45 : load == 2 ? 0.8 : 1.0;
+    const double over = S == 1 ? 2.0 : 3.0 + 0.5 * S;
+    return ((double)pairs / S + over) * ((double)full + part);
+  };
+  int best = 1;
+  double bt = est(1);
+  for (int S = 2; S <= std::min(pairs, 16); ++S) {
+    const double t = est(S);
+    if (t < bt * 0.97) {  // a split has to win clearly
+      bt = t;
+      best = S;
+    }
+  }
+  return best;
+}
+
+std::atomic<int> g_splits{0};  // test hook (0 = automatic)
+
 template <bool kDump>
-hipError_t launch(const GemmArgs<kDump>& a, hipStream_t stream) {
+hipError_t launch(GemmArgs<kDump> a, hipStream_t stream) {
   const int tiles = ((a.N + kBN - 1) / kBN) * ((a.M + kBM - 1) / kBM);
   auto kern = w4a4_gemm_kernel<kDump, kDump ? 1 : 3>;
   size_t pad = 0;
+  a.splits = 1;
   if constexpr (!kDump) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
       (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (pick_occupancy(tiles, cus) == 2) {
+    const int pairs = (a.K / 64 + 1) / 2;
+    if (a.epilogue != kEpilogueQkv) {
+      const int forced = g_splits.load(std::memory_order_relaxed);
+      a.splits = forced > 0 ? std::min(forced, pairs) : pick_splits(tiles, pairs, cus);
+    }
+    if (a.splits > 1) {
+      void* part = nullptr;
+      hipError_t e = stream_workspace(stream, (size_t)tiles * 4, (size_t)tiles * a.splits * 4 * 4096 * 4,
+                                      &a.count, &part);
+      if (e != hipSuccess) return e;
+      a.part = static_cast<float*>(part);
+    }
+    if (pick_occupancy(tiles * a.splits, cus) == 2) {
       kern = w4a4_gemm_kernel<kDump, 2>;
       // the lora tiles, and at least enough that only 2 workgroups fit a CU
       pad = max((size_t)(80 * 1024 - kStaticLds), (size_t)2 * kBN * a.r * 2);
@@ -586,7 +708,7 @@ hipError_t launch(const GemmArgs<kDump>& a, hipStream_t stream) {
       if (e != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL(kern, dim3(tiles), dim3(kThreads), pad, stream, a);
+  hipLaunchKernelGGL(kern, dim3(tiles, a.splits), dim3(kThreads), pad, stream, a);
   return hipGetLastError();
 }
 
@@ -597,6 +719,8 @@ std::atomic<int> g_path{0};
 }  // namespace
 
 void set_gemm_path_override(int path) { g_path.store(path, std::memory_order_relaxed); }
+
+void set_gemm_splits_override(int splits) { g_splits.store(std::max(0, splits), std::memory_order_relaxed); }
 
 hipError_t launch_w4a4_gemm_lora_up(const uint8_t* act_codes, const uint16_t* act_scales,
                                     const uint8_t* w_codes, const uint16_t* w_scales,
@@ -613,11 +737,13 @@ hipError_t launch_w4a4_gemm_lora_up(const uint8_t* act_codes, const uint16_t* ac
                                    bias, M, N, K, r, epilogue, y, acc_dump, stream);
   if (acc_dump != nullptr) {
     GemmArgs<true> a{act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,
-                     y, acc_dump, (int)M, (int)N, (int)K, 0, 0};
+                     y, acc_dump, (int)M, (int)N, (int)K, 0, kEpilogueNone, QkvEpilogue{}, 1,
+                     nullptr, nullptr};
     return launch<true>(a, stream);
   }
   GemmArgs<false> a{act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,
-                    y, nullptr, (int)M, (int)N, (int)K, (int)r, epilogue, QkvEpilogue{}};
+                    y, nullptr, (int)M, (int)N, (int)K, (int)r, epilogue, QkvEpilogue{}, 1,
+                    nullptr, nullptr};
   if (epilogue == kEpilogueQkv) {
     if (qkv == nullptr || N % 384 != 0) return hipErrorInvalidValue;
     a.qkv = *qkv;

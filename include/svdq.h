@@ -137,12 +137,25 @@ svdq_status svdq_debug_set_quant_plan(int k_blocks, int tiles_per_wg);
 
 /*
  * Test hook for call 2 (and svdq_w4a4_group_acc_debug): 0 chooses the kernel
- * by shape (the K-split kernel for up to 160 tokens, the tiled kernel above),
- * 1 forces the tiled kernel, 2 the K-split kernel wherever it is supported.
- * Both compute the same integers and the same dequantization; Y may differ in
- * fp32 rounding order.  Returns INVALID_VALUE for other values.
+ * by shape (the few-token kernel, whose waves split K, for up to 160 tokens;
+ * the tiled kernel above), 1 forces the tiled kernel, 2 the few-token kernel
+ * wherever it is supported.  Both compute the same integers and the same
+ * dequantization; Y may differ in fp32 rounding order.  Returns INVALID_VALUE
+ * for other values.
  */
 svdq_status svdq_debug_set_gemm_path(int path);
+
+/*
+ * Test hook for call 2's tiled kernel: the number of K-splits per output tile
+ * for every later call in this process (0 = chosen by shape; clipped to the
+ * number of group pairs K/128, rounded up).  With splits > 1 each workgroup
+ * runs a run of whole quant groups of its tile and the fp32 partial tiles are
+ * added in split order through the stream's workspace, so Y may differ from
+ * the unsplit result in fp32 rounding order but not between runs.  Ignored by
+ * the QKV epilogue and the accumulator dump.  Returns INVALID_VALUE outside
+ * 0..64.
+ */
+svdq_status svdq_debug_set_gemm_splits(int splits);
 
 /*
  * Call 2 - W4A4 GEMM with per-group int32 accumulation, per-group
@@ -163,6 +176,11 @@ svdq_status svdq_debug_set_gemm_path(int path);
  *   M >= 0 (0 is a no-op), N > 0 with N % 64 == 0, K > 0 with K % 64 == 0,
  *   r in {0,16,...,128}, group_size == 64
  *   y          device out, bf16 [M, N]
+ * With few output tiles (fewer than two 128 x 128 tiles per compute unit) the
+ * tiled kernel splits K over several workgroups per tile; their fp32 partial
+ * tiles go through the stream's workspace (the one call 1 uses, same rules:
+ * allocated or grown on first need, never during graph capture) and are added
+ * in a fixed order, so Y does not depend on timing.
  */
 svdq_status svdq_w4a4_gemm_lora_up(
     const void* act_codes, const void* act_scales,

@@ -180,6 +180,14 @@ def test_gemm_path_hook_arguments():
         assert L.svdq_debug_set_gemm_path(p) == SUCCESS
 
 
+def test_gemm_splits_hook_arguments():
+    L = lib()
+    assert L.svdq_debug_set_gemm_splits(-1) == INVALID_VALUE
+    assert L.svdq_debug_set_gemm_splits(65) == INVALID_VALUE
+    for v in (3, 64, 0):
+        assert L.svdq_debug_set_gemm_splits(v) == SUCCESS
+
+
 def _gpu_visible():
     try:
         import torch

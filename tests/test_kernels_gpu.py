@@ -362,3 +362,40 @@ def test_headline_group_accumulators_on_a_row_window():
     acc = K.w4a4_group_acc_debug(to_dev(ref["act_codes"]), to_dev(packed["w_codes"])).cpu().numpy()
     want = O.group_accumulators(ref["act_codes"], packed["w_codes"])
     assert np.array_equal(acc, want)
+
+
+# ---- K-split of the tiled kernel ----
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 8])
+@pytest.mark.parametrize("M,K,N,r", [(200, 1024, 192, 32), (300, 3072, 320, 16), (129, 640, 128, 0)])
+def test_forced_gemm_splits(splits, M, K, N, r):
+    """Each split count gives Y within the bar (partials added in split order),
+    the same bits on a second launch, and the same codes."""
+    import bit_diffusion_transformer_svdq_amd as K_
+    d, lam, packed = custom_case(M, K, N, r, seed=11 * M + splits)
+    ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
+    K_.debug_set_gemm_path(1)
+    K_.debug_set_gemm_splits(splits)
+    try:
+        got = _run(d, lam, packed)
+        again = _run(d, lam, packed)
+    finally:
+        K_.debug_set_gemm_splits(0)
+        K_.debug_set_gemm_path(0)
+    _check_quant(got, ref)
+    _check_y(got["y"], d, lam, packed, ref)
+    assert np.array_equal(got["y"], again["y"])
+
+
+@pytest.mark.parametrize("M,K,N", [(512, 3072, 3072), (256, 3072, 12288), (512, 12288, 3072)])
+def test_split_shapes_parity(M, K, N):
+    """Token counts of the text stream and the small-M sweep, where the tiled
+    kernel splits K automatically (96 to 192 tiles), at their full size."""
+    spec = S.LinearSpec(f"split{M}x{K}x{N}", 5, M, K, N, 32, outlier_frac=0.01, outlier_scale=30.0,
+                        heavy_tail=True, gelu_input=(K == 12288))
+    d, lam, packed = oracle_case(spec)
+    got = _run(d, lam, packed)
+    ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
+    _check_quant(got, ref, packed["lora_down"])
+    rows = [0, 1, 63, 64, 127, 128, 255, M - 2, M - 1]
+    _check_y(got["y"], d, lam, packed, ref, rows=sorted(set(rows)))

@@ -97,13 +97,15 @@ struct QuantArgs {
   int GB, TB, KB;   // groups per K-block, row tiles per workgroup, K-blocks
 };
 
-// One 64-wide group of one wave: smooth, quantize, pack, store, and accumulate
-// the lora_down partial.  mu_g points at the group's 64 reciprocals in LDS and
-// lf_g at its lora_down fragments in LDS ([NT][2 halves][64 lanes]).
+// One 64-wide group of one wave: smooth, quantize, pack, and accumulate the
+// lora_down partial.  mu_g points at the group's 64 reciprocals in LDS and
+// lf_g at its lora_down fragments in LDS ([NT][2 halves][64 lanes]).  Returns
+// the row's codes as bytes 4*seg..+3 (code_a) and 16+4*seg..+3 (code_b) of
+// the group's 32, and the scale's bf16 bits.
 template <int NT>
 __device__ __forceinline__ void quant_group(const uint4& xa, const uint4& xb, const float* mu_g,
-                                            const v8bf* lf_g, int g, int lane, bool row_ok,
-                                            uint8_t* crow, uint16_t* srow, v4f* lacc) {
+                                            const v8bf* lf_g, int lane, v4f* lacc, u32& code_a,
+                                            u32& code_b, u32& scale) {
   const int seg = lane >> 4;
   const v4f m0a = *reinterpret_cast<const v4f*>(mu_g + 8 * seg);
   const v4f m0b = *reinterpret_cast<const v4f*>(mu_g + 8 * seg + 4);
@@ -187,11 +189,46 @@ __device__ __forceinline__ void quant_group(const uint4& xa, const uint4& xb, co
                                                         0, 0, 0);
     }
   }
+  code_a = packed[0];
+  code_b = packed[1];
+  scale = sbits;
+}
+
+// Codes and scales of two consecutive groups g, g+1 of a row leave in 16-byte
+// and 4-byte stores.  The row's four lanes (seg = 0..3, lanes 16 apart) hold
+// dwords seg and 4+seg of each group's 32 bytes; a 4 x 4 transpose over seg
+// (two 32-lane swaps, then two 16-lane swaps) gives lane seg the dwords of
+// 16 contiguous bytes: group g bytes 0-15, 16-31, group g+1 bytes 0-15, 16-31.
+// Each store instruction then writes 64 contiguous bytes per row instead of
+// four separate 4-byte pieces, and scale stores halve.
+__device__ __forceinline__ void store_group_pair(u32 a0, u32 b0, u32 s0, u32 a1, u32 b1, u32 s1, int g,
+                                                 int seg, bool row_ok, bool scale_pair_aligned,
+                                                 uint8_t* crow, uint16_t* srow) {
+  const v2u32 t02 = __builtin_amdgcn_permlane32_swap(a0, a1, false, false);
+  const v2u32 t13 = __builtin_amdgcn_permlane32_swap(b0, b1, false, false);
+  const v2u32 u01 = __builtin_amdgcn_permlane16_swap(t02[0], t13[0], false, false);
+  const v2u32 u23 = __builtin_amdgcn_permlane16_swap(t02[1], t13[1], false, false);
+  if (row_ok) {
+    *reinterpret_cast<uint4*>(crow + 32 * g + 16 * seg) = uint4{u01[0], u01[1], u23[0], u23[1]};
+    if (seg == 0) {
+      if (scale_pair_aligned) {
+        *reinterpret_cast<u32*>(srow + g) = s0 | (s1 << 16);
+      } else {
+        srow[g] = (uint16_t)s0;
+        srow[g + 1] = (uint16_t)s1;
+      }
+    }
+  }
+}
+
+// the last group of an odd-sized block: 4-byte code stores
+__device__ __forceinline__ void store_group(u32 a, u32 b, u32 sc, int g, int seg, bool row_ok,
+                                            uint8_t* crow, uint16_t* srow) {
   if (row_ok) {
     uint8_t* c = crow + 32 * g + 4 * seg;
-    *reinterpret_cast<u32*>(c) = packed[0];
-    *reinterpret_cast<u32*>(c + 16) = packed[1];
-    if (seg == 0) srow[g] = (uint16_t)sbits;
+    *reinterpret_cast<u32*>(c) = a;
+    *reinterpret_cast<u32*>(c + 16) = b;
+    if (seg == 0) srow[g] = (uint16_t)sc;
   }
 }
 
@@ -293,27 +330,45 @@ __global__ __launch_bounds__(64 * kMaxTiles) void quant_lora_down_kernel(QuantAr
   // 4. walk the block's groups in full rounds of kDepth: each slot is consumed
   //    in place and then refilled with the group kDepth ahead (refilling first
   //    would make the compiler copy the slot and wait for every load in
-  //    flight); the last round's refills past the block re-read its last group
+  //    flight); the last round's refills past the block re-read its last group.
+  //    The codes of an even group (counted from the block start) wait in
+  //    registers for the next group; the pair is then stored together.
+  const int seg = lane >> 4;
+  const bool pair_aligned = (((size_t)row * a.G + g0) & 1) == 0;  // 4-byte scale pairs
+  u32 pa = 0, pb = 0, ps = 0;
+  auto emit = [&](int gl, u32 ca, u32 cb, u32 sc) {
+    if ((gl & 1) == 0) {
+      pa = ca;
+      pb = cb;
+      ps = sc;
+    } else {
+      store_group_pair(pa, pb, ps, ca, cb, sc, g0 + gl - 1, seg, row_ok, pair_aligned, crow, srow);
+    }
+  };
   const int nfull = gc / kDepth;
   for (int rnd = 0; rnd < nfull; ++rnd) {
 #pragma unroll
     for (int s = 0; s < kDepth; ++s) {
       const int gl = rnd * kDepth + s;
-      quant_group<NT>(ra[s], rb[s], mu_s + 64 * gl, lf_s + gl * NT * 128, g0 + gl, lane, row_ok,
-                      crow, srow, lacc);
+      u32 ca, cb, sc;
+      quant_group<NT>(ra[s], rb[s], mu_s + 64 * gl, lf_s + gl * NT * 128, lane, lacc, ca, cb, sc);
       const int gn = g0 + min(gl + kDepth, gc - 1);
       ra[s] = *reinterpret_cast<const uint4*>(xrow + 64 * gn);
       rb[s] = *reinterpret_cast<const uint4*>(xrow + 64 * gn + 32);
+      emit(gl, ca, cb, sc);
     }
   }
   // the remaining gc % kDepth groups sit in the first slots
 #pragma unroll
   for (int s = 0; s < kDepth; ++s) {
     const int gl = nfull * kDepth + s;
-    if (gl < gc)
-      quant_group<NT>(ra[s], rb[s], mu_s + 64 * gl, lf_s + gl * NT * 128, g0 + gl, lane, row_ok,
-                      crow, srow, lacc);
+    if (gl < gc) {
+      u32 ca, cb, sc;
+      quant_group<NT>(ra[s], rb[s], mu_s + 64 * gl, lf_s + gl * NT * 128, lane, lacc, ca, cb, sc);
+      emit(gl, ca, cb, sc);
+    }
   }
+  if (gc & 1) store_group(pa, pb, ps, g0 + gc - 1, seg, row_ok, crow, srow);
 
   if constexpr (NT > 0) {
     // lane l holds rows 4*(l/16)+v of the tile, rank 16t + l%16

@@ -211,6 +211,69 @@ def measure_pair(pair_name, steps, warmup):
             "gemm_down_TOP/s": 2.0 * M * sd.K * N_dn / t[3] / 1e12}
 
 
+def measure_qkv(steps, warmup):
+    """The fused QKV projection (M=4608, K=3072, N=9216, 24 heads of 128 per
+    third): call 1 + call 2 with the fused Q/K RMSNorm + rotary epilogue, and
+    the same with the plain epilogue, back to back on one stream."""
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K
+    import synthetic as S
+
+    spec = S.SPECS["qkv"]
+    d = S.make_linear(spec)
+    dev = torch.device("cuda:0")
+    K.check_device(0)
+    absmax = np.abs(S.bf16_bits_to_f32(d["x"])).max(axis=0).astype(np.float32)
+    L = _pack_dev(K, d["w"], K.smooth_from_absmax(absmax, d["w"]), d["bias"], spec.r, dev)
+    cos, sin = S.make_rope_tables(spec.M, 128)
+    cos, sin = torch.from_numpy(cos).to(dev), torch.from_numpy(sin).to(dev)
+    qn, kn = _bf(S.make_norm_weight(spec, 0), dev), _bf(S.make_norm_weight(spec, 1), dev)
+    M, Kd, N, r = spec.M, spec.K, spec.N, spec.r
+    per_set = 2 * M * Kd + 2 * M * N
+    nsets = int(min(16, max(NSETS, -(-ROTATE_BYTES // per_set))))
+    sets = [dict(x=_bf(d["x"], dev), y=torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+            for _ in range(nsets)]
+    q = (torch.empty((M, Kd // 2), dtype=torch.uint8, device=dev),
+         torch.empty((M, Kd // 64), dtype=torch.bfloat16, device=dev),
+         torch.empty((M, r), dtype=torch.bfloat16, device=dev))
+    stream = torch.cuda.current_stream()
+
+    def step(s, fused, evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        K.quantize_act_lora_down(s["x"], L["smooth"], L["lora_down"], out=q, stream=stream)
+        if evs is not None:
+            evs[1].record(stream)
+        if fused:
+            K.w4a4_gemm_qkv_norm_rope(q[0], q[1], L["w_codes"], L["w_scales"], q[2], L["lora_up"], L["bias"],
+                                      qn, kn, cos, sin, out=s["y"], stream=stream)
+        else:
+            K.w4a4_gemm_lora_up(q[0], q[1], L["w_codes"], L["w_scales"], q[2], L["lora_up"], L["bias"],
+                                out=s["y"], stream=stream)
+        if evs is not None:
+            evs[2].record(stream)
+
+    res = {"workload": f"qkv: fused QKV projection M={M} K={Kd} N={N} (3 x 24 heads of 128), rank {r}, "
+                       f"group 64, per-head RMSNorm + rotary epilogue on Q and K", "buffer_sets": nsets}
+    for fused in (False, True):
+        for i in range(warmup):
+            step(sets[i % nsets], fused)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            step(sets[i % nsets], fused, evs[i])
+        torch.cuda.synchronize()
+        tq = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+        tg = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+        key = "fused" if fused else "plain"
+        res[f"us_quant_{key}"] = tq * 1e6
+        res[f"us_gemm_{key}"] = tg * 1e6
+        res[f"gemm_TOP/s_{key}"] = 2.0 * M * N * Kd / tg / 1e12
+    res["eff_TOPS_fused"] = 2.0 * M * N * Kd / ((res["us_quant_fused"] + res["us_gemm_fused"]) * 1e-6) / 1e12
+    res["epilogue_extra_us"] = res["us_gemm_fused"] - res["us_gemm_plain"]
+    return res
+
+
 def measure_stack(batch, steps, warmup):
     """One denoising step's linear stack of a FLUX-like 12B DiT: 228 SVDQuant
     linears (456 launches), each layer with its own device buffers of packed
@@ -230,7 +293,13 @@ def measure_stack(batch, steps, warmup):
     for sp in specs:
         first_kn.setdefault((sp.K, sp.N), sp)
         first_mk.setdefault((sp.M, sp.K), sp)
-    xs = {mk: _bf(S.make_x(sp), dev) for mk, sp in first_mk.items()}
+    # activations: drawn once per shape at batch 1; a batch of B images
+    # repeats them B times (the timing does not depend on the values)
+    xs = {}
+    for (m, k), sp in first_mk.items():
+        x1 = _bf(S.make_x(sp.with_m(m // batch)), dev)
+        xs[(m, k)] = x1.repeat(batch, 1).contiguous()
+        del x1
     shape_pack = {}
     for kn, sp in first_kn.items():
         w = S.make_w(sp)
@@ -365,8 +434,9 @@ def main():
                     help="token counts of the same linear reported in the JSON line (HBM-bound regime)")
     ap.add_argument("--pair", default="mlp_pair",
                     help="chained pair reported in the JSON line ('' to skip)")
-    ap.add_argument("--stack", type=int, default=1,
-                    help="batch of the denoising-step stack reported in the JSON line (0 to skip)")
+    ap.add_argument("--qkv", type=int, default=1, help="report the fused QKV projection (0 to skip)")
+    ap.add_argument("--stack", default="1,4",
+                    help="batches of the denoising-step stack reported in the JSON line ('' or 0 to skip)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -442,8 +512,11 @@ def main():
         out["small_m"] = small
     if args.pair:
         out["mlp_pair"] = measure_pair(args.pair, 50, 20)
-    if args.stack:
-        out["step_stack"] = measure_stack(args.stack, 5, 2)
+    if args.qkv:
+        out["qkv_fused"] = measure_qkv(50, 20)
+    batches = [int(b) for b in str(args.stack).split(",") if b and int(b) > 0]
+    if batches:
+        out["step_stack"] = [measure_stack(b, 5, 2) for b in batches]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_rows)
 

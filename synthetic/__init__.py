@@ -30,7 +30,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["LinearSpec", "SPECS", "PAIRS", "make_linear", "make_w", "make_bias", "stack_specs",
+__all__ = ["LinearSpec", "SPECS", "PAIRS", "MOD_SPECS", "make_linear", "make_w", "make_bias",
+           "make_calibration", "stack_specs",
            "make_rope_tables", "make_norm_weight", "to_bf16_bits", "bf16_bits_to_f32"]
 
 # tensor ids inside one (config, layer) seed sequence
@@ -50,6 +51,7 @@ class LinearSpec:
     outlier_scale: float = 1.0
     heavy_tail: bool = False
     gelu_input: bool = False
+    silu_input: bool = False              # modulation input: SiLU of the conditioning vector
     row_outlier_frac: float = 0.0         # fraction of N output channels scaled (rounded)
     layer_id: int = 0
     note: str = field(default="", compare=False)
@@ -87,6 +89,28 @@ SPECS = {
                           outlier_scale=30.0, heavy_tail=True, row_outlier_frac=0.01, layer_id=2),
     "pair_down": LinearSpec("pair_down", 3, 4608, 12288, 3072, 32, heavy_tail=True, layer_id=3),
 }
+
+# modulation projections of a FLUX-like 12B DiT (AWQ W4A16): one conditioning
+# vector per image, SiLU of a pre-activation with 1 % of its channels x10;
+# double blocks 3072 -> 6 x 3072 (image and text stream), single blocks
+# 3072 -> 3 x 3072, the final layer 3072 -> 2 x 3072
+MOD_SPECS = {
+    "mod_double": LinearSpec("mod_double", 6, 1, 3072, 18432, 0, outlier_frac=0.01, outlier_scale=10.0,
+                             heavy_tail=True, silu_input=True, layer_id=0),
+    "mod_single": LinearSpec("mod_single", 6, 1, 3072, 9216, 0, outlier_frac=0.01, outlier_scale=10.0,
+                             heavy_tail=True, silu_input=True, layer_id=1),
+    "mod_final": LinearSpec("mod_final", 6, 1, 3072, 6144, 0, outlier_frac=0.01, outlier_scale=10.0,
+                            heavy_tail=True, silu_input=True, layer_id=2),
+}
+
+
+def make_calibration(spec: LinearSpec, rows: int = 32) -> np.ndarray:
+    """Calibration activations for an offline packer: rows drawn like the
+    layer's input, from a seed stream of their own (bf16 bits [rows, K])."""
+    d = dict(spec.__dict__)
+    d.update(M=int(rows), layer_id=spec.layer_id + 100000)
+    return make_x(LinearSpec(**d))
+
 
 # chained pairs: name -> (up spec, down spec)
 PAIRS = {"mlp_pair": ("pair_up", "pair_down")}
@@ -150,6 +174,8 @@ def make_x(spec: LinearSpec) -> np.ndarray:
     if n_out:
         ch = _rng(spec, _T_XOUT).choice(spec.K, size=n_out, replace=False)
         x[:, ch] *= spec.outlier_scale
+    if spec.silu_input:
+        x = x / (1.0 + np.exp(-x))
     return to_bf16_bits(x)
 
 

@@ -23,7 +23,8 @@ from ._lib import SvdqError, check, lib
 
 __all__ = ["SvdqError", "lib", "check_device", "quantize_act_lora_down", "w4a4_gemm_lora_up",
            "mlp_pair", "w4a4_gemm_qkv_norm_rope", "w4a4_group_acc_debug", "debug_set_quant_plan", "debug_set_gemm_path", "debug_set_gemm_splits",
-           "EPILOGUES", "smooth_from_absmax", "pack_weights", "GROUP_SIZE"]
+           "EPILOGUES", "smooth_from_absmax", "pack_weights", "awq_w4a16_gemm", "awq_pack_weights",
+           "GROUP_SIZE"]
 
 GROUP_SIZE = 64
 
@@ -201,6 +202,47 @@ def w4a4_group_acc_debug(act_codes, w_codes, stream=None):
                                          _ptr(acc), _stream(stream))
     check(st, "svdq_w4a4_group_acc_debug")
     return acc
+
+
+def awq_w4a16_gemm(x, smooth, w_codes, w_scales, w_zeros, bias=None, out=None, stream=None):
+    """AWQ W4A16 linear: x bf16 [M, K], smooth fp32 [K], codes u8 [N, K/2], scales bf16 [N, K/64],
+    zeros u8 [N, K/64], bias bf16 [N] or None -> Y bf16 [M, N]."""
+    torch = _torch()
+    M, K = x.shape
+    N = w_codes.shape[0]
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(smooth, torch.float32, (K,), "smooth")
+    _need(w_codes, torch.uint8, (N, K // 2), "w_codes")
+    _need(w_scales, torch.bfloat16, (N, K // GROUP_SIZE), "w_scales")
+    _need(w_zeros, torch.uint8, (N, K // GROUP_SIZE), "w_zeros")
+    if bias is not None:
+        _need(bias, torch.bfloat16, (N,), "bias")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    st = lib().svdq_awq_w4a16_gemm(_ptr(x), _ptr(smooth), _ptr(w_codes), _ptr(w_scales), _ptr(w_zeros),
+                                   _ptr(bias), M, N, K, GROUP_SIZE, _ptr(y), _stream(stream))
+    check(st, "svdq_awq_w4a16_gemm")
+    return y
+
+
+def awq_pack_weights(w_bf16: np.ndarray, x_calib_bf16: np.ndarray, n_grid: int = 20) -> dict:
+    """Host AWQ packer: W bf16 bits [N, K] + calibration activations bf16 bits [Mc, K] ->
+    smooth fp32 [K], codes u8 [N, K/2], scales (bf16 bits) [N, K/64], zeros u8 [N, K/64], alpha."""
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    xc = np.ascontiguousarray(x_calib_bf16, dtype=np.uint16)
+    N, K = w.shape
+    Mc = xc.shape[0]
+    smooth = np.empty(K, dtype=np.float32)
+    codes = np.empty((N, K // 2), dtype=np.uint8)
+    scales = np.empty((N, K // GROUP_SIZE), dtype=np.uint16)
+    zeros = np.empty((N, K // GROUP_SIZE), dtype=np.uint8)
+    alpha = ctypes.c_float(0.0)
+    vp = ctypes.c_void_p
+    st = lib().svdq_awq_pack_weights(w.ctypes.data_as(vp), xc.ctypes.data_as(vp), Mc, N, K, GROUP_SIZE,
+                                     int(n_grid), smooth.ctypes.data_as(vp), codes.ctypes.data_as(vp),
+                                     scales.ctypes.data_as(vp), zeros.ctypes.data_as(vp),
+                                     ctypes.cast(ctypes.pointer(alpha), vp))
+    check(st, "svdq_awq_pack_weights")
+    return {"smooth": smooth, "codes": codes, "scales": scales, "zeros": zeros, "alpha": float(alpha.value)}
 
 
 def smooth_from_absmax(x_absmax: np.ndarray, w_bf16: np.ndarray) -> np.ndarray:

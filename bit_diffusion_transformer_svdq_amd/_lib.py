@@ -40,12 +40,18 @@ SIGNATURES = {
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
         _i64, _i64, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p, ctypes.c_float,
         _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "svdq_awq_w4a16_gemm": (ctypes.c_int, [
+        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64,
+        _c_void_p, _c_void_p]),
     "svdq_w4a4_group_acc_debug": (ctypes.c_int, [
         _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p]),
     "svdq_smooth_from_absmax": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p]),
     "svdq_pack_weights": (ctypes.c_int, [
         _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _u64,
         _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "svdq_awq_pack_weights": (ctypes.c_int, [
+        _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, ctypes.c_int, _c_void_p, _c_void_p, _c_void_p,
+        _c_void_p, _c_void_p]),
 }
 
 _lib = None

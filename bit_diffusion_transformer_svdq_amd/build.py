@@ -30,7 +30,7 @@ HIP_FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
     "-Wall", "-Wno-unused-function",
 ]
-KERNELS = ["quant_lora_down.hip", "w4a4_gemm_lora_up.hip", "w4a4_gemm_skinny.hip"]
+KERNELS = ["quant_lora_down.hip", "w4a4_gemm_lora_up.hip", "w4a4_gemm_skinny.hip", "awq_w4a16_gemm.hip"]
 
 
 def _hipcc() -> str:

@@ -251,6 +251,34 @@ svdq_status svdq_w4a4_gemm_lora_up(const void* act_codes, const void* act_scales
                                    M, N, K, r, group_size, SVDQ_EPILOGUE_NONE, y, stream);
 }
 
+svdq_status svdq_awq_w4a16_gemm(const void* x, const float* smooth, const void* w_codes,
+                               const void* w_scales, const void* w_zeros, const void* bias, int64_t M,
+                               int64_t N, int64_t K, int64_t group_size, void* y, void* stream) {
+  if (M < 0 || N <= 0 || K <= 0 || group_size <= 0)
+    return fail(SVDQ_STATUS_INVALID_VALUE, "bad dims M=%lld N=%lld K=%lld group_size=%lld", (long long)M,
+                (long long)N, (long long)K, (long long)group_size);
+  if (group_size != 64) return fail(SVDQ_STATUS_NOT_SUPPORTED, "group_size %lld (only 64)", (long long)group_size);
+  if (K % 64 != 0) return fail(SVDQ_STATUS_NOT_SUPPORTED, "K=%lld is not a multiple of 64", (long long)K);
+  if (N % 32 != 0) return fail(SVDQ_STATUS_NOT_SUPPORTED, "N=%lld is not a multiple of 32", (long long)N);
+  if (M > (1ll << 20) || N > (1ll << 20) || svdq::awq_lds_bytes(K) > 160 * 1024)
+    return fail(SVDQ_STATUS_NOT_SUPPORTED, "problem too large M=%lld N=%lld K=%lld", (long long)M,
+                (long long)N, (long long)K);
+  if (M == 0) return ok();
+  if (!x || !smooth || !w_codes || !w_scales || !w_zeros || !y)
+    return fail(SVDQ_STATUS_INVALID_VALUE, "null x/smooth/w_codes/w_scales/w_zeros/y");
+  if (!aligned16(x) || !aligned16(smooth) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      !aligned16(w_zeros) || !aligned16(y) || (bias && !aligned16(bias)))
+    return fail(SVDQ_STATUS_INVALID_VALUE, "device pointers must be 16-byte aligned");
+  svdq_status s = check_current_device();
+  if (s != SVDQ_STATUS_SUCCESS) return s;
+  hipError_t e = svdq::launch_awq_w4a16(
+      static_cast<const uint16_t*>(x), smooth, static_cast<const uint8_t*>(w_codes),
+      static_cast<const uint16_t*>(w_scales), static_cast<const uint8_t*>(w_zeros),
+      static_cast<const uint16_t*>(bias), M, N, K, static_cast<uint16_t*>(y), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SVDQ_STATUS_HIP_ERROR, "awq launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 svdq_status svdq_w4a4_group_acc_debug(const void* act_codes, const void* w_codes, int64_t M,
                                       int64_t N, int64_t K, int64_t group_size, int32_t* acc,
                                       void* stream) {

@@ -352,4 +352,120 @@ svdq_status svdq_pack_weights(const uint16_t* w, const float* smooth, int64_t N,
   return svdq_internal_ok();
 }
 
+
+// AWQ W4A16 packer (Lin et al., 2023, "AWQ: Activation-aware Weight
+// Quantization"): s = clamp(mean|x|^alpha, 1e-4) / sqrt(max s * min s) for
+// alpha = i / n_grid, i = 0..n_grid-1; the alpha whose quantized layer has the
+// least mean squared output error on the calibration rows wins (the first on
+// ties); W * s is then quantized per 64-wide group to unsigned 4-bit codes with
+// Delta = bf16(max(max - min, 1e-5) / 15) and z = clamp(rint(-min / Delta), 0, 15).
+// The scheme is the one the Nunchaku Lite integration uses for its modulation
+// projections (mind-verse.de, "Effiziente Optimierung von Diffusionsmodellen
+// durch Nunchaku 4-Bit-Quantisierung", section "Nunchaku Lite: Nahtlose
+// Integration in Diffusers").
+svdq_status svdq_awq_pack_weights(const uint16_t* w, const uint16_t* x_calib, int64_t Mc, int64_t N,
+                                  int64_t K, int64_t group_size, int n_grid, float* smooth,
+                                  uint8_t* w_codes, uint16_t* w_scales, uint8_t* w_zeros, float* alpha_out) {
+  if (!w || !x_calib || !smooth || !w_codes || !w_scales || !w_zeros)
+    return svdq_internal_fail(SVDQ_STATUS_INVALID_VALUE, "null pointer");
+  if (Mc <= 0 || N <= 0 || K <= 0 || n_grid <= 0 || n_grid > 1000)
+    return svdq_internal_fail(SVDQ_STATUS_INVALID_VALUE, "bad dimensions or grid");
+  if (group_size != 64) return svdq_internal_fail(SVDQ_STATUS_NOT_SUPPORTED, "group_size must be 64");
+  if (K % 64 != 0) return svdq_internal_fail(SVDQ_STATUS_NOT_SUPPORTED, "K must be a multiple of 64");
+  const int64_t G = K / 64;
+  std::vector<double> x(static_cast<size_t>(Mc * K)), wd(static_cast<size_t>(N * K));
+  for (int64_t i = 0; i < Mc * K; ++i) x[i] = bf16_to_double(x_calib[i]);
+  for (int64_t i = 0; i < N * K; ++i) wd[i] = bf16_to_double(w[i]);
+  std::vector<double> sx(static_cast<size_t>(K), 0.0);
+  for (int64_t m = 0; m < Mc; ++m)
+    for (int64_t k = 0; k < K; ++k) sx[k] += std::fabs(x[m * K + k]);
+  for (int64_t k = 0; k < K; ++k) sx[k] /= static_cast<double>(Mc);
+
+  auto scales_for = [&](double alpha, std::vector<float>& s32) {
+    std::vector<double> s(static_cast<size_t>(K));
+    for (int64_t k = 0; k < K; ++k) s[k] = std::max(std::pow(sx[k], alpha), 1e-4);
+    const double mx = *std::max_element(s.begin(), s.end());
+    const double mn = *std::min_element(s.begin(), s.end());
+    const double nrm = std::sqrt(mx * mn);
+    for (int64_t k = 0; k < K; ++k) s32[k] = static_cast<float>(s[k] / nrm);
+  };
+  // quantizes row n of W * s; fills codes q (0..15), Delta bits, z
+  auto quant_row = [&](int64_t n, const std::vector<float>& s32, uint8_t* q, uint16_t* dbits, uint8_t* z) {
+    for (int64_t g = 0; g < G; ++g) {
+      double mx = -INFINITY, mn = INFINITY;
+      double v[64];
+      for (int j = 0; j < 64; ++j) {
+        const int64_t k = g * 64 + j;
+        v[j] = wd[n * K + k] * static_cast<double>(s32[k]);
+        mx = std::max(mx, v[j]);
+        mn = std::min(mn, v[j]);
+      }
+      const uint16_t db = double_to_bf16(std::max(mx - mn, 1e-5) / 15.0);
+      const double d = bf16_to_double(db);
+      const double zz = std::min(std::max(std::nearbyint(-mn / d), 0.0), 15.0);
+      for (int j = 0; j < 64; ++j)
+        q[g * 64 + j] = static_cast<uint8_t>(std::min(std::max(std::nearbyint(v[j] / d) + zz, 0.0), 15.0));
+      dbits[g] = db;
+      z[g] = static_cast<uint8_t>(zz);
+    }
+  };
+  // mean squared output error over the calibration rows; each thread sums its
+  // rows of W in order, the per-row sums are added in row order
+  auto loss_for = [&](const std::vector<float>& s32) {
+    std::vector<double> row_err(static_cast<size_t>(N), 0.0);
+    parallel_for(N, [&](int64_t a, int64_t b) {
+      std::vector<uint8_t> q(static_cast<size_t>(K)), z(static_cast<size_t>(G));
+      std::vector<uint16_t> db(static_cast<size_t>(G));
+      std::vector<double> diff(static_cast<size_t>(K));
+      for (int64_t n = a; n < b; ++n) {
+        quant_row(n, s32, q.data(), db.data(), z.data());
+        for (int64_t k = 0; k < K; ++k) {
+          const int64_t g = k / 64;
+          const double weff = ((double)q[k] - (double)z[g]) * bf16_to_double(db[g]) / (double)s32[k];
+          diff[k] = wd[n * K + k] - weff;
+        }
+        double e = 0.0;
+        for (int64_t m = 0; m < Mc; ++m) {
+          const double* xr = &x[m * K];
+          double acc[4] = {0.0, 0.0, 0.0, 0.0};
+          int64_t k = 0;
+          for (; k + 4 <= K; k += 4)
+            for (int j = 0; j < 4; ++j) acc[j] += xr[k + j] * diff[k + j];
+          double dot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+          for (; k < K; ++k) dot += xr[k] * diff[k];
+          e += dot * dot;
+        }
+        row_err[n] = e;
+      }
+    });
+    double tot = 0.0;
+    for (int64_t n = 0; n < N; ++n) tot += row_err[n];
+    return tot / static_cast<double>(Mc * N);
+  };
+
+  std::vector<float> s32(static_cast<size_t>(K)), best(static_cast<size_t>(K));
+  double best_loss = INFINITY, best_alpha = 0.0;
+  for (int i = 0; i < n_grid; ++i) {
+    const double alpha = static_cast<double>(i) / n_grid;
+    scales_for(alpha, s32);
+    const double l = loss_for(s32);
+    if (l < best_loss) {
+      best_loss = l;
+      best_alpha = alpha;
+      best = s32;
+    }
+  }
+  parallel_for(N, [&](int64_t a, int64_t b) {
+    std::vector<uint8_t> q(static_cast<size_t>(K));
+    for (int64_t n = a; n < b; ++n) {
+      quant_row(n, best, q.data(), w_scales + n * G, w_zeros + n * G);
+      for (int64_t i = 0; i < K / 2; ++i)
+        w_codes[n * (K / 2) + i] = static_cast<uint8_t>(q[2 * i] | (q[2 * i + 1] << 4));
+    }
+  });
+  std::memcpy(smooth, best.data(), sizeof(float) * static_cast<size_t>(K));
+  if (alpha_out) *alpha_out = static_cast<float>(best_alpha);
+  return svdq_internal_ok();
+}
+
 }  // extern "C"

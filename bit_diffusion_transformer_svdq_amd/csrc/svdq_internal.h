@@ -84,6 +84,14 @@ hipError_t launch_w4a4_gemm_skinny(const uint8_t* act_codes, const uint16_t* act
 // few-token kernel wherever it is supported.
 void set_gemm_path_override(int path);
 
+// AWQ W4A16 linear (x bf16 [M, K], unsigned 4-bit codes, bf16 scales and u8
+// zero points per 64-wide group).  Shapes validated by the caller: M > 0,
+// N % 32 == 0, K % 64 == 0, awq_lds_bytes(K) <= 160 KB.
+size_t awq_lds_bytes(int64_t K);
+hipError_t launch_awq_w4a16(const uint16_t* x, const float* smooth, const uint8_t* codes,
+                            const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias,
+                            int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
+
 // Test hook: K-splits per tile of the tiled kernel (0 = choose by shape;
 // clipped to the number of group pairs; ignored for the QKV epilogue).
 void set_gemm_splits_override(int splits);

@@ -264,6 +264,35 @@ svdq_status svdq_w4a4_group_acc_debug(
     int32_t* acc, void* stream);
 
 /*
+ * AWQ W4A16 linear: 4-bit weights with 16-bit activations, the second kernel
+ * family of the Nunchaku Lite integration, used for the adaptive-normalization
+ * and modulation projections (mind-verse.de, "Effiziente Optimierung von
+ * Diffusionsmodellen durch Nunchaku 4-Bit-Quantisierung", section "Nunchaku
+ * Lite: Nahtlose Integration in Diffusers"; precision int4, group_size 64 in
+ * the config of section "Native Ladefunktion in Diffusers").  Quantization as
+ * in AWQ (Lin et al., 2023); weights from svdq_awq_pack_weights.
+ *
+ *   x_hat  = bf16(fl32(x * fl32(1/smooth)))
+ *   Y[m,n] = bf16( sum_g Delta[n,g] * sum_{k in g} x_hat[m,k] (q[n,k] - z[n,g]) + bias[n] )
+ *            (exact products, fp32 accumulation)
+ *
+ *   x         device, bf16 [M, K]
+ *   smooth    device, fp32 [K]   activation-aware scale s (x is divided by it)
+ *   w_codes   device, u8   [N, K/2]  unsigned 4-bit codes q, element 2i in the low nibble
+ *   w_scales  device, bf16 [N, K/64] Delta
+ *   w_zeros   device, u8   [N, K/64] z in 0..15
+ *   bias      device, bf16 [N] or NULL
+ *   M >= 0 (0 is a no-op), N % 32 == 0, K % 64 == 0 with K <= 38912, group_size == 64
+ *   y         device out, bf16 [M, N]
+ * Built for few tokens (a conditioning vector per image): the packed weights
+ * are streamed once per 16 rows of x.  Errors as for svdq_w4a4_gemm_lora_up.
+ */
+svdq_status svdq_awq_w4a16_gemm(
+    const void* x, const float* smooth, const void* w_codes, const void* w_scales,
+    const void* w_zeros, const void* bias, int64_t M, int64_t N, int64_t K, int64_t group_size,
+    void* y, void* stream);
+
+/*
  * Host-side packer, step 1: the smoothing vector (mind-verse.de, section
  * "Nunchaku und SVDQuant": outliers of the activations are shifted into the
  * weights).  lambda_j = fl32(sqrt(max(a_j, 1e-5) / max(max_n |W_nj|, 1e-5))),
@@ -301,6 +330,24 @@ svdq_status svdq_pack_weights(const uint16_t* w, const float* smooth,
                               uint64_t seed,
                               uint8_t* w_codes, uint16_t* w_scales,
                               uint16_t* lora_down, uint16_t* lora_up);
+
+/*
+ * Host AWQ packer (CPU, caller-owned host buffers): the offline step of the
+ * AWQ W4A16 linear.  s_x[k] = mean over the Mc calibration rows of |x[m,k]|;
+ * for alpha = i / n_grid (i = 0..n_grid-1), s = clamp(s_x^alpha, 1e-4) /
+ * sqrt(max s * min s) rounded to fp32, W * s quantized per 64-wide group
+ * (Delta = bf16(max(max - min, 1e-5) / 15), z = clamp(rint(-min / Delta), 0, 15),
+ * q = clamp(rint(w / Delta) + z, 0, 15)); the alpha with the least mean squared
+ * output error on the calibration rows wins (the first on ties).  Outputs the
+ * winning s and the codes, scales and zeros of svdq_awq_w4a16_gemm, and alpha
+ * (alpha_out may be NULL).  Deterministic for any thread count.
+ *   w bf16 [N, K], x_calib bf16 [Mc, K]; Mc, N > 0, K % 64 == 0, group_size == 64,
+ *   1 <= n_grid <= 1000.
+ */
+svdq_status svdq_awq_pack_weights(const uint16_t* w, const uint16_t* x_calib, int64_t Mc, int64_t N,
+                                  int64_t K, int64_t group_size, int n_grid, float* smooth,
+                                  uint8_t* w_codes, uint16_t* w_scales, uint8_t* w_zeros,
+                                  float* alpha_out);
 
 #ifdef __cplusplus
 }

@@ -156,6 +156,29 @@ def test_qkv_entry_point_argument_errors():
         assert qkv() == NO_DEVICE
 
 
+def test_awq_entry_points_argument_errors():
+    L = lib()
+
+    def awq(M=4, N=64, K=256, g=64, x=FAKE, zeros=FAKE, bias=FAKE):
+        return L.svdq_awq_w4a16_gemm(x, FAKE, FAKE, FAKE, zeros, bias, M, N, K, g, FAKE, None)
+    assert awq(N=48) == NOT_SUPPORTED
+    assert awq(K=96) == NOT_SUPPORTED
+    assert awq(g=128) == NOT_SUPPORTED
+    assert awq(K=64 * 700) == NOT_SUPPORTED          # mu table beyond the LDS
+    assert awq(M=-1) == INVALID_VALUE
+    assert awq(x=None) == INVALID_VALUE
+    assert awq(zeros=None) == INVALID_VALUE
+    assert awq(bias=FAKE_ODD) == INVALID_VALUE
+    assert awq(M=0, x=None, zeros=None) == SUCCESS
+    if not _gpu_visible():
+        assert awq() == NO_DEVICE
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    assert L.svdq_awq_pack_weights(None, p, 4, 8, 64, 64, 20, p, p, p, p, None) == INVALID_VALUE
+    assert L.svdq_awq_pack_weights(p, p, 4, 8, 96, 64, 20, p, p, p, p, None) == NOT_SUPPORTED
+    assert L.svdq_awq_pack_weights(p, p, 4, 8, 64, 64, 0, p, p, p, p, None) == INVALID_VALUE
+
+
 def test_debug_hook_argument_errors():
     L = lib()
     assert L.svdq_w4a4_group_acc_debug(FAKE, FAKE, 4, 64, 64, 64, None, None) == INVALID_VALUE

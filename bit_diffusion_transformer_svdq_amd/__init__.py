@@ -24,6 +24,7 @@ from ._lib import SvdqError, check, lib
 __all__ = ["SvdqError", "lib", "check_device", "quantize_act_lora_down", "w4a4_gemm_lora_up",
            "mlp_pair", "w4a4_gemm_qkv_norm_rope", "w4a4_group_acc_debug", "debug_set_quant_plan", "debug_set_gemm_path", "debug_set_gemm_splits",
            "EPILOGUES", "smooth_from_absmax", "pack_weights", "awq_w4a16_gemm", "awq_pack_weights",
+           "quantize_act_lora_down_fp4", "fp4_gemm_lora_up", "pack_weights_fp4",
            "GROUP_SIZE"]
 
 GROUP_SIZE = 64
@@ -202,6 +203,73 @@ def w4a4_group_acc_debug(act_codes, w_codes, stream=None):
                                          _ptr(acc), _stream(stream))
     check(st, "svdq_w4a4_group_acc_debug")
     return acc
+
+
+def quantize_act_lora_down_fp4(x, smooth, lora_down=None, out=None, stream=None):
+    """Call 1, FP4 variant: -> (act_codes u8 [M, K/2] E2M1, act_scales u8 [M, K/32] E8M0,
+    lora_act bf16 [M, r])."""
+    torch = _torch()
+    M, K = x.shape
+    r = 0 if lora_down is None else lora_down.shape[0]
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(smooth, torch.float32, (K,), "smooth")
+    if r:
+        _need(lora_down, torch.bfloat16, (r, K), "lora_down")
+    if out is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+        lora_act = torch.empty((M, r), dtype=torch.bfloat16, device=x.device)
+    else:
+        codes, scales, lora_act = out
+    st = lib().svdq_quantize_act_lora_down_fp4(_ptr(x), _ptr(smooth), _ptr(lora_down) if r else None, M, K, r,
+                                                _ptr(codes), _ptr(scales), _ptr(lora_act) if r else None,
+                                                _stream(stream))
+    check(st, "svdq_quantize_act_lora_down_fp4")
+    return codes, scales, lora_act
+
+
+def fp4_gemm_lora_up(act_codes, act_scales, w_codes, w_scales, lora_act=None, lora_up=None, bias=None,
+                     out=None, stream=None, epilogue="none"):
+    """Call 2, FP4 variant: MXFP4 GEMM (block scales in the matrix core) + lora_up + bias -> Y bf16."""
+    torch = _torch()
+    M = act_codes.shape[0]
+    K = act_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    r = 0 if lora_up is None else lora_up.shape[1]
+    _need(act_codes, torch.uint8, (M, K // 2), "act_codes")
+    _need(act_scales, torch.uint8, (M, K // 32), "act_scales")
+    _need(w_codes, torch.uint8, (N, K // 2), "w_codes")
+    _need(w_scales, torch.uint8, (N, K // 32), "w_scales")
+    if r:
+        _need(lora_act, torch.bfloat16, (M, r), "lora_act")
+        _need(lora_up, torch.bfloat16, (N, r), "lora_up")
+    if bias is not None:
+        _need(bias, torch.bfloat16, (N,), "bias")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=act_codes.device) if out is None else out
+    st = lib().svdq_fp4_gemm_lora_up(_ptr(act_codes), _ptr(act_scales), _ptr(w_codes), _ptr(w_scales),
+                                     _ptr(lora_act) if r else None, _ptr(lora_up) if r else None, _ptr(bias),
+                                     M, N, K, r, EPILOGUES[epilogue], _ptr(y), _stream(stream))
+    check(st, "svdq_fp4_gemm_lora_up")
+    return y
+
+
+def pack_weights_fp4(w_bf16: np.ndarray, smooth: np.ndarray, rank: int, seed: int = 0) -> dict:
+    """Host packer, FP4 variant: -> w_codes u8 [N, K/2], w_scales u8 [N, K/32] (E8M0),
+    lora_down, lora_up (bf16 bits)."""
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    lam = np.ascontiguousarray(smooth, dtype=np.float32)
+    N, K = w.shape
+    codes = np.empty((N, K // 2), dtype=np.uint8)
+    scales = np.empty((N, K // 32), dtype=np.uint8)
+    down = np.empty((rank, K), dtype=np.uint16)
+    up = np.empty((N, rank), dtype=np.uint16)
+    vp = ctypes.c_void_p
+    st = lib().svdq_pack_weights_fp4(w.ctypes.data_as(vp), lam.ctypes.data_as(vp), N, K, int(rank), int(seed),
+                                     codes.ctypes.data_as(vp), scales.ctypes.data_as(vp),
+                                     down.ctypes.data_as(vp) if rank else None,
+                                     up.ctypes.data_as(vp) if rank else None)
+    check(st, "svdq_pack_weights_fp4")
+    return {"w_codes": codes, "w_scales": scales, "lora_down": down, "lora_up": up}
 
 
 def awq_w4a16_gemm(x, smooth, w_codes, w_scales, w_zeros, bias=None, out=None, stream=None):

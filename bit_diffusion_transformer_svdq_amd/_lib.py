@@ -40,6 +40,11 @@ SIGNATURES = {
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
         _i64, _i64, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p, ctypes.c_float,
         _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "svdq_quantize_act_lora_down_fp4": (ctypes.c_int, [
+        _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "svdq_fp4_gemm_lora_up": (ctypes.c_int, [
+        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+        _i64, _i64, _i64, _i64, ctypes.c_int, _c_void_p, _c_void_p]),
     "svdq_awq_w4a16_gemm": (ctypes.c_int, [
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64,
         _c_void_p, _c_void_p]),
@@ -49,6 +54,8 @@ SIGNATURES = {
     "svdq_pack_weights": (ctypes.c_int, [
         _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _u64,
         _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "svdq_pack_weights_fp4": (ctypes.c_int, [
+        _c_void_p, _c_void_p, _i64, _i64, _i64, _u64, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "svdq_awq_pack_weights": (ctypes.c_int, [
         _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, ctypes.c_int, _c_void_p, _c_void_p, _c_void_p,
         _c_void_p, _c_void_p]),

@@ -112,10 +112,10 @@ svdq_status svdq_check_device(int device) {
   return s;
 }
 
-svdq_status svdq_quantize_act_lora_down(const void* x, const float* smooth, const void* lora_down,
-                                        int64_t M, int64_t K, int64_t r, int64_t group_size,
-                                        void* act_codes, void* act_scales, void* lora_act,
-                                        void* stream) {
+static svdq_status quantize_common(const void* x, const float* smooth, const void* lora_down,
+                                   int64_t M, int64_t K, int64_t r, int64_t group_size,
+                                   void* act_codes, void* act_scales, void* lora_act, bool fp4,
+                                   void* stream) {
   if (M < 0 || K <= 0 || r < 0 || group_size <= 0)
     return fail(SVDQ_STATUS_INVALID_VALUE, "bad dims M=%lld K=%lld r=%lld group_size=%lld",
                 (long long)M, (long long)K, (long long)r, (long long)group_size);
@@ -137,9 +137,25 @@ svdq_status svdq_quantize_act_lora_down(const void* x, const float* smooth, cons
   hipError_t e = svdq::launch_quant_lora_down(
       static_cast<const uint16_t*>(x), smooth, static_cast<const uint16_t*>(lora_down), M, K, r,
       static_cast<uint8_t*>(act_codes), static_cast<uint16_t*>(act_scales),
-      static_cast<uint16_t*>(lora_act), static_cast<hipStream_t>(stream));
+      static_cast<uint16_t*>(lora_act), fp4, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SVDQ_STATUS_HIP_ERROR, "quantize launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+svdq_status svdq_quantize_act_lora_down(const void* x, const float* smooth, const void* lora_down,
+                                        int64_t M, int64_t K, int64_t r, int64_t group_size,
+                                        void* act_codes, void* act_scales, void* lora_act,
+                                        void* stream) {
+  return quantize_common(x, smooth, lora_down, M, K, r, group_size, act_codes, act_scales, lora_act, false,
+                         stream);
+}
+
+svdq_status svdq_quantize_act_lora_down_fp4(const void* x, const float* smooth, const void* lora_down,
+                                            int64_t M, int64_t K, int64_t r, void* act_codes,
+                                            void* act_scales, void* lora_act, void* stream) {
+  if (K > 0 && K % 128 != 0)
+    return fail(SVDQ_STATUS_NOT_SUPPORTED, "K=%lld is not a multiple of 128", (long long)K);
+  return quantize_common(x, smooth, lora_down, M, K, r, 64, act_codes, act_scales, lora_act, true, stream);
 }
 
 svdq_status svdq_debug_set_quant_plan(int k_blocks, int tiles_per_wg) {
@@ -249,6 +265,34 @@ svdq_status svdq_w4a4_gemm_lora_up(const void* act_codes, const void* act_scales
                                    void* y, void* stream) {
   return svdq_w4a4_gemm_lora_up_ex(act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,
                                    M, N, K, r, group_size, SVDQ_EPILOGUE_NONE, y, stream);
+}
+
+svdq_status svdq_fp4_gemm_lora_up(const void* act_codes, const void* act_scales, const void* w_codes,
+                                  const void* w_scales, const void* lora_act, const void* lora_up,
+                                  const void* bias, int64_t M, int64_t N, int64_t K, int64_t r, int epilogue,
+                                  void* y, void* stream) {
+  svdq_status s = validate_gemm(act_codes, w_codes, M, N, K, r, 64);
+  if (s != SVDQ_STATUS_SUCCESS) return s;
+  if (K % 128 != 0) return fail(SVDQ_STATUS_NOT_SUPPORTED, "K=%lld is not a multiple of 128", (long long)K);
+  if (epilogue != SVDQ_EPILOGUE_NONE && epilogue != SVDQ_EPILOGUE_GELU_TANH)
+    return fail(SVDQ_STATUS_INVALID_VALUE, "unknown epilogue %d", epilogue);
+  if (M == 0) return ok();
+  if (!act_scales || !w_scales || !y) return fail(SVDQ_STATUS_INVALID_VALUE, "null act_scales/w_scales/y");
+  if (r > 0 && (!lora_act || !lora_up))
+    return fail(SVDQ_STATUS_INVALID_VALUE, "r=%lld needs lora_act and lora_up", (long long)r);
+  if (!aligned16(act_scales) || !aligned16(w_scales) || !aligned16(y) ||
+      (bias && !aligned16(bias)) || (r > 0 && (!aligned16(lora_act) || !aligned16(lora_up))))
+    return fail(SVDQ_STATUS_INVALID_VALUE, "device pointers must be 16-byte aligned");
+  s = check_current_device();
+  if (s != SVDQ_STATUS_SUCCESS) return s;
+  hipError_t e = svdq::launch_fp4_gemm_lora_up(
+      static_cast<const uint8_t*>(act_codes), static_cast<const uint8_t*>(act_scales),
+      static_cast<const uint8_t*>(w_codes), static_cast<const uint8_t*>(w_scales),
+      static_cast<const uint16_t*>(lora_act), static_cast<const uint16_t*>(lora_up),
+      static_cast<const uint16_t*>(bias), M, N, K, r, epilogue, static_cast<uint16_t*>(y),
+      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SVDQ_STATUS_HIP_ERROR, "fp4 gemm launch: %s", hipGetErrorString(e));
+  return ok();
 }
 
 svdq_status svdq_awq_w4a16_gemm(const void* x, const float* smooth, const void* w_codes,

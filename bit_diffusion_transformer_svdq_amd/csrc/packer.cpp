@@ -233,9 +233,21 @@ svdq_status svdq_smooth_from_absmax(const float* x_absmax, const uint16_t* w, in
   return svdq_internal_ok();
 }
 
-svdq_status svdq_pack_weights(const uint16_t* w, const float* smooth, int64_t N, int64_t K, int64_t r,
-                              int64_t group_size, uint64_t seed, uint8_t* w_codes, uint16_t* w_scales,
-                              uint16_t* lora_down, uint16_t* lora_up) {
+}  // extern "C"
+
+namespace {
+
+// E2M1 code of t (|t| < 8 after the block scaling): nearest value, a midpoint
+// to the even code, above 6 saturating, zero without a sign
+uint8_t fp4_code(double t) {
+  const double m = std::fabs(t);
+  const int c = (m > 0.25) + (m >= 0.75) + (m > 1.25) + (m >= 1.75) + (m > 2.5) + (m >= 3.5) + (m > 5.0);
+  return static_cast<uint8_t>(c | ((t < 0 && c != 0) ? 8 : 0));
+}
+
+svdq_status pack_impl(const uint16_t* w, const float* smooth, int64_t N, int64_t K, int64_t r,
+                      int64_t group_size, uint64_t seed, uint8_t* w_codes, uint16_t* w_scales,
+                      uint16_t* lora_down, uint16_t* lora_up, bool fp4) {
   if (!w || !smooth || !w_codes || !w_scales) return svdq_internal_fail(SVDQ_STATUS_INVALID_VALUE, "null pointer");
   if (N <= 0 || K <= 0 || r < 0 || group_size <= 0)
     return svdq_internal_fail(SVDQ_STATUS_INVALID_VALUE, "bad dimensions");
@@ -316,7 +328,8 @@ svdq_status svdq_pack_weights(const uint16_t* w, const float* smooth, int64_t N,
     });
   }
 
-  // residual against the rounded factors, then per-group symmetric int4
+  // residual against the rounded factors, then per-group symmetric int4 or
+  // MXFP4 per 32-block
   const int64_t G = K / 64;
   parallel_for(N, [&](int64_t n0, int64_t n1) {
     std::vector<double> R(static_cast<size_t>(K));
@@ -327,6 +340,28 @@ svdq_status svdq_pack_weights(const uint16_t* w, const float* smooth, int64_t N,
         for (int64_t i = 0; i < r; ++i)
           lowrank += up_d[static_cast<size_t>(n) * r + i] * down_d[static_cast<size_t>(i) * K + k];
         R[k] = a[k] - lowrank;
+      }
+      if (fp4) {
+        // MXFP4 (OCP Microscaling v1.0): e = floor(log2 amax) - 2 in [-127, 127]
+        // (-127 for a zero block), elements R / 2^e to E2M1
+        uint8_t* sc = reinterpret_cast<uint8_t*>(w_scales) + static_cast<size_t>(n) * (K / 32);
+        for (int64_t b = 0; b < K / 32; ++b) {
+          const double* seg = &R[static_cast<size_t>(b) * 32];
+          double amax = 0.0;
+          for (int e = 0; e < 32; ++e) amax = std::max(amax, std::fabs(seg[e]));
+          int e = -127;
+          if (amax > 0) {
+            int x = 0;
+            (void)std::frexp(amax, &x);
+            e = std::max(-127, std::min(127, x - 1 - 2));
+          }
+          sc[b] = static_cast<uint8_t>(e + 127);
+          uint8_t* out = &w_codes[static_cast<size_t>(n) * (K / 2) + b * 16];
+          for (int i = 0; i < 32; i += 2)
+            out[i / 2] = static_cast<uint8_t>(fp4_code(std::ldexp(seg[i], -e)) |
+                                              (fp4_code(std::ldexp(seg[i + 1], -e)) << 4));
+        }
+        continue;
       }
       for (int64_t g = 0; g < G; ++g) {
         const double* seg = &R[static_cast<size_t>(g) * 64];
@@ -350,6 +385,24 @@ svdq_status svdq_pack_weights(const uint16_t* w, const float* smooth, int64_t N,
     }
   });
   return svdq_internal_ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+svdq_status svdq_pack_weights(const uint16_t* w, const float* smooth, int64_t N, int64_t K, int64_t r,
+                              int64_t group_size, uint64_t seed, uint8_t* w_codes, uint16_t* w_scales,
+                              uint16_t* lora_down, uint16_t* lora_up) {
+  return pack_impl(w, smooth, N, K, r, group_size, seed, w_codes, w_scales, lora_down, lora_up, false);
+}
+
+svdq_status svdq_pack_weights_fp4(const uint16_t* w, const float* smooth, int64_t N, int64_t K, int64_t r,
+                                  uint64_t seed, uint8_t* w_codes, uint8_t* w_scales, uint16_t* lora_down,
+                                  uint16_t* lora_up) {
+  if (K > 0 && K % 128 != 0) return svdq_internal_fail(SVDQ_STATUS_NOT_SUPPORTED, "K must be a multiple of 128");
+  return pack_impl(w, smooth, N, K, r, 64, seed, w_codes, reinterpret_cast<uint16_t*>(w_scales), lora_down,
+                   lora_up, true);
 }
 
 

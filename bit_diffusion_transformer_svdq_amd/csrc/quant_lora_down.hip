@@ -101,8 +101,9 @@ struct QuantArgs {
 // lora_down partial.  mu_g points at the group's 64 reciprocals in LDS and
 // lf_g at its lora_down fragments in LDS ([NT][2 halves][64 lanes]).  Returns
 // the row's codes as bytes 4*seg..+3 (code_a) and 16+4*seg..+3 (code_b) of
-// the group's 32, and the scale's bf16 bits.
-template <int NT>
+// the group's 32, and the scale's bf16 bits (int4), or the two E8M0 exponents
+// of the group's 32-blocks (MXFP4: block 2g in the low byte).
+template <int NT, bool kFp4>
 __device__ __forceinline__ void quant_group(const uint4& xa, const uint4& xb, const float* mu_g,
                                             const v8bf* lf_g, int lane, v4f* lacc, u32& code_a,
                                             u32& code_b, u32& scale) {
@@ -126,56 +127,111 @@ __device__ __forceinline__ void quant_group(const uint4& xa, const uint4& xb, co
     xf[2 * d] = lo_bf16(xh[d]);
     xf[2 * d + 1] = hi_bf16(xh[d]);
   }
-  // A = max |x_hat| over the group.  With the sign bit cleared, bf16 bit
-  // patterns of non-negative values order like the values, so the maximum is
-  // taken on 16-bit integers, two per instruction; the four lanes holding the
-  // row's group (l, l^16, l^32, l^48) are combined with two lane swaps.
-  v2u16 mm = __builtin_bit_cast(v2u16, xh[0] & 0x7FFF7FFFu);
+  if constexpr (kFp4) {
+    // MXFP4 (OCP Microscaling v1.0): per 32-block, shared exponent
+    // floor(log2 amax) - 2 as a biased E8M0 byte, which from the bf16 bits of
+    // the block maximum is max(E - 2, 0) (E its exponent field; a zero or
+    // subnormal maximum gives 0, the clamped -127).  Elements 0-7 of this lane
+    // are in block 0 (k = 8 seg + 0..7), elements 8-15 in block 1.  Each
+    // element is scaled by 2^(127 - e) (exact) and rounded to the nearest
+    // E2M1 value by the midpoint ladder 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5
+    // (a midpoint to the even code), above 6 saturating; zero has no sign.
+    v2u16 mb0 = __builtin_bit_cast(v2u16, xh[0] & 0x7FFF7FFFu);
+    v2u16 mb1 = __builtin_bit_cast(v2u16, xh[4] & 0x7FFF7FFFu);
 #pragma unroll
-  for (int d = 1; d < 8; ++d) mm = __builtin_elementwise_max(mm, __builtin_bit_cast(v2u16, xh[d] & 0x7FFF7FFFu));
-  u32 am = max((u32)mm[0], (u32)mm[1]);
-  {
-    const v2u32 sw = __builtin_amdgcn_permlane16_swap(am, am, false, false);
-    am = max(sw[0], sw[1]);
-    const v2u32 sw2 = __builtin_amdgcn_permlane32_swap(am, am, false, false);
-    am = max(sw2[0], sw2[1]);
-  }
-  const float amax = __builtin_bit_cast(float, am << 16);
-
-  // s = bf16(fl32(A / 7)) equals bf16(fl32(A * fl32(1/7))) for every
-  // non-negative bf16 A (checked exhaustively: the two fp32 values differ in
-  // the last bit at times, never across a bf16 rounding boundary).
-  const u32 sbits = pack_bf16(amax * kRcp7, 0.f) & 0xFFFFu;
-  const float s = __builtin_bit_cast(float, sbits << 16);
-  // iota = fl32(1/s): hardware reciprocal and one Newton step, exact for bf16
-  // s in [2^-100, 2^100] (checked exhaustively on the device); outside that
-  // range (never for real activations) the IEEE division.
-  float iota;
-  const bool fast = s >= 0x1p-100f && s <= 0x1p100f;
-  if (__builtin_amdgcn_ballot_w64(!fast && s > 0.f) == 0) {
-    const float r = __builtin_amdgcn_rcpf(s);
-    iota = fast ? __builtin_fmaf(__builtin_fmaf(-s, r, 1.0f), r, r) : 0.f;
+    for (int d = 1; d < 4; ++d) {
+      mb0 = __builtin_elementwise_max(mb0, __builtin_bit_cast(v2u16, xh[d] & 0x7FFF7FFFu));
+      mb1 = __builtin_elementwise_max(mb1, __builtin_bit_cast(v2u16, xh[4 + d] & 0x7FFF7FFFu));
+    }
+    u32 a0 = max((u32)mb0[0], (u32)mb0[1]);
+    u32 a1 = max((u32)mb1[0], (u32)mb1[1]);
+    {
+      const v2u32 s0 = __builtin_amdgcn_permlane16_swap(a0, a0, false, false);
+      const v2u32 s1 = __builtin_amdgcn_permlane16_swap(a1, a1, false, false);
+      a0 = max(s0[0], s0[1]);
+      a1 = max(s1[0], s1[1]);
+      const v2u32 t0 = __builtin_amdgcn_permlane32_swap(a0, a0, false, false);
+      const v2u32 t1 = __builtin_amdgcn_permlane32_swap(a1, a1, false, false);
+      a0 = max(t0[0], t0[1]);
+      a1 = max(t1[0], t1[1]);
+    }
+    const u32 e0 = (u32)max((int)(a0 >> 7) - 2, 0);
+    const u32 e1 = (u32)max((int)(a1 >> 7) - 2, 0);
+    const float inv[2] = {__builtin_bit_cast(float, (254u - e0) << 23),
+                          __builtin_bit_cast(float, (254u - e1) << 23)};
+    u32 packed[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      u32 w = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = xf[8 * i + e] * inv[i];
+        const float m = __builtin_fabsf(t);
+        const u32 c = (u32)(m > 0.25f) + (u32)(m >= 0.75f) + (u32)(m > 1.25f) + (u32)(m >= 1.75f) +
+                      (u32)(m > 2.5f) + (u32)(m >= 3.5f) + (u32)(m > 5.0f);
+        const u32 code = c | ((t < 0.f && c != 0u) ? 8u : 0u);
+        w |= code << (4 * e);
+      }
+      packed[i] = w;
+    }
+    code_a = packed[0];
+    code_b = packed[1];
+    scale = e0 | (e1 << 8);
   } else {
-    // a reciprocal that overflows (s < 2^-128) makes the group a zero group,
-    // like s = 0
-    const float r = 1.0f / s;
-    iota = (s > 0.f && r <= 0x1.fffffep127f) ? r : 0.f;
-  }
+    // A = max |x_hat| over the group.  With the sign bit cleared, bf16 bit
+    // patterns of non-negative values order like the values, so the maximum is
+    // taken on 16-bit integers, two per instruction; the four lanes holding the
+    // row's group (l, l^16, l^32, l^48) are combined with two lane swaps.
+    v2u16 mm = __builtin_bit_cast(v2u16, xh[0] & 0x7FFF7FFFu);
+  #pragma unroll
+    for (int d = 1; d < 8; ++d) mm = __builtin_elementwise_max(mm, __builtin_bit_cast(v2u16, xh[d] & 0x7FFF7FFFu));
+    u32 am = max((u32)mm[0], (u32)mm[1]);
+    {
+      const v2u32 sw = __builtin_amdgcn_permlane16_swap(am, am, false, false);
+      am = max(sw[0], sw[1]);
+      const v2u32 sw2 = __builtin_amdgcn_permlane32_swap(am, am, false, false);
+      am = max(sw2[0], sw2[1]);
+    }
+    const float amax = __builtin_bit_cast(float, am << 16);
 
-  // q = rint(x_hat * iota): the low byte of fma(x_hat, iota, 1.5 * 2^23) is q
-  // in two's complement.  Bytes are gathered with byte permutes (even and odd
-  // elements apart) and merged into nibbles (element 2i low).
-  u32 packed[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    u32 qb[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qb[e] = __builtin_bit_cast(u32, fmaf(xf[8 * i + e], iota, kRoundMagic));
-    const u32 ev = __builtin_amdgcn_perm(__builtin_amdgcn_perm(qb[6], qb[4], 0x0C0C0400u),
-                                         __builtin_amdgcn_perm(qb[2], qb[0], 0x0C0C0400u), 0x05040100u);
-    const u32 od = __builtin_amdgcn_perm(__builtin_amdgcn_perm(qb[7], qb[5], 0x0C0C0400u),
-                                         __builtin_amdgcn_perm(qb[3], qb[1], 0x0C0C0400u), 0x05040100u);
-    packed[i] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+    // s = bf16(fl32(A / 7)) equals bf16(fl32(A * fl32(1/7))) for every
+    // non-negative bf16 A (checked exhaustively: the two fp32 values differ in
+    // the last bit at times, never across a bf16 rounding boundary).
+    const u32 sbits = pack_bf16(amax * kRcp7, 0.f) & 0xFFFFu;
+    const float s = __builtin_bit_cast(float, sbits << 16);
+    // iota = fl32(1/s): hardware reciprocal and one Newton step, exact for bf16
+    // s in [2^-100, 2^100] (checked exhaustively on the device); outside that
+    // range (never for real activations) the IEEE division.
+    float iota;
+    const bool fast = s >= 0x1p-100f && s <= 0x1p100f;
+    if (__builtin_amdgcn_ballot_w64(!fast && s > 0.f) == 0) {
+      const float r = __builtin_amdgcn_rcpf(s);
+      iota = fast ? __builtin_fmaf(__builtin_fmaf(-s, r, 1.0f), r, r) : 0.f;
+    } else {
+      // a reciprocal that overflows (s < 2^-128) makes the group a zero group,
+      // like s = 0
+      const float r = 1.0f / s;
+      iota = (s > 0.f && r <= 0x1.fffffep127f) ? r : 0.f;
+    }
+
+    // q = rint(x_hat * iota): the low byte of fma(x_hat, iota, 1.5 * 2^23) is q
+    // in two's complement.  Bytes are gathered with byte permutes (even and odd
+    // elements apart) and merged into nibbles (element 2i low).
+    u32 packed[2];
+  #pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      u32 qb[8];
+  #pragma unroll
+      for (int e = 0; e < 8; ++e) qb[e] = __builtin_bit_cast(u32, fmaf(xf[8 * i + e], iota, kRoundMagic));
+      const u32 ev = __builtin_amdgcn_perm(__builtin_amdgcn_perm(qb[6], qb[4], 0x0C0C0400u),
+                                           __builtin_amdgcn_perm(qb[2], qb[0], 0x0C0C0400u), 0x05040100u);
+      const u32 od = __builtin_amdgcn_perm(__builtin_amdgcn_perm(qb[7], qb[5], 0x0C0C0400u),
+                                           __builtin_amdgcn_perm(qb[3], qb[1], 0x0C0C0400u), 0x05040100u);
+      packed[i] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+    }
+    code_a = packed[0];
+    code_b = packed[1];
+    scale = sbits;
   }
 
   // fused lora_down: lacc[t] += x_hat[16 rows, 64] @ L1[64, 16 ranks]
@@ -189,9 +245,6 @@ __device__ __forceinline__ void quant_group(const uint4& xa, const uint4& xb, co
                                                         0, 0, 0);
     }
   }
-  code_a = packed[0];
-  code_b = packed[1];
-  scale = sbits;
 }
 
 // Codes and scales of two consecutive groups g, g+1 of a row leave in 16-byte
@@ -232,7 +285,7 @@ __device__ __forceinline__ void store_group(u32 a, u32 b, u32 sc, int g, int seg
   }
 }
 
-template <int NT>  // NT = r / 16 rank tiles of 16
+template <int NT, bool kFp4>  // NT = r / 16 rank tiles of 16; kFp4: MXFP4 codes instead of int4
 __global__ __launch_bounds__(64 * kMaxTiles) void quant_lora_down_kernel(QuantArgs a) {
   constexpr int R = NT * 16;
   constexpr int kDepth = depth_for<NT>();
@@ -351,7 +404,7 @@ __global__ __launch_bounds__(64 * kMaxTiles) void quant_lora_down_kernel(QuantAr
     for (int s = 0; s < kDepth; ++s) {
       const int gl = rnd * kDepth + s;
       u32 ca, cb, sc;
-      quant_group<NT>(ra[s], rb[s], mu_s + 64 * gl, lf_s + gl * NT * 128, lane, lacc, ca, cb, sc);
+      quant_group<NT, kFp4>(ra[s], rb[s], mu_s + 64 * gl, lf_s + gl * NT * 128, lane, lacc, ca, cb, sc);
       const int gn = g0 + min(gl + kDepth, gc - 1);
       ra[s] = *reinterpret_cast<const uint4*>(xrow + 64 * gn);
       rb[s] = *reinterpret_cast<const uint4*>(xrow + 64 * gn + 32);
@@ -364,7 +417,7 @@ __global__ __launch_bounds__(64 * kMaxTiles) void quant_lora_down_kernel(QuantAr
     const int gl = nfull * kDepth + s;
     if (gl < gc) {
       u32 ca, cb, sc;
-      quant_group<NT>(ra[s], rb[s], mu_s + 64 * gl, lf_s + gl * NT * 128, lane, lacc, ca, cb, sc);
+      quant_group<NT, kFp4>(ra[s], rb[s], mu_s + 64 * gl, lf_s + gl * NT * 128, lane, lacc, ca, cb, sc);
       emit(gl, ca, cb, sc);
     }
   }
@@ -497,11 +550,11 @@ int cu_count(int dev) {
   return n;
 }
 
-template <int NT>
+template <int NT, bool kFp4>
 hipError_t launch_nt(const QuantArgs& a, const Plan& p, hipStream_t stream) {
   const dim3 grid(p.nrb, p.KB);
   const dim3 block(64 * p.TB);
-  auto kern = quant_lora_down_kernel<NT>;
+  auto kern = quant_lora_down_kernel<NT, kFp4>;
   if (p.lds + kMuBytes > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
@@ -520,7 +573,7 @@ void set_quant_plan_override(int k_blocks, int tiles_per_wg) {
 
 hipError_t launch_quant_lora_down(const uint16_t* x, const float* lam, const uint16_t* lora_down,
                                   int64_t M, int64_t K, int64_t r, uint8_t* codes,
-                                  uint16_t* scales, uint16_t* lora_act, hipStream_t stream) {
+                                  uint16_t* scales, uint16_t* lora_act, bool fp4, hipStream_t stream) {
   const int NT = (int)(r / 16);
   const int T = (int)((M + 15) / 16);
   const int G = (int)(K / 64);
@@ -555,15 +608,15 @@ hipError_t launch_quant_lora_down(const uint16_t* x, const float* lam, const uin
   }
 
   switch (NT) {
-    case 0: return launch_nt<0>(a, p, stream);
-    case 1: return launch_nt<1>(a, p, stream);
-    case 2: return launch_nt<2>(a, p, stream);
-    case 3: return launch_nt<3>(a, p, stream);
-    case 4: return launch_nt<4>(a, p, stream);
-    case 5: return launch_nt<5>(a, p, stream);
-    case 6: return launch_nt<6>(a, p, stream);
-    case 7: return launch_nt<7>(a, p, stream);
-    case 8: return launch_nt<8>(a, p, stream);
+    case 0: return fp4 ? launch_nt<0, true>(a, p, stream) : launch_nt<0, false>(a, p, stream);
+    case 1: return fp4 ? launch_nt<1, true>(a, p, stream) : launch_nt<1, false>(a, p, stream);
+    case 2: return fp4 ? launch_nt<2, true>(a, p, stream) : launch_nt<2, false>(a, p, stream);
+    case 3: return fp4 ? launch_nt<3, true>(a, p, stream) : launch_nt<3, false>(a, p, stream);
+    case 4: return fp4 ? launch_nt<4, true>(a, p, stream) : launch_nt<4, false>(a, p, stream);
+    case 5: return fp4 ? launch_nt<5, true>(a, p, stream) : launch_nt<5, false>(a, p, stream);
+    case 6: return fp4 ? launch_nt<6, true>(a, p, stream) : launch_nt<6, false>(a, p, stream);
+    case 7: return fp4 ? launch_nt<7, true>(a, p, stream) : launch_nt<7, false>(a, p, stream);
+    case 8: return fp4 ? launch_nt<8, true>(a, p, stream) : launch_nt<8, false>(a, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -46,10 +46,12 @@ hipError_t stream_workspace(hipStream_t stream, size_t counters, size_t bytes, u
 
 // Call 1: smoothing + int4 group quantization + packing + fused lora_down.
 // Shapes are validated by the caller: M > 0, K % 64 == 0, r % 16 == 0, r <= 128.
+// fp4: MXFP4 codes with two E8M0 exponents per 64-group (stored as one u16
+// per group: block 2g in the low byte) instead of int4 codes and bf16 scales.
 hipError_t launch_quant_lora_down(const uint16_t* x, const float* lam, const uint16_t* lora_down,
                                   int64_t M, int64_t K, int64_t r,
                                   uint8_t* codes, uint16_t* scales, uint16_t* lora_act,
-                                  hipStream_t stream);
+                                  bool fp4, hipStream_t stream);
 
 // Test hook: forces call 1's work split (K-blocks, row tiles per workgroup);
 // 0 keeps the automatic choice.  Affects later launches of this process.
@@ -79,6 +81,14 @@ hipError_t launch_w4a4_gemm_skinny(const uint8_t* act_codes, const uint16_t* act
                                    const uint16_t* bias, int64_t M, int64_t N, int64_t K,
                                    int64_t r, int epilogue, uint16_t* y, int32_t* acc_dump,
                                    hipStream_t stream);
+
+// Call 2 of the MXFP4 variant (tiled kernel; E8M0 scales u8 [rows, K/32],
+// K % 128 == 0; epilogue none or GELU).
+hipError_t launch_fp4_gemm_lora_up(const uint8_t* act_codes, const uint8_t* act_scales,
+                                  const uint8_t* w_codes, const uint8_t* w_scales,
+                                  const uint16_t* lora_act, const uint16_t* lora_up,
+                                  const uint16_t* bias, int64_t M, int64_t N, int64_t K, int64_t r,
+                                  int epilogue, uint16_t* y, hipStream_t stream);
 
 // Test hook: 0 = choose by shape, 1 = always the tiled kernel, 2 = the
 // few-token kernel wherever it is supported.

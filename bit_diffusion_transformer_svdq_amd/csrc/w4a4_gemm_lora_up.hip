@@ -62,6 +62,7 @@ namespace svdq {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
@@ -160,8 +161,11 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
 }
 
 // kOcc: waves per SIMD the register budget is sized for (main kernel); the
-// accumulator-dump test hook uses 1 so it never spills.
-template <bool kDump, int kOcc>
+// accumulator-dump test hook uses 1 so it never spills.  kFp4: the MXFP4
+// variant (codes are E2M1 nibbles, scales E8M0 bytes per 32-block); a ring
+// stage (128 k) is then one v_mfma_scale_f32_16x16x128_f8f6f4 per tile, the
+// block scales applied inside the matrix core, with no dequantization work.
+template <bool kDump, int kOcc, bool kFp4 = false>
 __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArgs<kDump> p) {
   // One LDS object per operand tile and scale area of every ring stage: the
   // compiler then sees that a DMA in flight into one object cannot alias the
@@ -232,7 +236,8 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
   const bool s_is_act = tid < kBM;
   const int s_idx = s_is_act ? tid : tid - kBM;
   const uint16_t* sbase = s_is_act ? p.act_scales : p.w_scales;  // wave-uniform
-  const u32 soff = (u32)(s_is_act ? min(m0 + sx_token(s_idx), M - 1) : min(n0 + s_idx, N - 1)) * (u32)G;
+  const u32 soff =
+      (u32)(s_is_act ? min(m0 + (kFp4 ? s_idx : sx_token(s_idx)), M - 1) : min(n0 + s_idx, N - 1)) * (u32)G;
   // register ring of raw bf16 scales, pair q in slot q % 3
   u32 slo[3], shi[3];
   auto load_scales = [&](int q, int k) {
@@ -248,6 +253,11 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
     u32 o = 4u * (u32)(s_is_act ? s_idx : 128 + s_idx);
     __asm__ volatile("" : "+v"(o));  // keeps the per-stage addresses out of registers
     uint8_t* sp = reinterpret_cast<uint8_t*>(sarea(buf)) + o;
+    if constexpr (kFp4) {
+      // the row's four E8M0 bytes of the stage (blocks 4q .. 4q+3), as loaded
+      *reinterpret_cast<u32*>(sp) = slo[k] | (shi[k] << 16);
+      return;
+    }
     const float f0 = __builtin_bit_cast(float, slo[k] << 16);
     const float f1 = __builtin_bit_cast(float, shi[k] << 16);
     *reinterpret_cast<float*>(sp) = s_is_act ? f0 * (1.0f / 256.0f) : f0;
@@ -364,7 +374,41 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
   // One pair: with registers to spare (2 workgroups per CU) both groups' LDS
   // reads are issued up front, so the second group's land during the first
   // one's compute; under the 3-per-CU register budget each group reads its own.
+  // MXFP4 stage: lane (l16, lseg) reads k-block lseg of its rows (granule
+  // lseg, 16 bytes = 32 codes) and the rows' E8M0 byte of that block
+  const int fw4 = 64 * (wn * 64 + l16) + 16 * (lseg ^ fsw);
+  const int fa4 = 64 * (wm * 64 + l16) + 16 * (lseg ^ fsw);
+  auto compute_stage_fp4 = [&](int buf, int sbuf) {
+    const uint8_t* wt = wtile(buf);
+    const uint8_t* at = atile(buf);
+    const uint8_t* sp = reinterpret_cast<const uint8_t*>(sarea(sbuf));
+    uint4 wq[4], aq[4];
+    int sw[4], sx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wq[i] = *reinterpret_cast<const uint4*>(wt + fw4 + 1024 * i);
+      sw[i] = sp[4 * (128 + wn * 64 + 16 * i + l16) + lseg];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      aq[j] = *reinterpret_cast<const uint4*>(at + fa4 + 1024 * j);
+      sx[j] = sp[4 * (wm * 64 + 16 * j + l16) + lseg];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v8i wa = {(int)wq[i].x, (int)wq[i].y, (int)wq[i].z, (int)wq[i].w, 0, 0, 0, 0};
+        const v8i ab = {(int)aq[j].x, (int)aq[j].y, (int)aq[j].z, (int)aq[j].w, 0, 0, 0, 0};
+        y[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, ab, y[i][j], 4, 4, 0, sw[i], 0, sx[j]);
+      }
+  };
   auto compute_pair = [&](int buf, int sbuf, int q) {
+    if constexpr (kFp4) {
+      compute_stage_fp4(buf, sbuf);
+      (void)q;
+      return;
+    }
     const int g0 = 2 * (qb + q);
     const bool two = g0 + 1 < G;
     if constexpr (kOcc <= 2) {
@@ -677,10 +721,10 @@ int pick_splits(int tiles, int pairs, int cus) {
 
 std::atomic<int> g_splits{0};  // test hook (0 = automatic)
 
-template <bool kDump>
+template <bool kDump, bool kFp4 = false>
 hipError_t launch(GemmArgs<kDump> a, hipStream_t stream) {
   const int tiles = ((a.N + kBN - 1) / kBN) * ((a.M + kBM - 1) / kBM);
-  auto kern = w4a4_gemm_kernel<kDump, kDump ? 1 : 3>;
+  auto kern = w4a4_gemm_kernel<kDump, kDump ? 1 : 3, kFp4>;
   size_t pad = 0;
   a.splits = 1;
   if constexpr (!kDump) {
@@ -700,7 +744,7 @@ hipError_t launch(GemmArgs<kDump> a, hipStream_t stream) {
       a.part = static_cast<float*>(part);
     }
     if (pick_occupancy(tiles * a.splits, cus) == 2) {
-      kern = w4a4_gemm_kernel<kDump, 2>;
+      kern = w4a4_gemm_kernel<kDump, 2, kFp4>;
       // the lora tiles, and at least enough that only 2 workgroups fit a CU
       pad = max((size_t)(80 * 1024 - kStaticLds), (size_t)2 * kBN * a.r * 2);
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -719,6 +763,20 @@ std::atomic<int> g_path{0};
 }  // namespace
 
 void set_gemm_path_override(int path) { g_path.store(path, std::memory_order_relaxed); }
+
+hipError_t launch_fp4_gemm_lora_up(const uint8_t* act_codes, const uint8_t* act_scales,
+                                  const uint8_t* w_codes, const uint8_t* w_scales,
+                                  const uint16_t* lora_act, const uint16_t* lora_up,
+                                  const uint16_t* bias, int64_t M, int64_t N, int64_t K, int64_t r,
+                                  int epilogue, uint16_t* y, hipStream_t stream) {
+  if (K % 128 != 0 || epilogue == kEpilogueQkv) return hipErrorInvalidValue;
+  // the E8M0 byte pairs of a 64-group travel like the int4 path's bf16 scale
+  GemmArgs<false> a{act_codes, reinterpret_cast<const uint16_t*>(act_scales), w_codes,
+                    reinterpret_cast<const uint16_t*>(w_scales), lora_act, lora_up, bias,
+                    y, nullptr, (int)M, (int)N, (int)K, (int)r, epilogue, QkvEpilogue{}, 1,
+                    nullptr, nullptr};
+  return launch<false, true>(a, stream);
+}
 
 void set_gemm_splits_override(int splits) { g_splits.store(std::max(0, splits), std::memory_order_relaxed); }
 

@@ -264,6 +264,44 @@ svdq_status svdq_w4a4_group_acc_debug(
     int32_t* acc, void* stream);
 
 /*
+ * FP4 variant of calls 1 and 2.  The svdq_w4a4 family also comes in a 4-bit
+ * floating-point precision (mind-verse.de, "Effiziente Optimierung von
+ * Diffusionsmodellen durch Nunchaku 4-Bit-Quantisierung", sections "Nunchaku
+ * Lite: Nahtlose Integration in Diffusers" and "Hardware-Unterstützung"; named
+ * nvfp4 there, group size 16, for Blackwell).  Here the element format is the
+ * one CDNA4's matrix cores compute on natively, OCP MXFP4 (Microscaling
+ * Formats v1.0): blocks of 32 along K share an E8M0 scale 2^e with
+ * e = floor(log2 max|v|) - 2 clamped to [-127, 127] (-127 for a zero block),
+ * elements are E2M1 (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; sign bit 3) rounded
+ * to nearest, a midpoint to the even code, above 6 saturating, zero unsigned.
+ * Smoothing and the low-rank branch are those of the int4 path.
+ *
+ * Call 1 (svdq_quantize_act_lora_down_fp4): as svdq_quantize_act_lora_down
+ * with x_hat quantized to MXFP4 per token and 32-block:
+ *   act_codes  device out, u8 [M, K/2] E2M1 codes, element 2i in the low nibble
+ *   act_scales device out, u8 [M, K/32] biased exponents e + 127
+ *   K % 128 == 0, group size fixed (32-blocks); other arguments and errors as
+ *   for the int4 call.  Codes and exponents are exactly defined.
+ * Call 2 (svdq_fp4_gemm_lora_up):
+ *   Y = bf16( sum_k deq(act)[m,k] deq(w)[n,k] + lora_act . lora_up^T + bias )
+ *   with deq(code, e) = E2M1(code) * 2^(e - 127), fp32 accumulation inside the
+ *   matrix core (v_mfma_scale_f32_16x16x128_f8f6f4, the block scales applied
+ *   there); w_codes u8 [N, K/2] and w_scales u8 [N, K/32] from
+ *   svdq_pack_weights_fp4; epilogue SVDQ_EPILOGUE_NONE or _GELU_TANH; K % 128
+ *   == 0; other arguments and errors as for svdq_w4a4_gemm_lora_up_ex.
+ */
+svdq_status svdq_quantize_act_lora_down_fp4(
+    const void* x, const float* smooth, const void* lora_down,
+    int64_t M, int64_t K, int64_t r,
+    void* act_codes, void* act_scales, void* lora_act, void* stream);
+svdq_status svdq_fp4_gemm_lora_up(
+    const void* act_codes, const void* act_scales,
+    const void* w_codes, const void* w_scales,
+    const void* lora_act, const void* lora_up, const void* bias,
+    int64_t M, int64_t N, int64_t K, int64_t r, int epilogue,
+    void* y, void* stream);
+
+/*
  * AWQ W4A16 linear: 4-bit weights with 16-bit activations, the second kernel
  * family of the Nunchaku Lite integration, used for the adaptive-normalization
  * and modulation projections (mind-verse.de, "Effiziente Optimierung von
@@ -330,6 +368,16 @@ svdq_status svdq_pack_weights(const uint16_t* w, const float* smooth,
                               uint64_t seed,
                               uint8_t* w_codes, uint16_t* w_scales,
                               uint16_t* lora_down, uint16_t* lora_up);
+
+/*
+ * Host packer of the FP4 variant: smoothing and rank-r split as
+ * svdq_pack_weights (same seed, same factors), the residual quantized to
+ * MXFP4 per row and 32-block: w_codes u8 [N, K/2], w_scales u8 [N, K/32].
+ * K % 128 == 0; errors as svdq_pack_weights.
+ */
+svdq_status svdq_pack_weights_fp4(const uint16_t* w, const float* smooth, int64_t N, int64_t K, int64_t r,
+                                  uint64_t seed, uint8_t* w_codes, uint8_t* w_scales, uint16_t* lora_down,
+                                  uint16_t* lora_up);
 
 /*
  * Host AWQ packer (CPU, caller-owned host buffers): the offline step of the

@@ -179,6 +179,26 @@ def test_awq_entry_points_argument_errors():
     assert L.svdq_awq_pack_weights(p, p, 4, 8, 64, 64, 0, p, p, p, p, None) == INVALID_VALUE
 
 
+def test_fp4_entry_points_argument_errors():
+    L = lib()
+
+    def q(M=64, K=256, r=16, x=FAKE):
+        return L.svdq_quantize_act_lora_down_fp4(x, FAKE, FAKE, M, K, r, FAKE, FAKE, FAKE, None)
+
+    def g(M=64, N=256, K=256, r=16, ep=0, asc=FAKE):
+        return L.svdq_fp4_gemm_lora_up(FAKE, asc, FAKE, FAKE, FAKE, FAKE, FAKE, M, N, K, r, ep, FAKE, None)
+    assert q(K=192) == NOT_SUPPORTED and g(K=192) == NOT_SUPPORTED
+    assert q(x=None) == INVALID_VALUE and g(asc=None) == INVALID_VALUE
+    assert g(ep=2) == INVALID_VALUE and g(N=96) == NOT_SUPPORTED
+    assert q(M=0, x=None) == SUCCESS and g(M=0, asc=None) == SUCCESS
+    if not _gpu_visible():
+        assert q() == NO_DEVICE and g() == NO_DEVICE and g(ep=1) == NO_DEVICE
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    assert L.svdq_pack_weights_fp4(p, p, 8, 192, 0, 0, p, p, None, None) == NOT_SUPPORTED
+    assert L.svdq_pack_weights_fp4(None, p, 8, 128, 0, 0, p, p, None, None) == INVALID_VALUE
+
+
 def test_debug_hook_argument_errors():
     L = lib()
     assert L.svdq_w4a4_group_acc_debug(FAKE, FAKE, 4, 64, 64, 64, None, None) == INVALID_VALUE

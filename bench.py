@@ -274,6 +274,161 @@ def measure_qkv(steps, warmup):
     return res
 
 
+FP4_PEAK_TFLOPS = 10100.0   # MI355X dense FP4 MFMA, 10.1 PFLOP/s
+
+
+def measure_fp4(spec_name, steps=100, warmup=50):
+    """The FP4 (MXFP4) variant of the same linear: call 1 (MXFP4 quantizer with
+    fused lora_down) + call 2 (block-scaled FP4 MFMA GEMM + lora_up + bias),
+    weights from the host packer, rotating buffer sets, HIP events per call."""
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K
+    import synthetic as S
+
+    spec = S.SPECS[spec_name]
+    d = S.make_linear(spec)
+    dev = torch.device("cuda:0")
+    K.check_device(0)
+    absmax = np.abs(S.bf16_bits_to_f32(d["x"])).max(axis=0).astype(np.float32)
+    lam = K.smooth_from_absmax(absmax, d["w"])
+    pk = K.pack_weights_fp4(d["w"], lam, spec.r)
+    M, Kd, N, r = spec.M, spec.K, spec.N, spec.r
+    per_set = 2 * M * Kd + 2 * M * N + N * Kd // 2
+    nsets = int(min(16, max(NSETS, -(-ROTATE_BYTES // per_set))))
+    sets = [dict(x=_bf(d["x"], dev), wc=torch.from_numpy(pk["w_codes"]).to(dev),
+                 ws=torch.from_numpy(pk["w_scales"]).to(dev),
+                 y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)) for _ in range(nsets)]
+    lam_t = torch.from_numpy(lam).to(dev)
+    down, up, bias = _bf(pk["lora_down"], dev), _bf(pk["lora_up"], dev), _bf(d["bias"], dev)
+    q = (torch.empty((M, Kd // 2), dtype=torch.uint8, device=dev),
+         torch.empty((M, Kd // 32), dtype=torch.uint8, device=dev),
+         torch.empty((M, r), dtype=torch.bfloat16, device=dev))
+    stream = torch.cuda.current_stream()
+
+    def step(s, evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        K.quantize_act_lora_down_fp4(s["x"], lam_t, down, out=q, stream=stream)
+        if evs is not None:
+            evs[1].record(stream)
+        K.fp4_gemm_lora_up(q[0], q[1], s["wc"], s["ws"], q[2], up, bias, out=s["y"], stream=stream)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for i in range(warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(sets[i % nsets], evs[i])
+    torch.cuda.synchronize()
+    tq = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    tg = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    ops = 2.0 * M * N * Kd
+    return {"workload": f"{spec_name} in MXFP4: M={M} K={Kd} N={N} rank {r}, E2M1 elements, E8M0 scale per 32",
+            "buffer_sets": nsets, "us_per_step": wall * 1e6, "eff_TFLOPS": ops / wall / 1e12,
+            "us_quant": tq * 1e6, "us_gemm": tg * 1e6, "gemm_TFLOP/s": ops / tg / 1e12,
+            "gemm_fp4_frac": ops / tg / 1e12 / FP4_PEAK_TFLOPS,
+            "quant_GB/s": (2 * M * Kd + M * Kd // 2 + M * Kd // 32 + 2 * M * r) / tq / 1e9}
+
+
+def awq_bytes(M, N, K):
+    """Algorithmic HBM bytes of one AWQ W4A16 linear (weights, scales, zero
+    points and bias read once, x and s read, Y written)."""
+    return N * K // 2 + 3 * N * (K // 64) + 2 * N + 2 * M * K + 4 * K + 2 * M * N
+
+
+def measure_awq(batch, steps=20, warmup=5, calib_rows=16):
+    """The AWQ W4A16 modulation projections of one denoising step of a FLUX-like
+    12B DiT: 19 double blocks x (image, text) 3072 -> 18432, 38 single blocks
+    3072 -> 9216, the final layer 3072 -> 6144; one conditioning vector per
+    image (M = batch); 77 launches, each layer with its own weight buffers.
+    Each shape is packed once by the host packer (AWQ search on calib_rows
+    calibration rows) and copied into every layer's buffers."""
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K
+    import synthetic as S
+
+    dev = torch.device("cuda:0")
+    K.check_device(0)
+    packs = {}
+    t0 = time.perf_counter()
+    for name, spec in S.MOD_SPECS.items():
+        w = S.make_w(spec)
+        pk = K.awq_pack_weights(w, S.make_calibration(spec, calib_rows))
+        packs[name] = dict(spec=spec.with_m(batch), x=_bf(S.make_x(spec.with_m(batch)), dev),
+                           smooth=torch.from_numpy(pk["smooth"]).to(dev),
+                           codes=torch.from_numpy(pk["codes"]).to(dev), scales=_bf(pk["scales"], dev),
+                           zeros=torch.from_numpy(pk["zeros"]).to(dev), bias=_bf(S.make_bias(spec), dev),
+                           alpha=pk["alpha"])
+    pack_s = time.perf_counter() - t0
+    order = ["mod_double"] * 38 + ["mod_single"] * 38 + ["mod_final"]
+    layers = []
+    for name in order:
+        src = packs[name]
+        layers.append(dict(name=name, spec=src["spec"], x=src["x"], smooth=src["smooth"], bias=src["bias"],
+                           codes=src["codes"].clone(), scales=src["scales"].clone(), zeros=src["zeros"].clone()))
+    ys = {n: torch.empty((batch, p["spec"].N), dtype=torch.bfloat16, device=dev) for n, p in packs.items()}
+    stream = torch.cuda.Stream()
+
+    def step():
+        for L in layers:
+            K.awq_w4a16_gemm(L["x"], L["smooth"], L["codes"], L["scales"], L["zeros"], L["bias"],
+                             out=ys[L["name"]], stream=stream)
+
+    def timed(fn, n):
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+        return (time.perf_counter() - t) / n
+
+    byts = sum(awq_bytes(L["spec"].M, L["spec"].N, L["spec"].K) for L in layers)
+    t_eager = timed(step, steps)
+    # per-launch kernel time of the largest shape, HIP events on the launch stream
+    L0 = layers[0]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    with torch.cuda.stream(stream):
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for L in layers[:38]:
+            K.awq_w4a16_gemm(L["x"], L["smooth"], L["codes"], L["scales"], L["zeros"], L["bias"],
+                             out=ys[L["name"]], stream=stream)
+        evs[1].record(stream)
+    torch.cuda.synchronize()
+    t_double = evs[0].elapsed_time(evs[1]) * 1e-3 / 38
+    b_double = awq_bytes(batch, 18432, 3072)
+    out = {"workload": f"AWQ W4A16 modulation projections of one denoising step, batch {batch}: 38 x 3072->18432, "
+                       f"38 x 3072->9216, 1 x 3072->6144, group 64, M = {batch}",
+           "launches": len(layers), "bytes_per_step": byts, "offline_pack_s": pack_s,
+           "alpha": {n: p["alpha"] for n, p in packs.items()},
+           "ms_eager": t_eager * 1e3, "GB/s_eager": byts / t_eager / 1e9,
+           "us_per_launch_3072x18432": t_double * 1e6,
+           "GB/s_3072x18432": b_double / t_double / 1e9,
+           "hbm_frac_3072x18432": b_double / t_double / 1e9 / HBM_PEAK_GBS}
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step()
+        t_graph = timed(g.replay, steps)
+        out.update({"ms_graph": t_graph * 1e3, "GB/s_graph": byts / t_graph / 1e9,
+                    "hbm_frac_graph": byts / t_graph / 1e9 / HBM_PEAK_GBS})
+    except Exception as e:
+        out["graph_error"] = f"{type(e).__name__}: {e}"
+    return out
+
+
 def measure_stack(batch, steps, warmup):
     """One denoising step's linear stack of a FLUX-like 12B DiT: 228 SVDQuant
     linears (456 launches), each layer with its own device buffers of packed
@@ -435,6 +590,9 @@ def main():
     ap.add_argument("--pair", default="mlp_pair",
                     help="chained pair reported in the JSON line ('' to skip)")
     ap.add_argument("--qkv", type=int, default=1, help="report the fused QKV projection (0 to skip)")
+    ap.add_argument("--fp4", type=int, default=1, help="report the FP4 (MXFP4) variant of the headline (0 to skip)")
+    ap.add_argument("--awq", default="1,4",
+                    help="batches of the AWQ W4A16 modulation stack reported in the JSON line ('' or 0 to skip)")
     ap.add_argument("--stack", default="1,4",
                     help="batches of the denoising-step stack reported in the JSON line ('' or 0 to skip)")
     ap.add_argument("--copy-calib", type=int, default=0,
@@ -514,6 +672,11 @@ def main():
         out["mlp_pair"] = measure_pair(args.pair, 50, 20)
     if args.qkv:
         out["qkv_fused"] = measure_qkv(50, 20)
+    if args.fp4:
+        out["fp4_mxfp4"] = measure_fp4(args.config)
+    awq_batches = [int(b) for b in str(args.awq).split(",") if b and int(b) > 0]
+    if awq_batches:
+        out["awq_w4a16"] = [measure_awq(b) for b in awq_batches]
     batches = [int(b) for b in str(args.stack).split(",") if b and int(b) > 0]
     if batches:
         out["step_stack"] = [measure_stack(b, 5, 2) for b in batches]

@@ -70,8 +70,9 @@ def mx_quantize_blocks(v, block: int = MX_BLOCK):
     R, K = v.shape
     vb = v.reshape(R, K // block, block)
     amax = np.abs(vb).max(axis=-1)
-    with np.errstate(divide="ignore"):
-        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    # floor(log2 amax) exactly, from the binary exponent (frexp: amax = f 2^x, f in [0.5, 1))
+    _, x = np.frexp(amax)
+    e = np.where(amax > 0, x.astype(np.float64) - 1 - 2, -127)
     e = np.clip(e, -127, 127)
     codes = fp4_round(vb / np.exp2(e)[..., None])
     return codes.reshape(R, K), (e + 127).astype(np.uint8)

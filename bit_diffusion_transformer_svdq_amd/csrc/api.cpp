@@ -305,7 +305,7 @@ svdq_status svdq_awq_w4a16_gemm(const void* x, const float* smooth, const void* 
   if (group_size != 64) return fail(SVDQ_STATUS_NOT_SUPPORTED, "group_size %lld (only 64)", (long long)group_size);
   if (K % 64 != 0) return fail(SVDQ_STATUS_NOT_SUPPORTED, "K=%lld is not a multiple of 64", (long long)K);
   if (N % 32 != 0) return fail(SVDQ_STATUS_NOT_SUPPORTED, "N=%lld is not a multiple of 32", (long long)N);
-  if (M > (1ll << 20) || N > (1ll << 20) || svdq::awq_lds_bytes(K, std::min<int64_t>(M, 16)) > 160 * 1024)
+  if (M > (1ll << 20) || N > (1ll << 20) || (M > 0 && !svdq::awq_supported(K, M)))
     return fail(SVDQ_STATUS_NOT_SUPPORTED, "problem too large M=%lld N=%lld K=%lld", (long long)M,
                 (long long)N, (long long)K);
   if (M == 0) return ok();

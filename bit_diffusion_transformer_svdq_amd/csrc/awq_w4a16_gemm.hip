@@ -49,6 +49,14 @@ typedef u32 v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kRing = 3;                 // code chunks in flight per wave
+constexpr int kRingStage = 1024 * kWaves;  // one chunk of each wave
+// workgroups per CU an instance fits in (LDS), at most 5 (registers)
+constexpr int awq_occupancy(int rows, int kmax) {
+  const int g = kmax / 64;
+  const int lds = kRing * kRingStage + 16 * ((3 * g + 63) & ~63) + 64 * g + 2 * rows * kmax;
+  return 160 * 1024 / lds < 5 ? 160 * 1024 / lds : 5;
+}
 
 struct AwqArgs {
   const uint16_t* x;
@@ -70,19 +78,41 @@ __device__ __forceinline__ u32 pack_bf16(float a, float b) {
   return __builtin_bit_cast(u32, __builtin_convertvector(f, v2bf));
 }
 
-__global__ __launch_bounds__(kThreads) void awq_w4a16_kernel(const AwqArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int P = a.K >> 5;                          // 16-byte code pieces per row
+// wait until at most n vector-memory operations of this wave are outstanding
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14));
+}
+// wait until all LDS operations of this wave are done
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14)); }
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// kRowsMax x kKMax: the largest token tile and K the instance stages.  Every
+// LDS area is a static object: the compiler then tracks which of them a DMA
+// in flight writes, and waits only for the ring stage a read depends on (an
+// access to dynamic LDS would wait for every DMA in flight).
+template <int kRowsMax, int kKMax>
+__global__ __launch_bounds__(kThreads, awq_occupancy(kRowsMax, kKMax)) void awq_w4a16_kernel(const AwqArgs a) {
+  constexpr int kGMax = kKMax / 64;
+  constexpr int kDzSlots = (3 * kGMax + 63) & ~63;  // Delta + z, whole 1 KB blocks
+  // Code ring: stage s holds, for each wave w, one chunk (2 groups x 16 rows
+  // x 32 bytes = 1 KB) at 1024 w.
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[kRingStage], ring1[kRingStage], ring2[kRingStage];
+  __shared__ __attribute__((aligned(16))) uint8_t dz_s[16 * kDzSlots];       // [16][G] Delta, [16][G] z
+  __shared__ __attribute__((aligned(16))) float xs_s[16 * kGMax];            // [G][16] sum x_hat
+  __shared__ __attribute__((aligned(16))) uint4 xh_s[kRowsMax * kKMax / 8];  // [rows][K/8]
+  auto stage_of = [&](int s) -> uint8_t* { return s == 0 ? ring0 : s == 1 ? ring1 : ring2; };
+  static_assert(kRing == 3, "one LDS object per ring stage");
+
   const int G = a.G;
-  const int ncode = 16 * P;                        // code slots of the 16 rows
-  const int nslots = ncode + 3 * G;                // + Delta (2G slots) + z (G slots)
-  const int wslots = (nslots + 63) & ~63;          // whole 1 KB DMA blocks
-  uint8_t* w_s = smem;                                                        // [ncode][16 B]
-  const uint16_t* d_s = reinterpret_cast<const uint16_t*>(smem + 16 * ncode);  // [16][G] Delta
-  const uint8_t* z_s = smem + 16 * ncode + 32 * G;                             // [16][G] z
-  float* xs_s = reinterpret_cast<float*>(smem + 16 * wslots);                  // [G][16] sum x_hat
-  v4f* red = reinterpret_cast<v4f*>(smem + 16 * wslots + 64 * G);              // [kWaves][64]
-  uint4* xh_s = reinterpret_cast<uint4*>(smem + 16 * wslots + 64 * G + kWaves * 64 * 16);  // [rows][K/8]
+  const int dzslots = (3 * G + 63) & ~63;
+  const uint16_t* d_s = reinterpret_cast<const uint16_t*>(dz_s);
+  const uint8_t* z_s = dz_s + 32 * G;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -92,10 +122,15 @@ __global__ __launch_bounds__(kThreads) void awq_w4a16_kernel(const AwqArgs a) {
   const int m0 = blockIdx.y * 16;
   const int rows = min(a.rows, a.M - m0);
   const int runs = a.K >> 3;
+  const int g_lo = (wave * G) / kWaves;             // groups [g_lo, g_hi) of this wave
+  const int g_hi = ((wave + 1) * G) / kWaves;
+  const int nch = (g_hi - g_lo + 1) >> 1;           // chunks of 2 groups
 
   // 1. Loads, in issue order (vector-memory counters retire in issue order):
-  //    1/s and x of the thread's first two runs (up to 4 token rows), then the
-  //    workgroup's weight block, so staging x_hat waits only for the small loads.
+  //    1/s and x of the thread's first two runs (up to 4 token rows); the 16
+  //    rows' Delta and z (contiguous in [N, G] layout, n0 a multiple of 16, so
+  //    both start on a 16-byte boundary); then exactly 3 code chunks of this
+  //    wave, so "at most 3 outstanding" means everything before has landed.
   uint4 xv[2][4];
   v4f sv[2][2];
 #pragma unroll
@@ -108,26 +143,30 @@ __global__ __launch_bounds__(kThreads) void awq_w4a16_kernel(const AwqArgs a) {
       xv[u][rr] = *reinterpret_cast<const uint4*>(a.x + (size_t)(m0 + min(rr, rows - 1)) * a.K + 8 * c);
   }
   __asm__ volatile("" ::: "memory");  // these small loads go out first
-  // Weight block, one 16-byte slot per lane: slots [0, 16P) are the codes,
-  // piece c of row r at r P + (c ^ r) inside complete 16-piece blocks (keeps
-  // the fragment reads free of bank conflicts); then the 16 rows' Delta and z,
-  // contiguous in [N, G] layout (n0 is a multiple of 16, so both start on a
-  // 16-byte boundary).  Pad lanes of the last block repeat the last slot.
-  auto swz = [&](int c, int r) { return ((c | 15) < P) ? (c ^ (r & 15)) : c; };
-  for (int j0 = 64 * wave; j0 < wslots; j0 += 64 * kWaves) {
-    const int j = min(j0 + lane, nslots - 1);
-    const uint8_t* src;
-    if (j < ncode) {
-      const int r = j / P, c = swz(j - r * P, r);
-      src = a.codes + (size_t)(n0 + r) * (a.K >> 1) + 16 * c;
-    } else if (j < ncode + 2 * G) {
-      src = reinterpret_cast<const uint8_t*>(a.scales) + (size_t)n0 * G * 2 + 16 * (j - ncode);
-    } else {
-      src = a.zeros + (size_t)n0 * G + 16 * (j - ncode - 2 * G);
-    }
-    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)(w_s + 16 * j0), 16, 0, 0);
+  // (a fixed count per wave: blocks past the last repeat it, pad lanes the
+  // last slot)
+#pragma unroll
+  for (int t = 0; t < kDzSlots / (64 * kWaves) + (kDzSlots % (64 * kWaves) != 0); ++t) {
+    const int j0 = min(64 * (wave + kWaves * t), dzslots - 64);
+    const int j = min(j0 + lane, 3 * G - 1);
+    const uint8_t* src = j < 2 * G ? reinterpret_cast<const uint8_t*>(a.scales) + (size_t)n0 * G * 2 + 16 * j
+                                   : a.zeros + (size_t)n0 * G + 16 * (j - 2 * G);
+    dma16(src, dz_s + 16 * j0);
   }
+  // Chunk i of the wave: groups g_lo + 2i, +1.  Lane l moves 16 bytes to
+  // slot l of the wave's 1 KB: row l / 4, position l % 4, which holds piece
+  // p = (l % 4) ^ (row / 4 % 4) of the row's 64 bytes (so the fragment reads
+  // of 16 rows hit distinct banks).  Chunks past the wave's last one repeat
+  // its last chunk (an L2 hit), keeping the count of DMAs per wave fixed.
+  const int drow_ = lane >> 2;
+  const int dpiece = (lane & 3) ^ ((drow_ >> 2) & 3);
+  const uint8_t* dsrc = a.codes + (size_t)(n0 + drow_) * (a.K >> 1) + 16 * (dpiece & 1);
+  auto dma_chunk = [&](int i, int s) {
+    const int g = min(g_lo + 2 * min(i, max(nch - 1, 0)) + (dpiece >> 1), G - 1);
+    dma16(dsrc + 32 * g, stage_of(s) + 1024 * wave);
+  };
+#pragma unroll
+  for (int s = 0; s < kRing; ++s) dma_chunk(s, s);
   __asm__ volatile("" ::: "memory");
 
   // 2. x_hat = bf16(fl32(x mu)), mu = fl32(1/s), each run of 8 stored in the
@@ -180,73 +219,71 @@ __global__ __launch_bounds__(kThreads) void awq_w4a16_kernel(const AwqArgs a) {
     for (int rr = 0; rr < rows; ++rr)
       stage(*reinterpret_cast<const uint4*>(a.x + (size_t)(m0 + rr) * a.K + 8 * c), mu, rr, c);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's DMAs have landed
+  wait_vm<kRing>();  // Delta, z and the x loads of this wave have landed
   __syncthreads();
 
-  // 3. Groups [g_lo, g_hi) of this wave (wave-uniform bounds).  Rows of A past
-  //    the tile's tokens repeat its last row: their outputs are not stored.
-  const int g_lo = (wave * G) / kWaves;
-  const int g_hi = ((wave + 1) * G) / kWaves;
+  // 3. The wave's chunks through the ring: wait for chunk i (the ring is the
+  //    wave's own, so no barrier), compute its two groups (independent MFMA
+  //    chains), refill the stage with chunk i + 3.  Rows of A past the tile's
+  //    tokens repeat its last row: their outputs are not stored.
   const uint4* xr = xh_s + (size_t)min(l16, rows - 1) * runs + 2 * seg;
-  const uint8_t* wrow = w_s + 16 * l16 * P + 8 * (seg & 1);
   const uint16_t* drow = d_s + l16 * G;
   const uint8_t* zrow = z_s + l16 * G;
+  const int fsw = (l16 >> 2) & 3;
+  const int foff = 1024 * wave + 64 * l16 + 8 * (seg & 1);
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
   v4f yacc = zero4;
-  // operands of one group, read from LDS one step ahead of their use
-  struct Ops {
-    uint4 r0, r1;
-    uint2 wv;
-    v4f xs;
-    u32 dl, z;
-  };
-  auto read_ops = [&](Ops& o, int g) {
-    o.r0 = xr[8 * g];
-    o.r1 = xr[8 * g + 1];
-    o.wv = *reinterpret_cast<const uint2*>(wrow + 16 * swz(2 * g + (seg >> 1), l16));
-    o.xs = *reinterpret_cast<const v4f*>(xs_s + 16 * g + 4 * seg);
-    o.dl = drow[g];
-    o.z = zrow[g];
-  };
-  auto mfma_ops = [&](const Ops& o) {
-    const v8bf af0 = __builtin_bit_cast(v8bf, v4u{o.r0.x, o.r0.y, o.r0.z, o.r0.w});
-    const v8bf af1 = __builtin_bit_cast(v8bf, v4u{o.r1.x, o.r1.y, o.r1.z, o.r1.w});
-    const u32 wd[2] = {o.wv.x, o.wv.y};
+  auto group = [&](const uint8_t* st, int h, int g) {
+    const int gr = min(g, G - 1);  // the second group of an odd tail is computed, not added
+    const uint4 r0 = xr[8 * gr], r1 = xr[8 * gr + 1];
+    // one 64-bit load (split into two 32-bit loads, the second lost the
+    // LDS-object information the waits depend on)
+    const uint64_t w64 = *reinterpret_cast<const uint64_t*>(st + foff + 16 * ((2 * h + (seg >> 1)) ^ fsw));
+    const v8bf af0 = __builtin_bit_cast(v8bf, v4u{r0.x, r0.y, r0.z, r0.w});
+    const v8bf af1 = __builtin_bit_cast(v8bf, v4u{r1.x, r1.y, r1.z, r1.w});
+    const u32 wd[2] = {(u32)w64, (u32)(w64 >> 32)};
     v8bf bf[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const v4u b = {(wd[h] & 0x000F000Fu) | 0x43004300u, ((wd[h] >> 4) & 0x000F000Fu) | 0x43004300u,
-                     ((wd[h] >> 8) & 0x000F000Fu) | 0x43004300u, ((wd[h] >> 12) & 0x000F000Fu) | 0x43004300u};
-      bf[h] = __builtin_bit_cast(v8bf, b);
+    for (int hh = 0; hh < 2; ++hh) {
+      const v4u b = {(wd[hh] & 0x000F000Fu) | 0x43004300u, ((wd[hh] >> 4) & 0x000F000Fu) | 0x43004300u,
+                     ((wd[hh] >> 8) & 0x000F000Fu) | 0x43004300u, ((wd[hh] >> 12) & 0x000F000Fu) | 0x43004300u};
+      bf[hh] = __builtin_bit_cast(v8bf, b);
     }
     const v4f acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af0, bf[0], zero4, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(af1, bf[1], acc, 0, 0, 0);
   };
-  auto finish = [&](const Ops& o, const v4f acc) {
-    const float dl = __builtin_bit_cast(float, o.dl << 16);
-    const float cz = -(128.0f + (float)o.z);
+  auto finish = [&](int g, const v4f acc) {
+    const float dl = __builtin_bit_cast(float, (u32)drow[g] << 16);
+    const float cz = -(128.0f + (float)zrow[g]);
+    const v4f xs = *reinterpret_cast<const v4f*>(xs_s + 16 * g + 4 * seg);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) yacc[v] = fmaf(dl, fmaf(cz, o.xs[v], acc[v]), yacc[v]);
+    for (int v = 0; v < 4; ++v) yacc[v] = fmaf(dl, fmaf(cz, xs[v], acc[v]), yacc[v]);
   };
-  // two groups per step (independent MFMA chains), the next two read ahead;
-  // indexes past the wave's range are clamped (read, never used)
-  const int glast = G - 1;
-  Ops o0, o1;
-  read_ops(o0, min(g_lo, glast));
-  read_ops(o1, min(g_lo + 1, glast));
-  for (int g = g_lo; g < g_hi; g += 2) {
-    Ops n0, n1;
-    read_ops(n0, min(g + 2, glast));
-    read_ops(n1, min(g + 3, glast));
-    const v4f acc0 = mfma_ops(o0);
-    const v4f acc1 = mfma_ops(o1);
-    finish(o0, acc0);
-    if (g + 1 < g_hi) finish(o1, acc1);
-    o0 = n0;
-    o1 = n1;
+  for (int i0 = 0; i0 < nch; i0 += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      // every step runs the same instructions (past the last chunk on
+      // repeated data), so the count of DMAs in flight is the same on every
+      // path and the compiler's own waits stay at one stage
+      const int i = i0 + u;
+      wait_vm<kRing - 1>();
+      const uint8_t* st = stage_of(u);
+      const int g = g_lo + 2 * i;
+      const v4f acc0 = group(st, 0, g);  // past the last chunk: computed, not added
+      const v4f acc1 = group(st, 1, g + 1);
+      wait_lds();  // the stage's reads are done before it is refilled
+      dma_chunk(i + kRing, u);
+      if (i < nch) {
+        finish(g, acc0);
+        if (g + 1 < g_hi) finish(g + 1, acc1);
+      }
+    }
   }
 
-  // 4. partials of the four waves added in wave order
+  // 4. partials of the four waves added in wave order, through the wave's own
+  //    1 KB of ring stage 0 once its DMAs have landed
+  wait_vm<0>();
+  v4f* red = reinterpret_cast<v4f*>(ring0);
   red[wave * 64 + lane] = yacc;
   __syncthreads();
   if (wave == 0) {
@@ -263,27 +300,35 @@ __global__ __launch_bounds__(kThreads) void awq_w4a16_kernel(const AwqArgs a) {
   }
 }
 
+// instances: (token rows, K) classes, smallest first
+struct AwqClass {
+  int rows, kmax;
+  void (*kernel)(AwqArgs);
+};
+constexpr AwqClass kClasses[] = {
+    {1, 4096, awq_w4a16_kernel<1, 4096>},   {1, 16384, awq_w4a16_kernel<1, 16384>},
+    {4, 4096, awq_w4a16_kernel<4, 4096>},   {4, 8192, awq_w4a16_kernel<4, 8192>},
+    {16, 4096, awq_w4a16_kernel<16, 4096>},
+};
+const AwqClass* awq_class(int64_t K, int64_t rows) {
+  for (const AwqClass& c : kClasses)
+    if (rows <= c.rows && K <= c.kmax) return &c;
+  return nullptr;
+}
+
 }  // namespace
 
-size_t awq_lds_bytes(int64_t K, int64_t rows) {
-  const size_t G = (size_t)K / 64;
-  const size_t wslots = ((size_t)16 * (K / 32) + 3 * G + 63) & ~(size_t)63;
-  return 16 * wslots + 64 * G + (size_t)kWaves * 64 * 16 + (size_t)rows * K * 2;
-}
+bool awq_supported(int64_t K, int64_t M) { return awq_class(K, std::min<int64_t>(M, 16)) != nullptr; }
 
 hipError_t launch_awq_w4a16(const uint16_t* x, const float* smooth, const uint8_t* codes,
                             const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias,
                             int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
   const int rows = (int)std::min<int64_t>(16, M);
   AwqArgs a{x, smooth, codes, scales, zeros, bias, y, (int)M, (int)N, (int)K, (int)(K / 64), rows};
-  const size_t lds = awq_lds_bytes(K, rows);
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(awq_w4a16_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  const AwqClass* c = awq_class(K, rows);
+  if (!c) return hipErrorInvalidValue;  // excluded by the caller's awq_supported check
   const dim3 grid((unsigned)((N + 15) / 16), (unsigned)((M + 15) / 16));
-  hipLaunchKernelGGL(awq_w4a16_kernel, grid, dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL(c->kernel, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -96,8 +96,9 @@ void set_gemm_path_override(int path);
 
 // AWQ W4A16 linear (x bf16 [M, K], unsigned 4-bit codes, bf16 scales and u8
 // zero points per 64-wide group).  Shapes validated by the caller: M > 0,
-// N % 32 == 0, K % 64 == 0, awq_lds_bytes(K, min(16, M)) <= 160 KB.
-size_t awq_lds_bytes(int64_t K, int64_t rows);
+// N % 32 == 0, K % 64 == 0, awq_supported(K, M): K <= 16384 for M == 1,
+// K <= 8192 for M <= 4, K <= 4096 otherwise (the LDS the instances stage).
+bool awq_supported(int64_t K, int64_t M);
 hipError_t launch_awq_w4a16(const uint16_t* x, const float* smooth, const uint8_t* codes,
                             const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias,
                             int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);

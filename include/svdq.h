@@ -321,10 +321,8 @@ svdq_status svdq_fp4_gemm_lora_up(
  *   w_zeros   device, u8   [N, K/64] z in 0..15
  *   bias      device, bf16 [N] or NULL
  *   M >= 0 (0 is a no-op), N % 32 == 0, K % 64 == 0, group_size == 64, and
- *   the workgroup's LDS (16 rows of codes with their Delta and z, x_hat and
- *   its group sums, a reduction area: 8.75K + K + 2K min(M, 16) + 4096
- *   bytes, rounded) within 160 KB, i.e. K <= 13568 for one token
- *   (NOT_SUPPORTED beyond)
+ *   K <= 16384 for M == 1, K <= 8192 for M <= 4, K <= 4096 for larger M (the
+ *   x_hat staged in LDS per 16-token tile; NOT_SUPPORTED beyond)
  *   y         device out, bf16 [M, N]
  * Built for few tokens (a conditioning vector per image): the packed weights
  * are streamed once per 16 rows of x, codes and x_hat staged in LDS.  Errors as for svdq_w4a4_gemm_lora_up.

@@ -164,7 +164,9 @@ def test_awq_entry_points_argument_errors():
     assert awq(N=48) == NOT_SUPPORTED
     assert awq(K=96) == NOT_SUPPORTED
     assert awq(g=128) == NOT_SUPPORTED
-    assert awq(K=64 * 700) == NOT_SUPPORTED          # mu table beyond the LDS
+    assert awq(K=64 * 700) == NOT_SUPPORTED          # x_hat staging beyond the LDS
+    assert awq(M=1, K=16384 + 64) == NOT_SUPPORTED
+    assert awq(M=5, K=4096 + 64) == NOT_SUPPORTED
     assert awq(M=-1) == INVALID_VALUE
     assert awq(x=None) == INVALID_VALUE
     assert awq(zeros=None) == INVALID_VALUE
@@ -172,6 +174,9 @@ def test_awq_entry_points_argument_errors():
     assert awq(M=0, x=None, zeros=None) == SUCCESS
     if not _gpu_visible():
         assert awq() == NO_DEVICE
+        assert awq(M=1, K=16384) == NO_DEVICE            # the largest staged shapes pass validation
+        assert awq(M=4, K=8192) == NO_DEVICE
+        assert awq(M=40, K=4096) == NO_DEVICE
     buf = ctypes.create_string_buffer(1 << 16)
     p = ctypes.cast(buf, ctypes.c_void_p)
     assert L.svdq_awq_pack_weights(None, p, 4, 8, 64, 64, 20, p, p, p, p, None) == INVALID_VALUE

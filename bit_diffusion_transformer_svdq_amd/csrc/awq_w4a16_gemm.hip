@@ -233,6 +233,10 @@ __global__ __launch_bounds__(kThreads, awq_occupancy(kRowsMax, kKMax)) void awq_
   const int foff = 1024 * wave + 64 * l16 + 8 * (seg & 1);
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
   v4f yacc = zero4;
+  // the two masks in registers (opaque to the compiler), so each nibble pair
+  // costs a shift and one v_and_or_b32 instead of separate and / or with literals
+  u32 kNibs = 0x000F000Fu, kBias = 0x43004300u;
+  __asm__ volatile("" : "+v"(kNibs), "+v"(kBias));
   auto group = [&](const uint8_t* st, int h, int g) {
     const int gr = min(g, G - 1);  // the second group of an odd tail is computed, not added
     const uint4 r0 = xr[8 * gr], r1 = xr[8 * gr + 1];
@@ -245,8 +249,8 @@ __global__ __launch_bounds__(kThreads, awq_occupancy(kRowsMax, kKMax)) void awq_
     v8bf bf[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const v4u b = {(wd[hh] & 0x000F000Fu) | 0x43004300u, ((wd[hh] >> 4) & 0x000F000Fu) | 0x43004300u,
-                     ((wd[hh] >> 8) & 0x000F000Fu) | 0x43004300u, ((wd[hh] >> 12) & 0x000F000Fu) | 0x43004300u};
+      const v4u b = {(wd[hh] & kNibs) | kBias, ((wd[hh] >> 4) & kNibs) | kBias, ((wd[hh] >> 8) & kNibs) | kBias,
+                     ((wd[hh] >> 12) & kNibs) | kBias};
       bf[hh] = __builtin_bit_cast(v8bf, b);
     }
     const v4f acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af0, bf[0], zero4, 0, 0, 0);
@@ -257,7 +261,8 @@ __global__ __launch_bounds__(kThreads, awq_occupancy(kRowsMax, kKMax)) void awq_
     const float cz = -(128.0f + (float)zrow[g]);
     const v4f xs = *reinterpret_cast<const v4f*>(xs_s + 16 * g + 4 * seg);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) yacc[v] = fmaf(dl, fmaf(cz, xs[v], acc[v]), yacc[v]);
+    for (int v = 0; v < (kRowsMax < 4 ? kRowsMax : 4); ++v)  // rows 4 seg + v of A beyond kRowsMax are not stored
+      yacc[v] = fmaf(dl, fmaf(cz, xs[v], acc[v]), yacc[v]);
   };
   for (int i0 = 0; i0 < nch; i0 += kRing) {
 #pragma unroll

@@ -51,10 +51,11 @@ def _check(got, x, b, pk, bias=True):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 64, 32), (3, 192, 96), (16, 256, 64), (17, 320, 96), (40, 1024, 160),
-                                   (2, 6144, 64), (20, 3072, 96)])
+                                   (2, 6144, 64), (20, 3072, 96), (1, 16384, 32), (4, 8192, 64), (5, 4096, 32)])
 def test_awq_small_shapes(M, K, N):
-    """Ragged token tiles, K of one group (three of the four waves idle), and
-    staging that needs more than 64 KB of LDS."""
+    """Ragged token tiles, K of one group (three of the four waves idle), an
+    odd number of groups per wave, and the largest K of each staged class
+    (one token: 16384, up to four: 8192, more: 4096)."""
     spec = S.LinearSpec(f"awq{M}x{K}x{N}", 8, M, K, N, 0, outlier_frac=0.03, outlier_scale=10.0,
                         heavy_tail=True, silu_input=True, layer_id=M + K + N)
     x, b, pk = _case(spec)

@@ -12,15 +12,14 @@
 //
 // These layers see one conditioning vector per image (M = batch), so the
 // kernel is a weight stream: a workgroup owns 16 output channels (one MFMA
-// n-tile) and one tile of up to 16 tokens, and its four waves split K.  The
-// workgroup's 16 rows of codes, and their Delta and z (contiguous in [N, G]
-// layout), go into LDS with global_load_lds_dwordx4, each instruction moving
-// 1 KB (reads of 32-byte pieces of 16 rows per instruction were request-bound
-// at ~1.1 TB/s); piece c of row r sits at slot r P + (c ^ r) within its
-// 16-piece block, which keeps the fragment reads free of bank conflicts.
-// Meanwhile x_hat of the tile's tokens is written to LDS in the operand order
-// below, with the per-group sums xs = sum_{k in g} x_hat; the fp32 partials of
-// the waves are added in wave order through LDS.
+// n-tile) and one tile of up to 16 tokens, and its four waves split K into
+// quarters.  x_hat of the tile's tokens is first written to LDS in the operand
+// order below, with the per-group sums xs = sum_{k in g} x_hat.  The 16 rows'
+// Delta and z then go into LDS by global_load_lds_dwordx4, and each wave
+// streams its quarter of the 16 code rows through a ring of its own: a chunk
+// is 2 groups x 16 rows x 32 bytes = 1 KB, one DMA instruction, three chunks
+// in flight.  The fp32 partials of the waves are added in wave order through
+// LDS.
 //
 // Per group a wave runs two v_mfma_f32_16x16x32_bf16 with A = x_hat and B =
 // 128 + q in bf16: ((w >> 4j) & 0x000F000F) | 0x43004300 turns nibbles j and
@@ -29,8 +28,8 @@
 // product is exact.  The group then adds Delta * (acc - (128 + z) xs).  Lane
 // k-slots: in the group's 64 k, lane segment seg takes k = 16 seg + 8 h +
 // (0..7) for chunk h = 0, 1, so its code bytes are one aligned 8-byte run (32
-// contiguous bytes per row).  Groups go two at a time (independent MFMA
-// chains) with the next two groups' operands read from LDS ahead.
+// contiguous bytes per row).  The two groups of a chunk are independent MFMA
+// chains.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -126,11 +125,10 @@ __global__ __launch_bounds__(kThreads, awq_occupancy(kRowsMax, kKMax)) void awq_
   const int g_hi = ((wave + 1) * G) / kWaves;
   const int nch = (g_hi - g_lo + 1) >> 1;           // chunks of 2 groups
 
-  // 1. Loads, in issue order (vector-memory counters retire in issue order):
-  //    1/s and x of the thread's first two runs (up to 4 token rows); the 16
-  //    rows' Delta and z (contiguous in [N, G] layout, n0 a multiple of 16, so
-  //    both start on a 16-byte boundary); then exactly 3 code chunks of this
-  //    wave, so "at most 3 outstanding" means everything before has landed.
+  // 1. 1/s and x of the thread's first two runs (up to 4 token rows).  The
+  //    LDS DMAs go out after x_hat is staged: while plain loads and LDS DMAs
+  //    are both in flight, the compiler waits for all of them before using a
+  //    loaded value, so DMAs issued first would hold up the staging.
   uint4 xv[2][4];
   v4f sv[2][2];
 #pragma unroll
@@ -142,17 +140,7 @@ __global__ __launch_bounds__(kThreads, awq_occupancy(kRowsMax, kKMax)) void awq_
     for (int rr = 0; rr < 4; ++rr)
       xv[u][rr] = *reinterpret_cast<const uint4*>(a.x + (size_t)(m0 + min(rr, rows - 1)) * a.K + 8 * c);
   }
-  __asm__ volatile("" ::: "memory");  // these small loads go out first
-  // (a fixed count per wave: blocks past the last repeat it, pad lanes the
-  // last slot)
-#pragma unroll
-  for (int t = 0; t < kDzSlots / (64 * kWaves) + (kDzSlots % (64 * kWaves) != 0); ++t) {
-    const int j0 = min(64 * (wave + kWaves * t), dzslots - 64);
-    const int j = min(j0 + lane, 3 * G - 1);
-    const uint8_t* src = j < 2 * G ? reinterpret_cast<const uint8_t*>(a.scales) + (size_t)n0 * G * 2 + 16 * j
-                                   : a.zeros + (size_t)n0 * G + 16 * (j - 2 * G);
-    dma16(src, dz_s + 16 * j0);
-  }
+  __asm__ volatile("" ::: "memory");  // all of them issued before the staging uses the first
   // Chunk i of the wave: groups g_lo + 2i, +1.  Lane l moves 16 bytes to
   // slot l of the wave's 1 KB: row l / 4, position l % 4, which holds piece
   // p = (l % 4) ^ (row / 4 % 4) of the row's 64 bytes (so the fragment reads
@@ -165,9 +153,6 @@ __global__ __launch_bounds__(kThreads, awq_occupancy(kRowsMax, kKMax)) void awq_
     const int g = min(g_lo + 2 * min(i, max(nch - 1, 0)) + (dpiece >> 1), G - 1);
     dma16(dsrc + 32 * g, stage_of(s) + 1024 * wave);
   };
-#pragma unroll
-  for (int s = 0; s < kRing; ++s) dma_chunk(s, s);
-  __asm__ volatile("" ::: "memory");
 
   // 2. x_hat = bf16(fl32(x mu)), mu = fl32(1/s), each run of 8 stored in the
   //    pair order (0,4), (1,5), (2,6), (3,7); xs[g][row] = sum of the group's
@@ -219,10 +204,25 @@ __global__ __launch_bounds__(kThreads, awq_occupancy(kRowsMax, kKMax)) void awq_
     for (int rr = 0; rr < rows; ++rr)
       stage(*reinterpret_cast<const uint4*>(a.x + (size_t)(m0 + rr) * a.K + 8 * c), mu, rr, c);
   }
+  // 3. The 16 rows' Delta and z (contiguous in [N, G] layout; n0 is a
+  //    multiple of 16, so both start on a 16-byte boundary), a fixed count of
+  //    DMAs per wave (blocks past the last repeat it, pad lanes the last
+  //    slot); then exactly 3 code chunks of this wave, so "at most 3
+  //    outstanding" means everything before has landed.
+#pragma unroll
+  for (int t = 0; t < kDzSlots / (64 * kWaves) + (kDzSlots % (64 * kWaves) != 0); ++t) {
+    const int j0 = min(64 * (wave + kWaves * t), dzslots - 64);
+    const int j = min(j0 + lane, 3 * G - 1);
+    const uint8_t* src = j < 2 * G ? reinterpret_cast<const uint8_t*>(a.scales) + (size_t)n0 * G * 2 + 16 * j
+                                   : a.zeros + (size_t)n0 * G + 16 * (j - 2 * G);
+    dma16(src, dz_s + 16 * j0);
+  }
+#pragma unroll
+  for (int s = 0; s < kRing; ++s) dma_chunk(s, s);
   wait_vm<kRing>();  // Delta, z and the x loads of this wave have landed
   __syncthreads();
 
-  // 3. The wave's chunks through the ring: wait for chunk i (the ring is the
+  // 4. The wave's chunks through the ring: wait for chunk i (the ring is the
   //    wave's own, so no barrier), compute its two groups (independent MFMA
   //    chains), refill the stage with chunk i + 3.  Rows of A past the tile's
   //    tokens repeat its last row: their outputs are not stored.
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(kThreads, awq_occupancy(kRowsMax, kKMax)) void awq_
     }
   }
 
-  // 4. partials of the four waves added in wave order, through the wave's own
+  // 5. partials of the four waves added in wave order, through the wave's own
   //    1 KB of ring stage 0 once its DMAs have landed
   wait_vm<0>();
   v4f* red = reinterpret_cast<v4f*>(ring0);

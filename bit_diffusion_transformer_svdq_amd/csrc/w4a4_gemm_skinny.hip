@@ -14,8 +14,8 @@
 // all of K at one wave per SIMD.  Here a workgroup owns 16*N16 weight rows and
 // a chunk of up to 64 tokens, and its 8 waves split K: wave w takes groups
 // [w*G/8, (w+1)*G/8).  Every weight byte is read from HBM once, by one wave,
-// straight into registers (16 rows x 32 bytes per load instruction), with all
-// of the wave's groups in flight when they fit its ring.  The token rows are
+// straight into registers (16 rows x 64 bytes, a group pair, per load
+// instruction), with a ring of 3 pairs in flight.  The token rows are
 // small and shared by every workgroup (L2).  At the end the 8 partial tiles
 // are added in a fixed order through LDS, so results do not depend on timing.
 //

@@ -116,3 +116,77 @@ def test_workspace_growth_during_capture_is_refused():
     torch.cuda.synchronize()
     ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
     assert np.array_equal(c.cpu().numpy(), ref["act_codes"])
+
+
+def test_graph_replays_awq_and_fp4_match_eager():
+    """The AWQ W4A16 linear and both MXFP4 calls inside one captured graph:
+    every replay (with eager work on the stream in between) reproduces the
+    eager outputs bit for bit, and those match the oracle."""
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K
+    import oracle.awq_oracle as A
+    import oracle.mxfp4_oracle as X
+    import synthetic as S
+    # MXFP4 linear, K split over workgroups in call 1 (workspace on the stream)
+    fspec = S.LinearSpec("graph_fp4", 10, 200, 512, 256, 16, outlier_frac=0.02, outlier_scale=30.0,
+                         heavy_tail=True, layer_id=81)
+    fd = S.make_linear(fspec)
+    flam = O.smooth_factors(O.activation_absmax(fd["x"]), fd["w"])
+    fpk = X.pack_weights_fp4(fd["w"], flam, fspec.r)
+    fx, fl = to_dev_bf16(fd["x"]), to_dev(np.asarray(flam, np.float32))
+    fld, flu = to_dev_bf16(fpk["lora_down"]), to_dev_bf16(fpk["lora_up"])
+    fwc, fws, fb = to_dev(fpk["w_codes"]), to_dev(fpk["w_scales"]), to_dev_bf16(fd["bias"])
+    fq = (torch.empty((200, 256), dtype=torch.uint8, device="cuda"),
+          torch.empty((200, 16), dtype=torch.uint8, device="cuda"),
+          torch.empty((200, 16), dtype=torch.bfloat16, device="cuda"))
+    fy = torch.empty((200, 256), dtype=torch.bfloat16, device="cuda")
+    # AWQ linear at one and at four tokens
+    aspec = S.LinearSpec("graph_awq", 8, 4, 1024, 256, 0, outlier_frac=0.03, outlier_scale=10.0,
+                         heavy_tail=True, silu_input=True, layer_id=82)
+    ax, aw = S.make_x(aspec), S.make_w(aspec)
+    apk = A.awq_pack(S.make_calibration(aspec, 16), aw)
+    adev = [to_dev(np.asarray(apk["smooth"], np.float32)), to_dev(apk["codes"]), to_dev_bf16(apk["scales"]),
+            to_dev(apk["zeros"]), to_dev_bf16(S.make_bias(aspec))]
+    ax4, ax1 = to_dev_bf16(ax), to_dev_bf16(ax[:1])
+    ay4 = torch.empty((4, 256), dtype=torch.bfloat16, device="cuda")
+    ay1 = torch.empty((1, 256), dtype=torch.bfloat16, device="cuda")
+    outs = (*fq, fy, ay4, ay1)
+    s = torch.cuda.Stream()
+
+    def chain():
+        c, sc, la = K.quantize_act_lora_down_fp4(fx, fl, fld, out=fq)
+        K.fp4_gemm_lora_up(c, sc, fwc, fws, la, flu, fb, out=fy)
+        K.awq_w4a16_gemm(ax4, *adev, out=ay4)
+        K.awq_w4a16_gemm(ax1, *adev, out=ay1)
+
+    K.debug_set_quant_plan(2, 0)
+    try:
+        with torch.cuda.stream(s):
+            chain()
+        torch.cuda.synchronize()
+        want = [t.clone() for t in outs]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            chain()
+        torch.cuda.synchronize()
+        for rep in range(3):
+            with torch.cuda.stream(s):
+                for t in outs:
+                    t.zero_()
+                chain()
+                for t in outs:
+                    t.fill_(7)
+                g.replay()
+            torch.cuda.synchronize()
+            for got, w in zip(outs, want):
+                assert torch.equal(got, w), rep
+    finally:
+        K.debug_set_quant_plan(0, 0)
+    ref = X.quantize_act_lora_down_fp4(fd["x"], flam, fpk["lora_down"])
+    assert np.array_equal(fq[0].cpu().numpy(), ref["act_codes"])
+    assert np.array_equal(fq[1].cpu().numpy(), ref["act_scales"])
+    want4, _ = A.awq_linear(ax, apk["smooth"], apk["codes"], apk["scales"], apk["zeros"], S.make_bias(aspec))
+    from tests.gpu_util import Y_MAX_ABS, Y_REL_FRO, bf16_bits, y_errors
+    rel, mx = y_errors(bf16_bits(ay4), want4)
+    assert rel <= Y_REL_FRO and mx <= Y_MAX_ABS, (rel, mx)
+    assert torch.equal(ay1[0], ay4[0])

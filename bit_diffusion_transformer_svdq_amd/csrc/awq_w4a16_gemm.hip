@@ -46,14 +46,12 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned int u32;
 typedef u32 v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kWaves = 4;                // waves per n-tile (they split K)
 constexpr int kRing = 3;                 // code chunks in flight per wave
-constexpr int kRingStage = 1024 * kWaves;  // one chunk of each wave
 // workgroups per CU an instance fits in (LDS), at most 5 (registers)
-constexpr int awq_occupancy(int rows, int kmax) {
+constexpr int awq_occupancy(int rows, int kmax, int tiles) {
   const int g = kmax / 64;
-  const int lds = kRing * kRingStage + 16 * ((3 * g + 63) & ~63) + 64 * g + 2 * rows * kmax;
+  const int lds = tiles * (kRing * 1024 * kWaves + 16 * ((3 * g + 63) & ~63)) + 64 * g + 2 * rows * kmax;
   return 160 * 1024 / lds < 5 ? 160 * 1024 / lds : 5;
 }
 
@@ -91,38 +89,48 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
                                    (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
 
-// kRowsMax x kKMax: the largest token tile and K the instance stages.  Every
-// LDS area is a static object: the compiler then tracks which of them a DMA
-// in flight writes, and waits only for the ring stage a read depends on (an
-// access to dynamic LDS would wait for every DMA in flight).
-template <int kRowsMax, int kKMax>
-__global__ __launch_bounds__(kThreads, awq_occupancy(kRowsMax, kKMax)) void awq_w4a16_kernel(const AwqArgs a) {
+// kRowsMax x kKMax: the largest token tile and K the instance stages;
+// kTiles: n-tiles per workgroup, each served by its own 4 waves, all sharing
+// the staged x_hat (several tiles per workgroup let a grid with more tiles
+// than one wave of workgroups run in one).  Every LDS area is a static
+// object: the compiler then tracks which of them a DMA in flight writes, and
+// waits only for the ring stage a read depends on (an access to dynamic LDS
+// would wait for every DMA in flight).
+template <int kRowsMax, int kKMax, int kTiles>
+__global__ __launch_bounds__(64 * kWaves * kTiles, awq_occupancy(kRowsMax, kKMax, kTiles))
+void awq_w4a16_kernel(const AwqArgs a) {
+  constexpr int kThr = 64 * kWaves * kTiles;
   constexpr int kGMax = kKMax / 64;
   constexpr int kDzSlots = (3 * kGMax + 63) & ~63;  // Delta + z, whole 1 KB blocks
+  constexpr int kRingStage = 1024 * kWaves * kTiles;
   // Code ring: stage s holds, for each wave w, one chunk (2 groups x 16 rows
   // x 32 bytes = 1 KB) at 1024 w.
   __shared__ __attribute__((aligned(16))) uint8_t ring0[kRingStage], ring1[kRingStage], ring2[kRingStage];
-  __shared__ __attribute__((aligned(16))) uint8_t dz_s[16 * kDzSlots];       // [16][G] Delta, [16][G] z
-  __shared__ __attribute__((aligned(16))) float xs_s[16 * kGMax];            // [G][16] sum x_hat
-  __shared__ __attribute__((aligned(16))) uint4 xh_s[kRowsMax * kKMax / 8];  // [rows][K/8]
+  __shared__ __attribute__((aligned(16))) uint8_t dz_s[kTiles * 16 * kDzSlots];  // per tile [16][G] Delta, z
+  __shared__ __attribute__((aligned(16))) float xs_s[16 * kGMax];                 // [G][16] sum x_hat
+  __shared__ __attribute__((aligned(16))) uint4 xh_s[kRowsMax * kKMax / 8];       // [rows][K/8]
   auto stage_of = [&](int s) -> uint8_t* { return s == 0 ? ring0 : s == 1 ? ring1 : ring2; };
   static_assert(kRing == 3, "one LDS object per ring stage");
-
-  const int G = a.G;
-  const int dzslots = (3 * G + 63) & ~63;
-  const uint16_t* d_s = reinterpret_cast<const uint16_t*>(dz_s);
-  const uint8_t* z_s = dz_s + 32 * G;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tg = wave / kWaves, wq = wave % kWaves;  // n-tile of the workgroup, K quarter
   const int l16 = lane & 15, seg = lane >> 4;
-  const int n0 = blockIdx.x * 16;
+  const int n0u = (blockIdx.x * kTiles + tg) * 16;   // past N only in a last, partial workgroup
+  const bool tile_ok = n0u < a.N;
+  const int n0 = tile_ok ? n0u : a.N - 16;           // loads of a missing tile repeat the last one
   const int m0 = blockIdx.y * 16;
   const int rows = min(a.rows, a.M - m0);
   const int runs = a.K >> 3;
-  const int g_lo = (wave * G) / kWaves;             // groups [g_lo, g_hi) of this wave
-  const int g_hi = ((wave + 1) * G) / kWaves;
+
+  const int G = a.G;
+  const int dzslots = (3 * G + 63) & ~63;
+  uint8_t* dzt = dz_s + tg * 16 * kDzSlots;
+  const uint16_t* d_s = reinterpret_cast<const uint16_t*>(dzt);
+  const uint8_t* z_s = dzt + 32 * G;
+  const int g_lo = (wq * G) / kWaves;               // groups [g_lo, g_hi) of this wave
+  const int g_hi = ((wq + 1) * G) / kWaves;
   const int nch = (g_hi - g_lo + 1) >> 1;           // chunks of 2 groups
 
   // 1. 1/s and x of the thread's first two runs (up to 4 token rows).  The
@@ -133,7 +141,7 @@ __global__ __launch_bounds__(kThreads, awq_occupancy(kRowsMax, kKMax)) void awq_
   v4f sv[2][2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int c = min(tid + u * kThreads, runs - 1);
+    const int c = min(tid + u * kThr, runs - 1);
     sv[u][0] = *reinterpret_cast<const v4f*>(a.smooth + 8 * c);
     sv[u][1] = *reinterpret_cast<const v4f*>(a.smooth + 8 * c + 4);
 #pragma unroll
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(kThreads, awq_occupancy(kRowsMax, kKMax)) void awq_
   };
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int c = tid + u * kThreads;
+    const int c = tid + u * kThr;
     if (c < runs) {  // uniform over each aligned 8 lanes
       float mu[8];
       recip(sv[u][0], sv[u][1], mu);
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(kThreads, awq_occupancy(kRowsMax, kKMax)) void awq_
         stage(*reinterpret_cast<const uint4*>(a.x + (size_t)(m0 + rr) * a.K + 8 * c), mu, rr, c);
     }
   }
-  for (int c = tid + 2 * kThreads; c < runs; c += kThreads) {  // K > 4096
+  for (int c = tid + 2 * kThr; c < runs; c += kThr) {  // more than two runs per thread
     float mu[8];
     recip(*reinterpret_cast<const v4f*>(a.smooth + 8 * c), *reinterpret_cast<const v4f*>(a.smooth + 8 * c + 4), mu);
     for (int rr = 0; rr < rows; ++rr)
@@ -211,11 +219,11 @@ __global__ __launch_bounds__(kThreads, awq_occupancy(kRowsMax, kKMax)) void awq_
   //    outstanding" means everything before has landed.
 #pragma unroll
   for (int t = 0; t < kDzSlots / (64 * kWaves) + (kDzSlots % (64 * kWaves) != 0); ++t) {
-    const int j0 = min(64 * (wave + kWaves * t), dzslots - 64);
+    const int j0 = min(64 * (wq + kWaves * t), dzslots - 64);
     const int j = min(j0 + lane, 3 * G - 1);
     const uint8_t* src = j < 2 * G ? reinterpret_cast<const uint8_t*>(a.scales) + (size_t)n0 * G * 2 + 16 * j
                                    : a.zeros + (size_t)n0 * G + 16 * (j - 2 * G);
-    dma16(src, dz_s + 16 * j0);
+    dma16(src, dzt + 16 * j0);
   }
 #pragma unroll
   for (int s = 0; s < kRing; ++s) dma_chunk(s, s);
@@ -285,16 +293,16 @@ __global__ __launch_bounds__(kThreads, awq_occupancy(kRowsMax, kKMax)) void awq_
     }
   }
 
-  // 5. partials of the four waves added in wave order, through the wave's own
-  //    1 KB of ring stage 0 once its DMAs have landed
+  // 5. partials of each tile's four waves added in wave order, through the
+  //    wave's own 1 KB of ring stage 0 once its DMAs have landed
   wait_vm<0>();
   v4f* red = reinterpret_cast<v4f*>(ring0);
   red[wave * 64 + lane] = yacc;
   __syncthreads();
-  if (wave == 0) {
-    v4f sum = red[lane];
+  if (wq == 0 && tile_ok) {
+    v4f sum = red[wave * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) sum += red[w * 64 + lane];
+    for (int w = 1; w < kWaves; ++w) sum += red[(wave + w) * 64 + lane];
     const int n = n0 + l16;
     const float b = a.bias ? __builtin_bit_cast(float, (u32)a.bias[n] << 16) : 0.f;
 #pragma unroll
@@ -305,16 +313,21 @@ __global__ __launch_bounds__(kThreads, awq_occupancy(kRowsMax, kKMax)) void awq_
   }
 }
 
-// instances: (token rows, K) classes, smallest first
+// instances: (token rows, K) classes, smallest first, one n-tile per
+// workgroup; up to four tokens with K <= 3072 also with three n-tiles per
+// workgroup, for grids that one tile per workgroup would run in more than one
+// wave of workgroups
 struct AwqClass {
-  int rows, kmax;
+  int rows, kmax, tiles;
   void (*kernel)(AwqArgs);
 };
 constexpr AwqClass kClasses[] = {
-    {1, 4096, awq_w4a16_kernel<1, 4096>},   {1, 16384, awq_w4a16_kernel<1, 16384>},
-    {4, 4096, awq_w4a16_kernel<4, 4096>},   {4, 8192, awq_w4a16_kernel<4, 8192>},
-    {16, 4096, awq_w4a16_kernel<16, 4096>},
+    {1, 4096, 1, awq_w4a16_kernel<1, 4096, 1>},  {1, 16384, 1, awq_w4a16_kernel<1, 16384, 1>},
+    {4, 4096, 1, awq_w4a16_kernel<4, 4096, 1>},  {4, 8192, 1, awq_w4a16_kernel<4, 8192, 1>},
+    {16, 4096, 1, awq_w4a16_kernel<16, 4096, 1>},
 };
+constexpr AwqClass kWide = {4, 3072, 3, awq_w4a16_kernel<4, 3072, 3>};
+constexpr int kCus = 256;
 const AwqClass* awq_class(int64_t K, int64_t rows) {
   for (const AwqClass& c : kClasses)
     if (rows <= c.rows && K <= c.kmax) return &c;
@@ -332,8 +345,13 @@ hipError_t launch_awq_w4a16(const uint16_t* x, const float* smooth, const uint8_
   AwqArgs a{x, smooth, codes, scales, zeros, bias, y, (int)M, (int)N, (int)K, (int)(K / 64), rows};
   const AwqClass* c = awq_class(K, rows);
   if (!c) return hipErrorInvalidValue;  // excluded by the caller's awq_supported check
-  const dim3 grid((unsigned)((N + 15) / 16), (unsigned)((M + 15) / 16));
-  hipLaunchKernelGGL(c->kernel, grid, dim3(kThreads), 0, stream, a);
+  const int64_t ntiles = N / 16, mtiles = (M + 15) / 16;
+  if (rows > 1 && rows <= kWide.rows && K <= kWide.kmax &&
+      ntiles * mtiles > (int64_t)awq_occupancy(c->rows, c->kmax, 1) * kCus &&
+      (ntiles + kWide.tiles - 1) / kWide.tiles * mtiles <= (int64_t)awq_occupancy(4, 3072, 3) * kCus)
+    c = &kWide;
+  const dim3 grid((unsigned)((ntiles + c->tiles - 1) / c->tiles), (unsigned)mtiles);
+  hipLaunchKernelGGL(c->kernel, grid, dim3(64 * kWaves * c->tiles), 0, stream, a);
   return hipGetLastError();
 }
 

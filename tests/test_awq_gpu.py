@@ -63,11 +63,22 @@ def test_awq_small_shapes(M, K, N):
     _check(_run(x, b, pk, bias=False), x, b, pk, bias=False)
 
 
-@pytest.mark.parametrize("name,M", [("mod_double", 1), ("mod_single", 4), ("mod_final", 2)])
+@pytest.mark.parametrize("name,M", [("mod_double", 1), ("mod_single", 4), ("mod_final", 2), ("mod_double", 4),
+                                    ("mod_double", 3)])
 def test_awq_modulation_shapes(name, M):
     """The modulation projections of a 12B DiT at their full size (3072 ->
-    18432 / 9216 / 6144) for 1, 2 and 4 images."""
+    18432 / 9216 / 6144) for 1 to 4 images (3072 -> 18432 at 3 and 4 images
+    runs three n-tiles per workgroup)."""
     spec = S.MOD_SPECS[name].with_m(M)
+    x, b, pk = _case(spec, search=False)
+    _check(_run(x, b, pk), x, b, pk)
+
+
+def test_awq_three_tiles_per_workgroup_ragged():
+    """770 n-tiles at 3 per workgroup: the last workgroup has a missing tile
+    (its loads repeat the last tile, nothing is stored for it)."""
+    spec = S.LinearSpec("awq_wide", 8, 2, 3072, 12320, 0, outlier_frac=0.03, outlier_scale=10.0,
+                        heavy_tail=True, silu_input=True, layer_id=91)
     x, b, pk = _case(spec, search=False)
     _check(_run(x, b, pk), x, b, pk)
 

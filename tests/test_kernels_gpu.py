@@ -3,7 +3,7 @@
 Bar: activation codes, activation scales and the int32 group accumulators are
 bit-exact; lora_act is within one bf16 ulp (fp32 vs float64 summation order);
 Y is within relative Frobenius 5e-3 and max-abs 1e-2 * max|Y*| of the float64
-oracle.  Weights are packed by the oracle, so the kernels are judged on the
+oracle.  Weights are packed by the oracle, so the kernels are checked on the
 oracle's own inputs; the C++ packer is checked separately on the CPU.
 """
 import numpy as np

@@ -507,7 +507,12 @@ size_t lds_bytes(int GB, int NT) { return (size_t)GB * NT * 2048; }  // dynamic 
 //  - with K split, each row tile's fp32 partial is written and read back
 //    through the last-level cache: ~NT per tile, at half weight;
 //  - the workgroup's prologue (lambda, reciprocals, barrier): ~1;
-// times the number of workgroups that share a compute unit.
+// times the number of workgroups that share a compute unit; plus, with more
+// than 8 K-blocks, the last wave of each row tile adding the tile's KB
+// partials (NT fragments each) on the critical path: 0.2 per fragment.
+// Without that term a few hundred tokens got 24-192 K-blocks of a single
+// group, and call 1 took 12-40 us where 16-48 blocks of 2-4 groups take
+// 9-16 us.
 Plan make_plan(int T, int G, int NT, int cus) {
   const int GB0 = std::min(G, 8);
   Plan best{1, GB0, (G + GB0 - 1) / GB0, T, lds_bytes(GB0, NT)};
@@ -525,7 +530,8 @@ Plan make_plan(int T, int G, int NT, int cus) {
       const double mem = (double)TB * GB;
       const double valu = 3.5 * ((TB + 3) / 4) * GB;
       const double lora = 0.5 * GB * NT + (KB > 1 ? 0.5 * TB * NT : 0.0);
-      const double cost = per_cu * (std::max(mem, valu) + lora + 1.0);
+      const double reduce = KB > 8 ? 0.2 * KB * NT : 0.0;
+      const double cost = per_cu * (std::max(mem, valu) + lora + 1.0) + reduce;
       if (cost < best_cost - 1e-9) {
         best_cost = cost;
         best = Plan{TB, GB, KB, nrb, lds};

@@ -51,7 +51,8 @@ def _check(got, x, b, pk, bias=True):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 64, 32), (3, 192, 96), (16, 256, 64), (17, 320, 96), (40, 1024, 160),
-                                   (2, 6144, 64), (20, 3072, 96), (1, 16384, 32), (4, 8192, 64), (5, 4096, 32)])
+                                   (2, 6144, 64), (20, 3072, 96), (1, 16384, 32), (4, 8192, 64), (5, 4096, 32),
+                                   (1, 320, 96), (1, 4096, 64)])
 def test_awq_small_shapes(M, K, N):
     """Ragged token tiles, K of one group (three of the four waves idle), an
     odd number of groups per wave, and the largest K of each staged class
@@ -64,7 +65,7 @@ def test_awq_small_shapes(M, K, N):
 
 
 @pytest.mark.parametrize("name,M", [("mod_double", 1), ("mod_single", 4), ("mod_final", 2), ("mod_double", 4),
-                                    ("mod_double", 3)])
+                                    ("mod_double", 3), ("mod_single", 1), ("mod_final", 1)])
 def test_awq_modulation_shapes(name, M):
     """The modulation projections of a 12B DiT at their full size (3072 ->
     18432 / 9216 / 6144) for 1 to 4 images (3072 -> 18432 at 3 and 4 images

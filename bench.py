@@ -426,6 +426,38 @@ def measure_awq(batch, steps=20, warmup=5, calib_rows=16):
                     "hbm_frac_graph": byts / t_graph / 1e9 / HBM_PEAK_GBS})
     except Exception as e:
         out["graph_error"] = f"{type(e).__name__}: {e}"
+    # the same 77 projections as 3 stacked launches (every projection of one
+    # shape reads the same conditioning vector): one weight buffer per shape
+    # holding all of its layers, as a loader would lay them out
+    stacks = []
+    for name in ("mod_double", "mod_single", "mod_final"):
+        Ls = [L for L in layers if L["name"] == name]
+        src = packs[name]
+        stacks.append(dict(x=src["x"], smooth=torch.stack([L["smooth"] for L in Ls]),
+                           codes=torch.stack([L["codes"] for L in Ls]), scales=torch.stack([L["scales"] for L in Ls]),
+                           zeros=torch.stack([L["zeros"] for L in Ls]), bias=torch.stack([L["bias"] for L in Ls]),
+                           y=torch.empty((len(Ls), batch, src["spec"].N), dtype=torch.bfloat16, device=dev)))
+
+    def step_stacked():
+        for st in stacks:
+            K.awq_w4a16_gemm_stacked(st["x"], st["smooth"], st["codes"], st["scales"], st["zeros"], st["bias"],
+                                     out=st["y"], stream=stream)
+
+    t_st = timed(step_stacked, steps)
+    # the stacked 38 x 3072 -> 18432 launch alone, HIP events on the launch stream
+    with torch.cuda.stream(stream):
+        evs[0].record(stream)
+        for _ in range(10):
+            st = stacks[0]
+            K.awq_w4a16_gemm_stacked(st["x"], st["smooth"], st["codes"], st["scales"], st["zeros"], st["bias"],
+                                     out=st["y"], stream=stream)
+        evs[1].record(stream)
+    torch.cuda.synchronize()
+    t_st0 = evs[0].elapsed_time(evs[1]) * 1e-3 / 10
+    b_st0 = 38 * b_double
+    out.update({"launches_stacked": len(stacks), "ms_stacked": t_st * 1e3, "GB/s_stacked": byts / t_st / 1e9,
+                "hbm_frac_stacked": byts / t_st / 1e9 / HBM_PEAK_GBS,
+                "us_stacked_38x3072x18432": t_st0 * 1e6, "GB/s_stacked_38x3072x18432": b_st0 / t_st0 / 1e9})
     return out
 
 

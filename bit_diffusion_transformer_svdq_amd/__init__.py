@@ -23,7 +23,8 @@ from ._lib import SvdqError, check, lib
 
 __all__ = ["SvdqError", "lib", "check_device", "quantize_act_lora_down", "w4a4_gemm_lora_up",
            "mlp_pair", "w4a4_gemm_qkv_norm_rope", "w4a4_group_acc_debug", "debug_set_quant_plan", "debug_set_gemm_path", "debug_set_gemm_splits",
-           "EPILOGUES", "smooth_from_absmax", "pack_weights", "awq_w4a16_gemm", "awq_pack_weights",
+           "EPILOGUES", "smooth_from_absmax", "pack_weights", "awq_w4a16_gemm", "awq_w4a16_gemm_stacked",
+           "awq_pack_weights",
            "quantize_act_lora_down_fp4", "fp4_gemm_lora_up", "pack_weights_fp4",
            "GROUP_SIZE"]
 
@@ -289,6 +290,26 @@ def awq_w4a16_gemm(x, smooth, w_codes, w_scales, w_zeros, bias=None, out=None, s
     st = lib().svdq_awq_w4a16_gemm(_ptr(x), _ptr(smooth), _ptr(w_codes), _ptr(w_scales), _ptr(w_zeros),
                                    _ptr(bias), M, N, K, GROUP_SIZE, _ptr(y), _stream(stream))
     check(st, "svdq_awq_w4a16_gemm")
+    return y
+
+
+def awq_w4a16_gemm_stacked(x, smooth, w_codes, w_scales, w_zeros, bias=None, out=None, stream=None):
+    """L AWQ W4A16 linears sharing x: x bf16 [M, K], smooth fp32 [L, K], codes u8 [L, N, K/2],
+    scales bf16 [L, N, K/64], zeros u8 [L, N, K/64], bias bf16 [L, N] or None -> Y bf16 [L, M, N]."""
+    torch = _torch()
+    M, K = x.shape
+    L, N = w_codes.shape[0], w_codes.shape[1]
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(smooth, torch.float32, (L, K), "smooth")
+    _need(w_codes, torch.uint8, (L, N, K // 2), "w_codes")
+    _need(w_scales, torch.bfloat16, (L, N, K // GROUP_SIZE), "w_scales")
+    _need(w_zeros, torch.uint8, (L, N, K // GROUP_SIZE), "w_zeros")
+    if bias is not None:
+        _need(bias, torch.bfloat16, (L, N), "bias")
+    y = torch.empty((L, M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    st = lib().svdq_awq_w4a16_gemm_stacked(_ptr(x), _ptr(smooth), _ptr(w_codes), _ptr(w_scales), _ptr(w_zeros),
+                                           _ptr(bias), L, M, N, K, GROUP_SIZE, _ptr(y), _stream(stream))
+    check(st, "svdq_awq_w4a16_gemm_stacked")
     return y
 
 

@@ -48,6 +48,9 @@ SIGNATURES = {
     "svdq_awq_w4a16_gemm": (ctypes.c_int, [
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64,
         _c_void_p, _c_void_p]),
+    "svdq_awq_w4a16_gemm_stacked": (ctypes.c_int, [
+        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _i64,
+        _c_void_p, _c_void_p]),
     "svdq_w4a4_group_acc_debug": (ctypes.c_int, [
         _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p]),
     "svdq_smooth_from_absmax": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p]),

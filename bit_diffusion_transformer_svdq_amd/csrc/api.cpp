@@ -296,19 +296,21 @@ svdq_status svdq_fp4_gemm_lora_up(const void* act_codes, const void* act_scales,
   return ok();
 }
 
-svdq_status svdq_awq_w4a16_gemm(const void* x, const float* smooth, const void* w_codes,
-                               const void* w_scales, const void* w_zeros, const void* bias, int64_t M,
-                               int64_t N, int64_t K, int64_t group_size, void* y, void* stream) {
-  if (M < 0 || N <= 0 || K <= 0 || group_size <= 0)
-    return fail(SVDQ_STATUS_INVALID_VALUE, "bad dims M=%lld N=%lld K=%lld group_size=%lld", (long long)M,
-                (long long)N, (long long)K, (long long)group_size);
+namespace {
+// the AWQ linear, one or L stacked layers sharing x
+svdq_status awq_call(const void* x, const float* smooth, const void* w_codes, const void* w_scales,
+                     const void* w_zeros, const void* bias, int64_t L, int64_t M, int64_t N, int64_t K,
+                     int64_t group_size, void* y, void* stream) {
+  if (L < 0 || M < 0 || N <= 0 || K <= 0 || group_size <= 0)
+    return fail(SVDQ_STATUS_INVALID_VALUE, "bad dims L=%lld M=%lld N=%lld K=%lld group_size=%lld", (long long)L,
+                (long long)M, (long long)N, (long long)K, (long long)group_size);
   if (group_size != 64) return fail(SVDQ_STATUS_NOT_SUPPORTED, "group_size %lld (only 64)", (long long)group_size);
   if (K % 64 != 0) return fail(SVDQ_STATUS_NOT_SUPPORTED, "K=%lld is not a multiple of 64", (long long)K);
   if (N % 32 != 0) return fail(SVDQ_STATUS_NOT_SUPPORTED, "N=%lld is not a multiple of 32", (long long)N);
-  if (M > (1ll << 20) || N > (1ll << 20) || (M > 0 && !svdq::awq_supported(K, M)))
-    return fail(SVDQ_STATUS_NOT_SUPPORTED, "problem too large M=%lld N=%lld K=%lld", (long long)M,
-                (long long)N, (long long)K);
-  if (M == 0) return ok();
+  if (L > 65535 || M > (1ll << 20) || N > (1ll << 20) || (M > 0 && !svdq::awq_supported(K, M)))
+    return fail(SVDQ_STATUS_NOT_SUPPORTED, "problem too large L=%lld M=%lld N=%lld K=%lld", (long long)L,
+                (long long)M, (long long)N, (long long)K);
+  if (M == 0 || L == 0) return ok();
   if (!x || !smooth || !w_codes || !w_scales || !w_zeros || !y)
     return fail(SVDQ_STATUS_INVALID_VALUE, "null x/smooth/w_codes/w_scales/w_zeros/y");
   if (!aligned16(x) || !aligned16(smooth) || !aligned16(w_codes) || !aligned16(w_scales) ||
@@ -319,9 +321,23 @@ svdq_status svdq_awq_w4a16_gemm(const void* x, const float* smooth, const void* 
   hipError_t e = svdq::launch_awq_w4a16(
       static_cast<const uint16_t*>(x), smooth, static_cast<const uint8_t*>(w_codes),
       static_cast<const uint16_t*>(w_scales), static_cast<const uint8_t*>(w_zeros),
-      static_cast<const uint16_t*>(bias), M, N, K, static_cast<uint16_t*>(y), static_cast<hipStream_t>(stream));
+      static_cast<const uint16_t*>(bias), L, M, N, K, static_cast<uint16_t*>(y), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SVDQ_STATUS_HIP_ERROR, "awq launch: %s", hipGetErrorString(e));
   return ok();
+}
+}  // namespace
+
+svdq_status svdq_awq_w4a16_gemm(const void* x, const float* smooth, const void* w_codes,
+                               const void* w_scales, const void* w_zeros, const void* bias, int64_t M,
+                               int64_t N, int64_t K, int64_t group_size, void* y, void* stream) {
+  return awq_call(x, smooth, w_codes, w_scales, w_zeros, bias, 1, M, N, K, group_size, y, stream);
+}
+
+svdq_status svdq_awq_w4a16_gemm_stacked(const void* x, const float* smooth, const void* w_codes,
+                                       const void* w_scales, const void* w_zeros, const void* bias,
+                                       int64_t L, int64_t M, int64_t N, int64_t K, int64_t group_size,
+                                       void* y, void* stream) {
+  return awq_call(x, smooth, w_codes, w_scales, w_zeros, bias, L, M, N, K, group_size, y, stream);
 }
 
 svdq_status svdq_w4a4_group_acc_debug(const void* act_codes, const void* w_codes, int64_t M,

@@ -98,8 +98,20 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
 // would wait for every DMA in flight).
 template <int kRowsMax, int kKMax, int kTiles>
 __global__ __launch_bounds__(64 * kWaves * kTiles, awq_occupancy(kRowsMax, kKMax, kTiles))
-void awq_w4a16_kernel(const AwqArgs a) {
+void awq_w4a16_kernel(const AwqArgs args) {
   constexpr int kThr = 64 * kWaves * kTiles;
+  // layer blockIdx.z of a stack of L linears that share x: its own 1/s,
+  // codes, Delta, z, bias and output, at fixed strides
+  AwqArgs a = args;
+  {
+    const size_t l = blockIdx.z, N = (size_t)args.N, K = (size_t)args.K, G = (size_t)args.G;
+    a.smooth += l * K;
+    a.codes += l * N * (K / 2);
+    a.scales += l * N * G;
+    a.zeros += l * N * G;
+    if (a.bias) a.bias += l * N;
+    a.y += l * (size_t)args.M * N;
+  }
   constexpr int kGMax = kKMax / 64;
   constexpr int kDzSlots = (3 * kGMax + 63) & ~63;  // Delta + z, whole 1 KB blocks
   constexpr int kRingStage = 1024 * kWaves * kTiles;
@@ -340,7 +352,7 @@ bool awq_supported(int64_t K, int64_t M) { return awq_class(K, std::min<int64_t>
 
 hipError_t launch_awq_w4a16(const uint16_t* x, const float* smooth, const uint8_t* codes,
                             const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias,
-                            int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+                            int64_t L, int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
   const int rows = (int)std::min<int64_t>(16, M);
   AwqArgs a{x, smooth, codes, scales, zeros, bias, y, (int)M, (int)N, (int)K, (int)(K / 64), rows};
   const AwqClass* c = awq_class(K, rows);
@@ -350,7 +362,7 @@ hipError_t launch_awq_w4a16(const uint16_t* x, const float* smooth, const uint8_
       ntiles * mtiles > (int64_t)awq_occupancy(c->rows, c->kmax, 1) * kCus &&
       (ntiles + kWide.tiles - 1) / kWide.tiles * mtiles <= (int64_t)awq_occupancy(4, 3072, 3) * kCus)
     c = &kWide;
-  const dim3 grid((unsigned)((ntiles + c->tiles - 1) / c->tiles), (unsigned)mtiles);
+  const dim3 grid((unsigned)((ntiles + c->tiles - 1) / c->tiles), (unsigned)mtiles, (unsigned)L);
   hipLaunchKernelGGL(c->kernel, grid, dim3(64 * kWaves * c->tiles), 0, stream, a);
   return hipGetLastError();
 }

@@ -98,10 +98,13 @@ void set_gemm_path_override(int path);
 // zero points per 64-wide group).  Shapes validated by the caller: M > 0,
 // N % 32 == 0, K % 64 == 0, awq_supported(K, M): K <= 16384 for M == 1,
 // K <= 8192 for M <= 4, K <= 4096 otherwise (the LDS the instances stage).
+// L linears stacked at fixed strides (smooth [L][K], codes [L][N][K/2],
+// scales and zeros [L][N][K/64], bias [L][N], y [L][M][N]) share x; L >= 1,
+// L <= 65535.
 bool awq_supported(int64_t K, int64_t M);
 hipError_t launch_awq_w4a16(const uint16_t* x, const float* smooth, const uint8_t* codes,
                             const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias,
-                            int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
+                            int64_t L, int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
 
 // Test hook: K-splits per tile of the tiled kernel (0 = choose by shape;
 // clipped to the number of group pairs; ignored for the QKV epilogue).

@@ -333,6 +333,31 @@ svdq_status svdq_awq_w4a16_gemm(
     void* y, void* stream);
 
 /*
+ * L AWQ W4A16 linears of the same shape that take the same input, in one
+ * launch: Y_l = the linear above with layer l's smoothing vector, codes,
+ * Delta, z and bias, for l = 0..L-1.  The modulation projections of a
+ * diffusion transformer are such a set: every block's adaptive-normalization
+ * projection reads the same conditioning vector (mind-verse.de, section
+ * "Nunchaku Lite: Nahtlose Integration in Diffusers", modulation layers kept
+ * at awq_w4a16), so a step's projections of one shape can run together
+ * instead of one launch per block.  Every layer's result is bit-identical to
+ * svdq_awq_w4a16_gemm on that layer's arrays.
+ *   x         device, bf16 [M, K]            shared by all layers
+ *   smooth    device, fp32 [L, K]
+ *   w_codes   device, u8   [L, N, K/2]
+ *   w_scales  device, bf16 [L, N, K/64]
+ *   w_zeros   device, u8   [L, N, K/64]
+ *   bias      device, bf16 [L, N] or NULL
+ *   y         device out, bf16 [L, M, N]
+ *   0 <= L <= 65535 (0 is a no-op, above NOT_SUPPORTED); M, N, K and
+ *   group_size as for svdq_awq_w4a16_gemm.  Errors as for that call.
+ */
+svdq_status svdq_awq_w4a16_gemm_stacked(
+    const void* x, const float* smooth, const void* w_codes, const void* w_scales,
+    const void* w_zeros, const void* bias, int64_t L, int64_t M, int64_t N, int64_t K,
+    int64_t group_size, void* y, void* stream);
+
+/*
  * Host-side packer, step 1: the smoothing vector (mind-verse.de, section
  * "Nunchaku und SVDQuant": outliers of the activations are shifted into the
  * weights).  lambda_j = fl32(sqrt(max(a_j, 1e-5) / max(max_n |W_nj|, 1e-5))),

@@ -177,6 +177,20 @@ def test_awq_entry_points_argument_errors():
         assert awq(M=1, K=16384) == NO_DEVICE            # the largest staged shapes pass validation
         assert awq(M=4, K=8192) == NO_DEVICE
         assert awq(M=40, K=4096) == NO_DEVICE
+
+    def stacked(Ls=3, M=4, N=64, K=256, g=64, x=FAKE, bias=FAKE):
+        return L.svdq_awq_w4a16_gemm_stacked(x, FAKE, FAKE, FAKE, FAKE, bias, Ls, M, N, K, g, FAKE, None)
+    assert stacked(Ls=-1) == INVALID_VALUE
+    assert stacked(Ls=65536) == NOT_SUPPORTED
+    assert stacked(N=48) == NOT_SUPPORTED
+    assert stacked(M=5, K=4096 + 64) == NOT_SUPPORTED
+    assert stacked(x=None) == INVALID_VALUE
+    assert stacked(bias=FAKE_ODD) == INVALID_VALUE
+    assert stacked(Ls=0, x=None) == SUCCESS
+    assert stacked(M=0, x=None) == SUCCESS
+    if not _gpu_visible():
+        assert stacked() == NO_DEVICE
+        assert stacked(Ls=65535, M=1, K=16384) == NO_DEVICE
     buf = ctypes.create_string_buffer(1 << 16)
     p = ctypes.cast(buf, ctypes.c_void_p)
     assert L.svdq_awq_pack_weights(None, p, 4, 8, 64, 64, 20, p, p, p, p, None) == INVALID_VALUE

@@ -88,3 +88,38 @@ def test_awq_repeated_launches_are_bit_identical():
     spec = S.LinearSpec("awqrep", 8, 5, 512, 96, 0, outlier_frac=0.03, outlier_scale=10.0, silu_input=True)
     x, b, pk = _case(spec)
     assert np.array_equal(_run(x, b, pk), _run(x, b, pk))
+
+
+def _stack(packs, key):
+    return np.ascontiguousarray(np.stack([pk[key] for pk in packs]))
+
+
+@pytest.mark.parametrize("M,K,N,L", [(1, 512, 96, 3), (4, 320, 64, 2), (20, 256, 32, 3), (1, 3072, 18432, 4),
+                                     (4, 3072, 18432, 2)])
+def test_awq_stacked_matches_single_layers(M, K, N, L):
+    """L layers sharing x in one launch: every layer's output is bit-identical
+    to the one-layer call on its own arrays, and layer 0 matches the oracle
+    (3072 -> 18432 at four tokens: three n-tiles per workgroup)."""
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K_
+    cases = []
+    for l in range(L):
+        spec = S.LinearSpec(f"awqst{M}x{K}x{N}", 8, M, K, N, 0, outlier_frac=0.03, outlier_scale=10.0,
+                            heavy_tail=True, silu_input=True, layer_id=300 + l)
+        cases.append(_case(spec, search=K * N <= 512 * 96))
+    x = cases[0][0]                      # the shared input
+    packs = [c[2] for c in cases]
+    biases = [c[1] for c in cases]
+    xd = to_dev_bf16(x)
+    sm = to_dev(np.asarray(_stack(packs, "smooth"), np.float32))
+    codes, scales, zeros = to_dev(_stack(packs, "codes")), to_dev_bf16(_stack(packs, "scales")), \
+        to_dev(_stack(packs, "zeros"))
+    bias = to_dev_bf16(np.ascontiguousarray(np.stack(biases)))
+    for b in (bias, None):
+        ys = K_.awq_w4a16_gemm_stacked(xd, sm, codes, scales, zeros, b)
+        torch.cuda.synchronize()
+        for l in range(L):
+            y1 = K_.awq_w4a16_gemm(xd, sm[l], codes[l], scales[l], zeros[l], None if b is None else b[l])
+            torch.cuda.synchronize()
+            assert torch.equal(ys[l], y1), l
+    _check(bf16_bits(ys[0]), x, None, packs[0], bias=False)

@@ -119,7 +119,7 @@ def test_workspace_growth_during_capture_is_refused():
 
 
 def test_graph_replays_awq_and_fp4_match_eager():
-    """The AWQ W4A16 linear and both MXFP4 calls inside one captured graph:
+    """The AWQ W4A16 linear (one layer and a stack) and both MXFP4 calls inside one captured graph:
     every replay (with eager work on the stream in between) reproduces the
     eager outputs bit for bit, and those match the oracle."""
     import torch
@@ -150,7 +150,10 @@ def test_graph_replays_awq_and_fp4_match_eager():
     ax4, ax1 = to_dev_bf16(ax), to_dev_bf16(ax[:1])
     ay4 = torch.empty((4, 256), dtype=torch.bfloat16, device="cuda")
     ay1 = torch.empty((1, 256), dtype=torch.bfloat16, device="cuda")
-    outs = (*fq, fy, ay4, ay1)
+    # the same layer twice as a stack of 2 sharing x
+    sdev = [torch.stack([t, t]).contiguous() for t in adev]
+    ays = torch.empty((2, 4, 256), dtype=torch.bfloat16, device="cuda")
+    outs = (*fq, fy, ay4, ay1, ays)
     s = torch.cuda.Stream()
 
     def chain():
@@ -158,6 +161,7 @@ def test_graph_replays_awq_and_fp4_match_eager():
         K.fp4_gemm_lora_up(c, sc, fwc, fws, la, flu, fb, out=fy)
         K.awq_w4a16_gemm(ax4, *adev, out=ay4)
         K.awq_w4a16_gemm(ax1, *adev, out=ay1)
+        K.awq_w4a16_gemm_stacked(ax4, *sdev, out=ays)
 
     K.debug_set_quant_plan(2, 0)
     try:
@@ -190,3 +194,4 @@ def test_graph_replays_awq_and_fp4_match_eager():
     rel, mx = y_errors(bf16_bits(ay4), want4)
     assert rel <= Y_REL_FRO and mx <= Y_MAX_ABS, (rel, mx)
     assert torch.equal(ay1[0], ay4[0])
+    assert torch.equal(ays[0], ay4) and torch.equal(ays[1], ay4)

@@ -121,3 +121,51 @@ def test_fp4_headline_shape_sampled_rows():
     d, lam, pk = _case(S.SPECS["mlp_up"])
     rows = [0, 1, 127, 128, 2047, 4095, 4096, 4607]
     _check(_run(d, lam, pk), d, lam, pk, rows=rows)
+
+
+def _bf16_ladder_blocks(s: int) -> np.ndarray:
+    """Blocks of 32 bf16 patterns whose maximum 6 * 2^s fixes the shared
+    exponent at s (elements divide by 2^s exactly), filled with every E2M1
+    rounding midpoint times 2^s, its two bf16 neighbours, and their negatives."""
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]) * 2.0 ** s
+    base = S.to_bf16_bits(mids).astype(np.int64)
+    vals = np.concatenate([base - 1, base, base + 1])            # one bf16 ulp below / above
+    vals = np.concatenate([vals, vals | 0x8000]).astype(np.uint16)  # and the negatives
+    top = S.to_bf16_bits(np.array([6.0 * 2.0 ** s]))
+    pad = np.concatenate([top, vals])                             # 43 values
+    out = np.resize(pad, 64)                                      # two blocks, each holding 6 * 2^s
+    out[32] = top[0]
+    return out
+
+
+def test_fp4_quantizer_midpoint_neighbours_and_signs():
+    """The hardware E2M1 converter plus the sign-of-zero fixup against the
+    oracle's midpoint ladder (MX specification rounding: nearest, midpoints to
+    the even code, saturation above 6, zero unsigned) on every bf16 input that
+    borders a midpoint, at several block exponents; negatives that round to
+    zero (small values, -0.25 * 2^s exactly, -0.0) must give code 0;
+    maxima in (6, 8) * 2^s saturate; blocks whose exponent clamps at -127."""
+    d, lam, pk = _case(_spec(48, 256, 64, 16, 7))
+    x = np.zeros((16, 256), dtype=np.uint16)
+    for i, s in enumerate([-40, -9, -1, 0, 3, 17, 60, 100]):
+        x[i, :64] = _bf16_ladder_blocks(s)
+        x[i, 64:128] = _bf16_ladder_blocks(s + 1)[::-1]
+        # negatives rounding to zero, negative zero, and saturating maxima
+        neg_small = -np.array([0.25, 0.2, 0.125, 2.0 ** -6, 0.249])
+        blk = np.concatenate([[7.0, -7.5, 7.96875, 6.5], neg_small, [0.0] * 23]) * 2.0 ** s
+        x[i, 128:160] = S.to_bf16_bits(blk)
+        x[i, 128 + 9] = 0x8000                                   # -0.0
+        x[i, 160:192] = S.to_bf16_bits(np.resize(np.array([-7.9375, 6.25, -0.75, 0.0]), 32) * 2.0 ** s)
+    # exponent clamped at -127: normal values just above 2^-126
+    tiny = np.array([1.0, 1.25, 1.5, 1.75, 1.125, -1.5, -1.0, 1.875]) * 2.0 ** -126
+    x[8:16, :32] = S.to_bf16_bits(np.resize(tiny, 32))
+    x[8:16, 192:256] = x[0:8, 0:64]
+    ones = np.ones(256, dtype=np.float32)
+    got = _run(d, ones, pk, x_bits=np.tile(x, (3, 1)))
+    ref = X.quantize_act_lora_down_fp4(np.tile(x, (3, 1)), ones, pk["lora_down"])
+    assert np.array_equal(got[1], ref["act_scales"]), np.argwhere(got[1] != ref["act_scales"])[:5]
+    assert np.array_equal(got[0], ref["act_codes"]), np.argwhere(got[0] != ref["act_codes"])[:5]
+    # the clamped blocks really clamp, and no code 8 (negative zero) appears
+    assert np.all(ref["act_scales"][8:16, 0] == 0)
+    codes = X.unpack_fp4(got[0])
+    assert not np.any(codes == 8)

@@ -11,8 +11,8 @@ import pytest
 
 import oracle as O
 import synthetic as S
-from tests.gpu_util import (Y_MAX_ABS, Y_REL_FRO, bf16_bits, custom_case, oracle_case, to_dev,
-                            to_dev_bf16, ulp_distance, y_errors)
+from tests.gpu_util import (bf16_bits, check_quant as _check_quant, check_y as _check_y, custom_case,
+                            oracle_case, to_dev, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,46 +41,6 @@ def _run(d, lam, packed, bias=True):
     torch.cuda.synchronize()
     return {"act_codes": codes.cpu().numpy(), "act_scales": bf16_bits(scales),
             "lora_act": bf16_bits(la), "y": bf16_bits(y)}
-
-
-def _check_quant(got, ref, lora_down=None):
-    assert np.array_equal(got["act_scales"], ref["act_scales"]), \
-        np.argwhere(got["act_scales"] != ref["act_scales"])[:5]
-    assert np.array_equal(got["act_codes"], ref["act_codes"]), \
-        np.argwhere(got["act_codes"] != ref["act_codes"])[:5]
-    if ref["lora_act"].size:
-        _check_lora_act(got["lora_act"], ref, lora_down)
-
-
-def _check_lora_act(got_bits, ref, lora_down):
-    """lora_act = bf16(x_hat @ L1) with fp32 accumulation on the GPU.
-
-    Bound from the arithmetic: both sides round to bf16 once (half an ulp each),
-    and an fp32 sum of K products (exact bf16 x bf16 products) is off by at most
-    K * 2^-24 * sum_k |x_hat_k L1_k|.  Where the sum does not cancel this is
-    below one ulp, and almost every element must be within one ulp."""
-    d = ulp_distance(got_bits, ref["lora_act"])
-    assert (d <= 1).mean() >= 0.999, (d > 1).sum()
-    if lora_down is None:
-        assert d.max() <= 1
-        return
-    xh = np.abs(O.bf16_to_f64(ref["xhat"]))
-    mag = xh @ np.abs(O.bf16_to_f64(lora_down)).T
-    K = xh.shape[1]
-    got = O.bf16_to_f64(got_bits)
-    want = O.bf16_to_f64(ref["lora_act"])
-    ulp = np.maximum(np.abs(want), np.abs(got)) * 2.0 ** -7
-    assert np.all(np.abs(got - want) <= ulp + K * 2.0 ** -24 * mag)
-
-
-def _check_y(y_bits, d, lam, packed, ref_a, rows=None, bias=True):
-    y_ref, _ = O.linear_output(ref_a["act_codes"], ref_a["act_scales"], packed["w_codes"],
-                               packed["w_scales"], ref_a["lora_act"], packed["lora_up"],
-                               d["bias"] if bias else None, rows=rows)
-    got = y_bits if rows is None else y_bits[np.asarray(rows)]
-    rel, mx = y_errors(got, y_ref)
-    assert rel <= Y_REL_FRO and mx <= Y_MAX_ABS, (rel, mx)
-    return rel, mx
 
 
 def test_tiny_config_full_parity():

@@ -2,8 +2,18 @@
 
 Thin Python binding over libsvdq.so (C ABI: include/svdq.h).  Every step of
 the hot path runs in the library's HIP kernels; this module only marshals
-arguments: it checks dtypes and shapes, allocates outputs with torch on the
-current device, and passes raw pointers and the current HIP stream.
+arguments: it checks dtypes, shapes and devices of inputs and of caller-given
+outputs, allocates outputs and device workspaces with torch on the current
+device, and passes raw pointers and the current HIP stream.
+
+Workspaces.  Calls 1 and 2 may need a device workspace (the C ABI's
+svdq_*_workspace_size).  Pass ``workspace=`` (a zero-filled uint8 device
+tensor, reused across calls ordered on one stream) or let the binding keep one
+per (device, stream): it is allocated zero-filled by torch on first need and
+replaced by a larger one when a call needs more.  A replaced buffer stays
+alive until ``release_workspaces()``, because a HIP graph captured earlier may
+still point at it.  While the stream is being captured the binding never
+allocates: make one eager call of the largest shape before capturing.
 
 Two online calls (the charmloop.ai news item on Nunchaku in Diffusers,
 paragraph on the 16-bit branch, names the two fusions):
@@ -26,7 +36,7 @@ __all__ = ["SvdqError", "lib", "check_device", "quantize_act_lora_down", "w4a4_g
            "EPILOGUES", "smooth_from_absmax", "pack_weights", "awq_w4a16_gemm", "awq_w4a16_gemm_stacked",
            "awq_pack_weights",
            "quantize_act_lora_down_fp4", "fp4_gemm_lora_up", "pack_weights_fp4",
-           "GROUP_SIZE"]
+           "release_workspaces", "GROUP_SIZE"]
 
 GROUP_SIZE = 64
 
@@ -59,12 +69,55 @@ def _need(t, dtype, shape, name):
     del torch
 
 
+def _need_out(t, dtype, shape, device, name):
+    """A caller-given output: exact dtype and shape, contiguous, on the inputs' device."""
+    _need(t, dtype, shape, name)
+    if t.numel() and t.device != device:
+        raise ValueError(f"{name}: must be on {device}, got {t.device}")
+
+
+_WS: dict = {}        # (device index, stream handle) -> zero-filled uint8 tensor
+_WS_RETIRED: list = []
+
+
+def release_workspaces() -> None:
+    """Drop the binding's cached workspaces (and the replaced ones kept for
+    graphs captured earlier); later calls allocate afresh."""
+    _WS.clear()
+    _WS_RETIRED.clear()
+
+
+def _workspace(need: int, device, stream, given):
+    """(pointer, bytes) of a workspace of at least `need` bytes for a call on `stream`."""
+    torch = _torch()
+    if given is not None:
+        if given.dtype != torch.uint8 or not given.is_contiguous() or given.device != device:
+            raise ValueError("workspace: must be a contiguous uint8 tensor on the call's device")
+        return ctypes.c_void_p(given.data_ptr()), given.numel()
+    if need == 0:
+        return None, 0
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    key = (device.index, s.cuda_stream)
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < need:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError(f"the call needs a workspace of {need} bytes and the stream is being "
+                               "captured: make one eager call of this shape before capturing")
+        with torch.cuda.stream(s):
+            nb = max(need + need // 4, 0 if buf is None else buf.numel())
+            new = torch.zeros(nb, dtype=torch.uint8, device=device)
+        if buf is not None:
+            _WS_RETIRED.append(buf)
+        _WS[key] = buf = new
+    return ctypes.c_void_p(buf.data_ptr()), buf.numel()
+
+
 def check_device(device: int = 0) -> None:
     """Raise unless HIP device ``device`` is a gfx950."""
     check(lib().svdq_check_device(int(device)), "svdq_check_device")
 
 
-def quantize_act_lora_down(x, smooth, lora_down=None, out=None, stream=None):
+def quantize_act_lora_down(x, smooth, lora_down=None, out=None, stream=None, workspace=None):
     """Call 1: smoothing + int4 quantization + packing + fused lora_down.
 
     x bf16 [M, K], smooth fp32 [K], lora_down bf16 [r, K] or None (r = 0).
@@ -84,9 +137,13 @@ def quantize_act_lora_down(x, smooth, lora_down=None, out=None, stream=None):
         lora_act = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
     else:
         codes, scales, lora_act = out
+        _need_out(codes, torch.uint8, (M, K // 2), dev, "act_codes")
+        _need_out(scales, torch.bfloat16, (M, K // GROUP_SIZE), dev, "act_scales")
+        _need_out(lora_act, torch.bfloat16, (M, r), dev, "lora_act")
+    ws, wsb = _workspace(lib().svdq_quantize_act_workspace_size(M, K, r), dev, stream, workspace)
     st = lib().svdq_quantize_act_lora_down(
         _ptr(x), _ptr(smooth), _ptr(lora_down) if r else None, M, K, r, GROUP_SIZE,
-        _ptr(codes), _ptr(scales), _ptr(lora_act) if r else None, _stream(stream))
+        _ptr(codes), _ptr(scales), _ptr(lora_act) if r else None, ws, wsb, _stream(stream))
     check(st, "svdq_quantize_act_lora_down")
     return codes, scales, lora_act
 
@@ -109,8 +166,16 @@ def debug_set_gemm_splits(splits: int = 0) -> None:
 EPILOGUES = {"none": 0, "gelu_tanh": 1}
 
 
+def _out_y(out, M, N, device, lead=()):
+    torch = _torch()
+    if out is None:
+        return torch.empty((*lead, M, N), dtype=torch.bfloat16, device=device)
+    _need_out(out, torch.bfloat16, (*lead, M, N), device, "y")
+    return out
+
+
 def w4a4_gemm_lora_up(act_codes, act_scales, w_codes, w_scales, lora_act=None, lora_up=None,
-                      bias=None, out=None, stream=None, epilogue="none"):
+                      bias=None, out=None, stream=None, epilogue="none", workspace=None):
     """Call 2: W4A4 GEMM + per-group dequant + fused lora_up + bias -> Y bf16 [M, N].
 
     epilogue "gelu_tanh" applies GELU (tanh form) to y + b before the rounding.
@@ -129,11 +194,13 @@ def w4a4_gemm_lora_up(act_codes, act_scales, w_codes, w_scales, lora_act=None, l
         _need(lora_up, torch.bfloat16, (N, r), "lora_up")
     if bias is not None:
         _need(bias, torch.bfloat16, (N,), "bias")
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=act_codes.device) if out is None else out
+    dev = act_codes.device
+    y = _out_y(out, M, N, dev)
+    ws, wsb = _workspace(lib().svdq_w4a4_gemm_workspace_size(M, N, K, r), dev, stream, workspace)
     st = lib().svdq_w4a4_gemm_lora_up_ex(
         _ptr(act_codes), _ptr(act_scales), _ptr(w_codes), _ptr(w_scales),
         _ptr(lora_act) if r else None, _ptr(lora_up) if r else None, _ptr(bias),
-        M, N, K, r, GROUP_SIZE, EPILOGUES[epilogue], _ptr(y), _stream(stream))
+        M, N, K, r, GROUP_SIZE, EPILOGUES[epilogue], _ptr(y), ws, wsb, _stream(stream))
     check(st, "svdq_w4a4_gemm_lora_up_ex")
     return y
 
@@ -163,7 +230,7 @@ def w4a4_gemm_qkv_norm_rope(act_codes, act_scales, w_codes, w_scales, lora_act, 
     _need(k_norm, torch.bfloat16, (head_dim,), "k_norm")
     _need(rope_cos, torch.float32, (M, head_dim // 2), "rope_cos")
     _need(rope_sin, torch.float32, (M, head_dim // 2), "rope_sin")
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=act_codes.device) if out is None else out
+    y = _out_y(out, M, N, act_codes.device)
     st = lib().svdq_w4a4_gemm_qkv_norm_rope(
         _ptr(act_codes), _ptr(act_scales), _ptr(w_codes), _ptr(w_scales),
         _ptr(lora_act) if r else None, _ptr(lora_up) if r else None, _ptr(bias),
@@ -191,22 +258,25 @@ def mlp_pair(x, up: dict, down: dict, h_out=None, out=None, stream=None):
     return y, h
 
 
-def w4a4_group_acc_debug(act_codes, w_codes, stream=None):
-    """Test hook: the exact int32 group accumulators [M, N, K/64] of call 2's main loop."""
+def w4a4_group_acc_debug(act_codes, w_codes, rows=None, cols=None, stream=None):
+    """Test hook: the exact int32 group accumulators of call 2's main loop for the
+    window rows = (m0, mc), cols = (n0, nc) (default: everything) -> [mc, nc, K/64]."""
     torch = _torch()
     M = act_codes.shape[0]
     K = act_codes.shape[1] * 2
     N = w_codes.shape[0]
     _need(act_codes, torch.uint8, (M, K // 2), "act_codes")
     _need(w_codes, torch.uint8, (N, K // 2), "w_codes")
-    acc = torch.empty((M, N, K // GROUP_SIZE), dtype=torch.int32, device=act_codes.device)
-    st = lib().svdq_w4a4_group_acc_debug(_ptr(act_codes), _ptr(w_codes), M, N, K, GROUP_SIZE,
+    m0, mc = (0, M) if rows is None else rows
+    n0, nc = (0, N) if cols is None else cols
+    acc = torch.empty((max(mc, 0), max(nc, 0), K // GROUP_SIZE), dtype=torch.int32, device=act_codes.device)
+    st = lib().svdq_w4a4_group_acc_debug(_ptr(act_codes), _ptr(w_codes), M, N, K, m0, mc, n0, nc,
                                          _ptr(acc), _stream(stream))
     check(st, "svdq_w4a4_group_acc_debug")
     return acc
 
 
-def quantize_act_lora_down_fp4(x, smooth, lora_down=None, out=None, stream=None):
+def quantize_act_lora_down_fp4(x, smooth, lora_down=None, out=None, stream=None, workspace=None):
     """Call 1, FP4 variant: -> (act_codes u8 [M, K/2] E2M1, act_scales u8 [M, K/32] E8M0,
     lora_act bf16 [M, r])."""
     torch = _torch()
@@ -222,15 +292,19 @@ def quantize_act_lora_down_fp4(x, smooth, lora_down=None, out=None, stream=None)
         lora_act = torch.empty((M, r), dtype=torch.bfloat16, device=x.device)
     else:
         codes, scales, lora_act = out
+        _need_out(codes, torch.uint8, (M, K // 2), x.device, "act_codes")
+        _need_out(scales, torch.uint8, (M, K // 32), x.device, "act_scales")
+        _need_out(lora_act, torch.bfloat16, (M, r), x.device, "lora_act")
+    ws, wsb = _workspace(lib().svdq_quantize_act_workspace_size(M, K, r), x.device, stream, workspace)
     st = lib().svdq_quantize_act_lora_down_fp4(_ptr(x), _ptr(smooth), _ptr(lora_down) if r else None, M, K, r,
                                                 _ptr(codes), _ptr(scales), _ptr(lora_act) if r else None,
-                                                _stream(stream))
+                                                ws, wsb, _stream(stream))
     check(st, "svdq_quantize_act_lora_down_fp4")
     return codes, scales, lora_act
 
 
 def fp4_gemm_lora_up(act_codes, act_scales, w_codes, w_scales, lora_act=None, lora_up=None, bias=None,
-                     out=None, stream=None, epilogue="none"):
+                     out=None, stream=None, epilogue="none", workspace=None):
     """Call 2, FP4 variant: MXFP4 GEMM (block scales in the matrix core) + lora_up + bias -> Y bf16."""
     torch = _torch()
     M = act_codes.shape[0]
@@ -246,10 +320,11 @@ def fp4_gemm_lora_up(act_codes, act_scales, w_codes, w_scales, lora_act=None, lo
         _need(lora_up, torch.bfloat16, (N, r), "lora_up")
     if bias is not None:
         _need(bias, torch.bfloat16, (N,), "bias")
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=act_codes.device) if out is None else out
+    y = _out_y(out, M, N, act_codes.device)
+    ws, wsb = _workspace(lib().svdq_fp4_gemm_workspace_size(M, N, K, r), act_codes.device, stream, workspace)
     st = lib().svdq_fp4_gemm_lora_up(_ptr(act_codes), _ptr(act_scales), _ptr(w_codes), _ptr(w_scales),
                                      _ptr(lora_act) if r else None, _ptr(lora_up) if r else None, _ptr(bias),
-                                     M, N, K, r, EPILOGUES[epilogue], _ptr(y), _stream(stream))
+                                     M, N, K, r, EPILOGUES[epilogue], _ptr(y), ws, wsb, _stream(stream))
     check(st, "svdq_fp4_gemm_lora_up")
     return y
 
@@ -286,7 +361,7 @@ def awq_w4a16_gemm(x, smooth, w_codes, w_scales, w_zeros, bias=None, out=None, s
     _need(w_zeros, torch.uint8, (N, K // GROUP_SIZE), "w_zeros")
     if bias is not None:
         _need(bias, torch.bfloat16, (N,), "bias")
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    y = _out_y(out, M, N, x.device)
     st = lib().svdq_awq_w4a16_gemm(_ptr(x), _ptr(smooth), _ptr(w_codes), _ptr(w_scales), _ptr(w_zeros),
                                    _ptr(bias), M, N, K, GROUP_SIZE, _ptr(y), _stream(stream))
     check(st, "svdq_awq_w4a16_gemm")
@@ -306,7 +381,7 @@ def awq_w4a16_gemm_stacked(x, smooth, w_codes, w_scales, w_zeros, bias=None, out
     _need(w_zeros, torch.uint8, (L, N, K // GROUP_SIZE), "w_zeros")
     if bias is not None:
         _need(bias, torch.bfloat16, (L, N), "bias")
-    y = torch.empty((L, M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    y = _out_y(out, M, N, x.device, lead=(L,))
     st = lib().svdq_awq_w4a16_gemm_stacked(_ptr(x), _ptr(smooth), _ptr(w_codes), _ptr(w_scales), _ptr(w_zeros),
                                            _ptr(bias), L, M, N, K, GROUP_SIZE, _ptr(y), _stream(stream))
     check(st, "svdq_awq_w4a16_gemm_stacked")

@@ -17,6 +17,7 @@ SUCCESS, INVALID_VALUE, NOT_SUPPORTED, ARCH_MISMATCH, NO_DEVICE, HIP_ERROR, INTE
 _c_void_p = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _u64 = ctypes.c_uint64
+_size = ctypes.c_size_t
 
 # name -> (restype, argtypes), in the order of include/svdq.h
 SIGNATURES = {
@@ -26,25 +27,29 @@ SIGNATURES = {
     "svdq_check_device": (ctypes.c_int, [ctypes.c_int]),
     "svdq_quantize_act_lora_down": (ctypes.c_int, [
         _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64,
-        _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "svdq_quantize_act_workspace_size": (_size, [_i64, _i64, _i64]),
     "svdq_debug_set_quant_plan": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     "svdq_debug_set_gemm_path": (ctypes.c_int, [ctypes.c_int]),
     "svdq_debug_set_gemm_splits": (ctypes.c_int, [ctypes.c_int]),
     "svdq_w4a4_gemm_lora_up": (ctypes.c_int, [
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-        _i64, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p]),
+        _i64, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "svdq_w4a4_gemm_workspace_size": (_size, [_i64, _i64, _i64, _i64]),
     "svdq_w4a4_gemm_lora_up_ex": (ctypes.c_int, [
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-        _i64, _i64, _i64, _i64, _i64, ctypes.c_int, _c_void_p, _c_void_p]),
+        _i64, _i64, _i64, _i64, _i64, ctypes.c_int, _c_void_p, _c_void_p, _size, _c_void_p]),
     "svdq_w4a4_gemm_qkv_norm_rope": (ctypes.c_int, [
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
         _i64, _i64, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p, ctypes.c_float,
         _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "svdq_quantize_act_lora_down_fp4": (ctypes.c_int, [
-        _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+        _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+        _c_void_p, _size, _c_void_p]),
     "svdq_fp4_gemm_lora_up": (ctypes.c_int, [
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-        _i64, _i64, _i64, _i64, ctypes.c_int, _c_void_p, _c_void_p]),
+        _i64, _i64, _i64, _i64, ctypes.c_int, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "svdq_fp4_gemm_workspace_size": (_size, [_i64, _i64, _i64, _i64]),
     "svdq_awq_w4a16_gemm": (ctypes.c_int, [
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64,
         _c_void_p, _c_void_p]),
@@ -52,7 +57,7 @@ SIGNATURES = {
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _i64,
         _c_void_p, _c_void_p]),
     "svdq_w4a4_group_acc_debug": (ctypes.c_int, [
-        _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p]),
+        _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _c_void_p, _c_void_p]),
     "svdq_smooth_from_absmax": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p]),
     "svdq_pack_weights": (ctypes.c_int, [
         _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _u64,

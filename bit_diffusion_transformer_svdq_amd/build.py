@@ -30,6 +30,9 @@ HIP_FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
     "-Wall", "-Wno-unused-function",
 ]
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HOST_API_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+                  "-I", os.path.join(ROCM, "include")]
 KERNELS = ["quant_lora_down.hip", "w4a4_gemm_lora_up.hip", "w4a4_gemm_skinny.hip", "awq_w4a16_gemm.hip"]
 
 
@@ -63,11 +66,11 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
             cmd[2] = "-save-temps=obj"
         _run(cmd, verbose)
         objs.append(obj)
-    for host_src in ("api.cpp", "workspace.cpp"):
-        obj = os.path.join(BUILD_DIR, host_src.replace(".cpp", ".o"))
-        _run([hipcc, "-c", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC,
-              os.path.join(CSRC, host_src), "-o", obj], verbose)
-        objs.append(obj)
+    # the C ABI is host code: g++ against the HIP runtime API
+    api_obj = os.path.join(BUILD_DIR, "api.o")
+    _run(["g++", "-c", *HOST_API_FLAGS, "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, "api.cpp"),
+          "-o", api_obj], verbose)
+    objs.append(api_obj)
     packer_obj = os.path.join(BUILD_DIR, "packer.o")
     _run(["g++", "-c", "-O3", "-march=x86-64-v3", "-std=c++17", "-fPIC", "-Wall", "-fno-fast-math",
           "-ffp-contract=off", "-I", INCLUDE, os.path.join(CSRC, "packer.cpp"), "-o", packer_obj], verbose)

@@ -36,7 +36,7 @@
 
 #include <algorithm>
 
-#include "svdq_internal.h"
+#include "svdq_device.h"
 
 namespace svdq {
 namespace {

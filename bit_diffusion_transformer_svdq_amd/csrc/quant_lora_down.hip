@@ -50,7 +50,7 @@
 #include <algorithm>
 #include <atomic>
 
-#include "svdq_internal.h"
+#include "svdq_device.h"
 
 namespace svdq {
 namespace {
@@ -547,17 +547,37 @@ Plan make_plan(int T, int G, int NT, int cus) {
 
 std::atomic<int> g_force_tb{0}, g_force_kb{0};  // test hook (0 = automatic)
 
-
-int cu_count(int dev) {
-  static int cache[64] = {0};
-  if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev];
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
-    (void)hipGetLastError();
-    n = 256;
+// The plan of a call on the current device, with the test hook's forced split.
+Plan plan_for(int64_t M, int64_t K, int64_t r) {
+  const int NT = (int)(r / 16);
+  const int T = (int)((M + 15) / 16);
+  const int G = (int)(K / 64);
+  Plan p = make_plan(T, G, NT, current_cus());
+  const int force_kb = g_force_kb.load(), force_tb = g_force_tb.load();
+  if (force_kb > 0 || force_tb > 0) {
+    const int TB = force_tb > 0 ? std::min(force_tb, kMaxTiles) : p.TB;
+    const int KB0 = force_kb > 0 ? std::min(force_kb, G) : p.KB;
+    const int GB = (G + KB0 - 1) / KB0;
+    if (GB <= kMaxGB && lds_bytes(GB, NT) + kMuBytes <= (size_t)kLdsLimit)
+      p = Plan{TB, GB, (G + GB - 1) / GB, (T + TB - 1) / TB, lds_bytes(GB, NT)};
   }
-  if (dev >= 0 && dev < 64) cache[dev] = n;
-  return n;
+  // a split K needs one workspace counter per row tile: beyond that many row
+  // tiles K is split only where the LDS requires it (K > 64 groups), and the
+  // C ABI rejects such shapes
+  if (p.KB > 1 && NT > 0 && (size_t)T > kWsMaxCounters) {
+    const int GB = std::min(G, kMaxGB);
+    p = Plan{p.TB, GB, (G + GB - 1) / GB, p.nrb, lds_bytes(GB, NT)};
+  }
+  return p;
+}
+
+// With K split over several blocks, T arrival counters and the fp32 lora
+// partials [KB][T][NT][4][64].
+size_t part_counters(const Plan& p, int64_t M, int64_t r) {
+  return (r > 0 && p.KB > 1) ? (size_t)((M + 15) / 16) : 0;
+}
+size_t part_bytes(const Plan& p, int64_t M, int64_t r) {
+  return (r > 0 && p.KB > 1) ? (size_t)p.KB * (size_t)((M + 15) / 16) * (size_t)(r / 16) * 64 * 16 : 0;
 }
 
 template <int NT, bool kFp4>
@@ -581,40 +601,31 @@ void set_quant_plan_override(int k_blocks, int tiles_per_wg) {
   g_force_tb.store(std::max(0, tiles_per_wg));
 }
 
+size_t quant_workspace_bytes(int64_t M, int64_t K, int64_t r) {
+  if (M <= 0) return 0;
+  const Plan p = plan_for(M, K, r);
+  return ws_bytes(part_counters(p, M, r), part_bytes(p, M, r));
+}
+
 hipError_t launch_quant_lora_down(const uint16_t* x, const float* lam, const uint16_t* lora_down,
                                   int64_t M, int64_t K, int64_t r, uint8_t* codes,
-                                  uint16_t* scales, uint16_t* lora_act, bool fp4, hipStream_t stream) {
+                                  uint16_t* scales, uint16_t* lora_act, bool fp4, Workspace ws,
+                                  hipStream_t stream) {
   const int NT = (int)(r / 16);
-  const int T = (int)((M + 15) / 16);
-  const int G = (int)(K / 64);
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-
-  Plan p = make_plan(T, G, NT, cu_count(dev));
-  const int force_kb = g_force_kb.load(), force_tb = g_force_tb.load();
-  if (force_kb > 0 || force_tb > 0) {
-    const int TB = force_tb > 0 ? std::min(force_tb, kMaxTiles) : p.TB;
-    const int KB0 = force_kb > 0 ? std::min(force_kb, G) : p.KB;
-    const int GB = (G + KB0 - 1) / KB0;
-    if (GB <= kMaxGB && lds_bytes(GB, NT) + kMuBytes <= (size_t)kLdsLimit)
-      p = Plan{TB, GB, (G + GB - 1) / GB, (T + TB - 1) / TB, lds_bytes(GB, NT)};
-  }
+  const Plan p = plan_for(M, K, r);
 
   QuantArgs a;
   a.x = x; a.lam = lam; a.lora_down = lora_down;
   a.codes = codes; a.scales = scales; a.lora_act = lora_act;
   a.part = nullptr; a.count = nullptr;
-  a.M = (int)M; a.K = (int)K; a.T = T; a.G = G;
+  a.M = (int)M; a.K = (int)K; a.T = (int)((M + 15) / 16); a.G = (int)(K / 64);
   a.GB = p.GB; a.TB = p.TB; a.KB = p.KB;
 
-  if (NT > 0 && p.KB > 1) {
-    // T arrival counters and the fp32 partials [KB][T][NT][4][64]
-    const size_t part_need = (size_t)p.KB * T * NT * 64 * 16;
-    void* part = nullptr;
-    e = stream_workspace(stream, (size_t)T, part_need, &a.count, &part);
-    if (e != hipSuccess) return e;
-    a.part = static_cast<float*>(part);
+  const size_t nc = part_counters(p, M, r);
+  if (nc > 0) {
+    if (ws.bytes < ws_bytes(nc, part_bytes(p, M, r))) return hipErrorInvalidValue;
+    a.count = ws_counters(ws);
+    a.part = static_cast<float*>(ws_scratch(ws));
   }
 
   switch (NT) {

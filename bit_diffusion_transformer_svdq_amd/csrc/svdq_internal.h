@@ -1,23 +1,12 @@
 // Internal declarations shared by the C ABI (api.cpp) and the HIP kernel files.
+// Host-only: the C ABI and the packer build without the device compiler.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace svdq {
-
-// Output epilogue of call 2: GELU with the tanh approximation (Hendrycks and
-// Gimpel, 2016), 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), for the MLP
-// projections the W4A4 layer serves (mind-verse.de, "Effiziente Optimierung
-// von Diffusionsmodellen durch Nunchaku 4-Bit-Quantisierung", section "Nunchaku
-// Lite: Nahtlose Integration in Diffusers").  With e = exp(2u) the identity
-// 0.5 x (1 + tanh u) = x - x / (e + 1) needs one exponential and one
-// reciprocal, and gives x for e = inf and 0 for e = 0.
-__device__ __forceinline__ float gelu_tanh(float x) {
-  const float u = 0.7978845608028654f * __builtin_fmaf(0.044715f * x, x * x, x);
-  const float e = __expf(2.0f * u);
-  return x - __fdividef(x, e + 1.0f);
-}
 
 // Epilogue codes of call 2 (values of the C ABI's svdq_epilogue, plus the
 // fused QKV epilogue of svdq_w4a4_gemm_qkv_norm_rope).
@@ -36,41 +25,68 @@ struct QkvEpilogue {
   float eps;
 };
 
-// The library's device scratch for `stream` on the current device: at least
-// `counters` u32 counters, zero between launches (every kernel that uses one
-// leaves it at zero), and at least `bytes` of scratch after them.  Allocates
-// or grows on demand (never while the stream is capturing: then
-// hipErrorStreamCaptureUnsupported); outgrown buffers stay allocated.
-hipError_t stream_workspace(hipStream_t stream, size_t counters, size_t bytes, uint32_t** counter_ptr,
-                            void** scratch_ptr);
+// Caller-owned device workspace of a call: a fixed region of u32 arrival
+// counters first, then scratch bytes (fp32 partial sums of the K-split
+// reductions).  The counters are zero whenever no launch using them runs: the
+// caller zero-fills the buffer once, and every kernel leaves the counters it
+// used at zero.  Because the counter region has the same place and size for
+// every call, one workspace serves calls of any shape in turn; the scratch
+// after it is always written before it is read.
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+constexpr size_t kWsCounterBytes = 1024 * 1024;         // the counter region
+constexpr size_t kWsMaxCounters = kWsCounterBytes / 4;  // plans never need more
+constexpr size_t ws_bytes(size_t counters, size_t scratch) {
+  return (counters == 0 && scratch == 0) ? 0 : kWsCounterBytes + scratch;
+}
+inline uint32_t* ws_counters(const Workspace& w) { return static_cast<uint32_t*>(w.ptr); }
+inline void* ws_scratch(const Workspace& w) { return static_cast<uint8_t*>(w.ptr) + kWsCounterBytes; }
+
+// Compute units of the current device (cached; 256 when no device answers).
+int current_cus();
 
 // Call 1: smoothing + int4 group quantization + packing + fused lora_down.
 // Shapes are validated by the caller: M > 0, K % 64 == 0, r % 16 == 0, r <= 128.
 // fp4: MXFP4 codes with two E8M0 exponents per 64-group (stored as one u16
 // per group: block 2g in the low byte) instead of int4 codes and bf16 scales.
+// The workspace must hold quant_workspace_bytes(M, K, r) bytes (planned for
+// the current device and the test hook's forced split).
+size_t quant_workspace_bytes(int64_t M, int64_t K, int64_t r);
 hipError_t launch_quant_lora_down(const uint16_t* x, const float* lam, const uint16_t* lora_down,
                                   int64_t M, int64_t K, int64_t r,
                                   uint8_t* codes, uint16_t* scales, uint16_t* lora_act,
-                                  bool fp4, hipStream_t stream);
+                                  bool fp4, Workspace ws, hipStream_t stream);
 
 // Test hook: forces call 1's work split (K-blocks, row tiles per workgroup);
 // 0 keeps the automatic choice.  Affects later launches of this process.
 void set_quant_plan_override(int k_blocks, int tiles_per_wg);
 
-// Call 2: W4A4 GEMM + group dequant + fused lora_up + bias.  When `acc_dump` is
-// not null the kernel writes the int32 group accumulators [M, N, K/64] there
+// Window of the accumulator dump: rows [m_lo, m_hi) and columns [n_lo, n_hi)
+// of the launched problem go to acc[((m - m_lo) * (n_hi - n_lo) + n - n_lo) * G + g].
+struct DumpWindow {
+  int32_t* acc = nullptr;
+  int m_lo = 0, m_hi = 0, n_lo = 0, n_hi = 0;
+};
+
+// Call 2: W4A4 GEMM + group dequant + fused lora_up + bias.  When `dump.acc` is
+// not null the kernel writes the int32 group accumulators of the window there
 // instead of Y (scales, lora and bias are then ignored).
 // Shapes are validated by the caller: M > 0, N % 64 == 0, K % 64 == 0,
 // r % 16 == 0, r <= 128.
 // `qkv` is read only for epilogue == kEpilogueQkv (then N % 384 == 0), which
 // always runs on the tiled kernel.
+// The workspace must hold gemm_workspace_bytes(M, N, K, r, epilogue, fp4)
+// bytes (planned for the current device and the test hooks' forced settings).
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r, int epilogue, bool fp4);
 hipError_t launch_w4a4_gemm_lora_up(const uint8_t* act_codes, const uint16_t* act_scales,
                                     const uint8_t* w_codes, const uint16_t* w_scales,
                                     const uint16_t* lora_act, const uint16_t* lora_up,
                                     const uint16_t* bias,
                                     int64_t M, int64_t N, int64_t K, int64_t r, int epilogue,
-                                    const QkvEpilogue* qkv, uint16_t* y, int32_t* acc_dump,
-                                    hipStream_t stream);
+                                    const QkvEpilogue* qkv, uint16_t* y, const DumpWindow& dump,
+                                    Workspace ws, hipStream_t stream);
 
 // Call 2 for few tokens: K split over the waves of a workgroup, weights
 // streamed once.  Same arguments and results as launch_w4a4_gemm_lora_up.
@@ -79,7 +95,7 @@ hipError_t launch_w4a4_gemm_skinny(const uint8_t* act_codes, const uint16_t* act
                                    const uint8_t* w_codes, const uint16_t* w_scales,
                                    const uint16_t* lora_act, const uint16_t* lora_up,
                                    const uint16_t* bias, int64_t M, int64_t N, int64_t K,
-                                   int64_t r, int epilogue, uint16_t* y, int32_t* acc_dump,
+                                   int64_t r, int epilogue, uint16_t* y, const DumpWindow& dump,
                                    hipStream_t stream);
 
 // Call 2 of the MXFP4 variant (tiled kernel; E8M0 scales u8 [rows, K/32],
@@ -88,7 +104,7 @@ hipError_t launch_fp4_gemm_lora_up(const uint8_t* act_codes, const uint8_t* act_
                                   const uint8_t* w_codes, const uint8_t* w_scales,
                                   const uint16_t* lora_act, const uint16_t* lora_up,
                                   const uint16_t* bias, int64_t M, int64_t N, int64_t K, int64_t r,
-                                  int epilogue, uint16_t* y, hipStream_t stream);
+                                  int epilogue, uint16_t* y, Workspace ws, hipStream_t stream);
 
 // Test hook: 0 = choose by shape, 1 = always the tiled kernel, 2 = the
 // few-token kernel wherever it is supported.

@@ -56,7 +56,7 @@
 #include <algorithm>
 #include <atomic>
 
-#include "svdq_internal.h"
+#include "svdq_device.h"
 
 namespace svdq {
 namespace {
@@ -131,6 +131,7 @@ struct GemmArgs {
   const uint16_t* bias;
   uint16_t* y;
   int32_t* acc;
+  int acc_m_lo, acc_m_hi, acc_n_lo, acc_n_hi;  // dump window (kDump)
   int M, N, K, r;
   int epilogue;  // kEpilogueNone, kEpilogueGelu (after the bias) or kEpilogueQkv
   QkvEpilogue qkv;
@@ -203,24 +204,26 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
 
   // DMA role: instruction k (0, 1) of a wave fills slots 256k + 64*wave + lane
   // of each operand tile, i.e. row s >> 2, granule (s & 3) ^ r[3:2]: four lanes
-  // cover the 64 bytes of one row.  32-bit lane offsets from the kernel
-  // arguments (codes arrays are below 2 GiB).
+  // cover the 64 bytes of one row.  The workgroup's first row is a 64-bit base
+  // pointer; lane offsets within its 128 rows fit 32 bits for every K.
+  const uint8_t* wbase = p.w_codes + (size_t)n0 * (size_t)KB;
+  const uint8_t* abase = p.act_codes + (size_t)m0 * (size_t)KB;
   u32 woff[2], aoff[2], gsel[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int s = 256 * k + 64 * wave + lane;
     const int row = s >> 2;
     gsel[k] = (u32)((s & 3) ^ ((row >> 2) & 3));
-    woff[k] = (u32)min(n0 + row, N - 1) * (u32)KB + 16u * (gsel[k] & 1u);
-    aoff[k] = (u32)min(m0 + row, M - 1) * (u32)KB + 16u * (gsel[k] & 1u);
+    woff[k] = (u32)(min(n0 + row, N - 1) - n0) * (u32)KB + 16u * (gsel[k] & 1u);
+    aoff[k] = (u32)(min(m0 + row, M - 1) - m0) * (u32)KB + 16u * (gsel[k] & 1u);
   }
   // group pair q -> stage buffer buf (the second group clamped to the last one)
   auto dma_pair = [&](int q, int buf) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const u32 col = 32u * (u32)min(2 * (qb + q) + (int)(gsel[k] >> 1), G - 1);
-      dma16(p.w_codes + (woff[k] + col), wtile(buf) + 4096 * k + 1024 * wave);
-      dma16(p.act_codes + (aoff[k] + col), atile(buf) + 4096 * k + 1024 * wave);
+      dma16(wbase + (woff[k] + col), wtile(buf) + 4096 * k + 1024 * wave);
+      dma16(abase + (aoff[k] + col), atile(buf) + 4096 * k + 1024 * wave);
     }
   };
 
@@ -235,9 +238,10 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
   // scale role: threads 0..127 -> token slot tid, 128..255 -> weight row tid-128
   const bool s_is_act = tid < kBM;
   const int s_idx = s_is_act ? tid : tid - kBM;
-  const uint16_t* sbase = s_is_act ? p.act_scales : p.w_scales;  // wave-uniform
-  const u32 soff =
-      (u32)(s_is_act ? min(m0 + (kFp4 ? s_idx : sx_token(s_idx)), M - 1) : min(n0 + s_idx, N - 1)) * (u32)G;
+  // wave-uniform base row of the workgroup's scales (64-bit), 32-bit offsets within
+  const uint16_t* sbase = s_is_act ? p.act_scales + (size_t)m0 * (size_t)G : p.w_scales + (size_t)n0 * (size_t)G;
+  const u32 soff = (u32)(s_is_act ? min(m0 + (kFp4 ? s_idx : sx_token(s_idx)), M - 1) - m0
+                                  : min(n0 + s_idx, N - 1) - n0) * (u32)G;
   // register ring of raw bf16 scales, pair q in slot q % 3
   u32 slo[3], shi[3];
   auto load_scales = [&](int q, int k) {
@@ -326,7 +330,9 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
           for (int v = 0; v < 4; ++v) {
             const int n = n0 + wn * 64 + 16 * i + 4 * lseg + v;
             const int a = acc[v];
-            if (m < M && n < N) p.acc[((size_t)m * N + n) * G + g] = (a - kMagicBits) >> 8;
+            if (m >= p.acc_m_lo && m < p.acc_m_hi && n >= p.acc_n_lo && n < p.acc_n_hi)
+              p.acc[((size_t)(m - p.acc_m_lo) * (size_t)(p.acc_n_hi - p.acc_n_lo) + (size_t)(n - p.acc_n_lo)) * G + g] =
+                  (a - kMagicBits) >> 8;
           }
         }
     } else {
@@ -720,30 +726,53 @@ int pick_splits(int tiles, int pairs, int cus) {
 }
 
 std::atomic<int> g_splits{0};  // test hook (0 = automatic)
+std::atomic<int> g_path{0};    // test hook: 0 = by shape, 1 = tiled, 2 = few-token kernel
+
+// How call 2 runs a shape on the current device.
+struct GemmPlan {
+  bool skinny;  // the few-token kernel
+  int tiles;    // 128 x 128 output tiles (tiled kernel)
+  int splits;   // K-splits per tile
+  int occ;      // workgroups per CU the tiled kernel is built for (2 or 3)
+};
+
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int epilogue, bool fp4) {
+  GemmPlan g{false, (int)(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM)), 1, 3};
+  const int path = g_path.load(std::memory_order_relaxed);
+  if (!fp4 && epilogue != kEpilogueQkv && path != 1 && skinny_supported(M, N, K) &&
+      (path == 2 || M <= kSkinnyMaxM)) {
+    g.skinny = true;
+    return g;
+  }
+  const int cus = current_cus();
+  const int pairs = (int)((K / 64 + 1) / 2);
+  if (epilogue != kEpilogueQkv) {
+    const int forced = g_splits.load(std::memory_order_relaxed);
+    g.splits = forced > 0 ? std::min(forced, pairs) : pick_splits(g.tiles, pairs, cus);
+    if ((size_t)g.tiles * 4 > kWsMaxCounters) g.splits = 1;  // one workspace counter per wave sub-tile
+  }
+  g.occ = pick_occupancy(g.tiles * g.splits, cus);
+  return g;
+}
+
+// K-split partials: one arrival counter per wave sub-tile, and per tile and
+// split four 64 x 64 fp32 sub-tiles.
+size_t split_counters(const GemmPlan& g) { return g.splits > 1 ? (size_t)g.tiles * 4 : 0; }
+size_t split_bytes(const GemmPlan& g) { return g.splits > 1 ? (size_t)g.tiles * g.splits * 4 * 4096 * 4 : 0; }
 
 template <bool kDump, bool kFp4 = false>
-hipError_t launch(GemmArgs<kDump> a, hipStream_t stream) {
-  const int tiles = ((a.N + kBN - 1) / kBN) * ((a.M + kBM - 1) / kBM);
+hipError_t launch(GemmArgs<kDump> a, const GemmPlan& g, Workspace ws, hipStream_t stream) {
   auto kern = w4a4_gemm_kernel<kDump, kDump ? 1 : 3, kFp4>;
   size_t pad = 0;
-  a.splits = 1;
+  a.splits = kDump ? 1 : g.splits;
   if constexpr (!kDump) {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const int pairs = (a.K / 64 + 1) / 2;
-    if (a.epilogue != kEpilogueQkv) {
-      const int forced = g_splits.load(std::memory_order_relaxed);
-      a.splits = forced > 0 ? std::min(forced, pairs) : pick_splits(tiles, pairs, cus);
+    const size_t nc = split_counters(g);
+    if (nc > 0) {
+      if (ws.bytes < ws_bytes(nc, split_bytes(g))) return hipErrorInvalidValue;
+      a.count = ws_counters(ws);
+      a.part = static_cast<float*>(ws_scratch(ws));
     }
-    if (a.splits > 1) {
-      void* part = nullptr;
-      hipError_t e = stream_workspace(stream, (size_t)tiles * 4, (size_t)tiles * a.splits * 4 * 4096 * 4,
-                                      &a.count, &part);
-      if (e != hipSuccess) return e;
-      a.part = static_cast<float*>(part);
-    }
-    if (pick_occupancy(tiles * a.splits, cus) == 2) {
+    if (g.occ == 2) {
       kern = w4a4_gemm_kernel<kDump, 2, kFp4>;
       // the lora tiles, and at least enough that only 2 workgroups fit a CU
       pad = max((size_t)(80 * 1024 - kStaticLds), (size_t)2 * kBN * a.r * 2);
@@ -752,61 +781,64 @@ hipError_t launch(GemmArgs<kDump> a, hipStream_t stream) {
       if (e != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL(kern, dim3(tiles, a.splits), dim3(kThreads), pad, stream, a);
+  hipLaunchKernelGGL(kern, dim3(g.tiles, a.splits), dim3(kThreads), pad, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-namespace {
-std::atomic<int> g_path{0};
-}  // namespace
-
 void set_gemm_path_override(int path) { g_path.store(path, std::memory_order_relaxed); }
+
+void set_gemm_splits_override(int splits) { g_splits.store(std::max(0, splits), std::memory_order_relaxed); }
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r, int epilogue, bool fp4) {
+  (void)r;
+  if (M <= 0) return 0;
+  const GemmPlan g = gemm_plan(M, N, K, epilogue, fp4);
+  if (g.skinny) return 0;
+  return ws_bytes(split_counters(g), split_bytes(g));
+}
 
 hipError_t launch_fp4_gemm_lora_up(const uint8_t* act_codes, const uint8_t* act_scales,
                                   const uint8_t* w_codes, const uint8_t* w_scales,
                                   const uint16_t* lora_act, const uint16_t* lora_up,
                                   const uint16_t* bias, int64_t M, int64_t N, int64_t K, int64_t r,
-                                  int epilogue, uint16_t* y, hipStream_t stream) {
+                                  int epilogue, uint16_t* y, Workspace ws, hipStream_t stream) {
   if (K % 128 != 0 || epilogue == kEpilogueQkv) return hipErrorInvalidValue;
   // the E8M0 byte pairs of a 64-group travel like the int4 path's bf16 scale
   GemmArgs<false> a{act_codes, reinterpret_cast<const uint16_t*>(act_scales), w_codes,
                     reinterpret_cast<const uint16_t*>(w_scales), lora_act, lora_up, bias,
-                    y, nullptr, (int)M, (int)N, (int)K, (int)r, epilogue, QkvEpilogue{}, 1,
+                    y, nullptr, 0, 0, 0, 0, (int)M, (int)N, (int)K, (int)r, epilogue, QkvEpilogue{}, 1,
                     nullptr, nullptr};
-  return launch<false, true>(a, stream);
+  return launch<false, true>(a, gemm_plan(M, N, K, epilogue, true), ws, stream);
 }
-
-void set_gemm_splits_override(int splits) { g_splits.store(std::max(0, splits), std::memory_order_relaxed); }
 
 hipError_t launch_w4a4_gemm_lora_up(const uint8_t* act_codes, const uint16_t* act_scales,
                                     const uint8_t* w_codes, const uint16_t* w_scales,
                                     const uint16_t* lora_act, const uint16_t* lora_up,
                                     const uint16_t* bias, int64_t M, int64_t N, int64_t K,
                                     int64_t r, int epilogue, const QkvEpilogue* qkv, uint16_t* y,
-                                    int32_t* acc_dump, hipStream_t stream) {
+                                    const DumpWindow& dump, Workspace ws, hipStream_t stream) {
   // Few tokens: the 128 x 128 tile grid leaves most CUs idle; the K-split
   // kernel streams the weights with every CU instead.
-  const int path = g_path.load(std::memory_order_relaxed);
-  if (epilogue != kEpilogueQkv && path != 1 && skinny_supported(M, N, K) &&
-      (path == 2 || M <= kSkinnyMaxM))
+  const GemmPlan g = gemm_plan(M, N, K, epilogue, false);
+  if (g.skinny)
     return launch_w4a4_gemm_skinny(act_codes, act_scales, w_codes, w_scales, lora_act, lora_up,
-                                   bias, M, N, K, r, epilogue, y, acc_dump, stream);
-  if (acc_dump != nullptr) {
+                                   bias, M, N, K, r, epilogue, y, dump, stream);
+  if (dump.acc != nullptr) {
     GemmArgs<true> a{act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,
-                     y, acc_dump, (int)M, (int)N, (int)K, 0, kEpilogueNone, QkvEpilogue{}, 1,
-                     nullptr, nullptr};
-    return launch<true>(a, stream);
+                     y, dump.acc, dump.m_lo, dump.m_hi, dump.n_lo, dump.n_hi, (int)M, (int)N, (int)K, 0,
+                     kEpilogueNone, QkvEpilogue{}, 1, nullptr, nullptr};
+    return launch<true>(a, g, Workspace{}, stream);
   }
   GemmArgs<false> a{act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,
-                    y, nullptr, (int)M, (int)N, (int)K, (int)r, epilogue, QkvEpilogue{}, 1,
+                    y, nullptr, 0, 0, 0, 0, (int)M, (int)N, (int)K, (int)r, epilogue, QkvEpilogue{}, 1,
                     nullptr, nullptr};
   if (epilogue == kEpilogueQkv) {
     if (qkv == nullptr || N % 384 != 0) return hipErrorInvalidValue;
     a.qkv = *qkv;
   }
-  return launch<false>(a, stream);
+  return launch<false>(a, g, ws, stream);
 }
 
 }  // namespace svdq

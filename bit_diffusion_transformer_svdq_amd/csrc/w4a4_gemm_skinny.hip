@@ -33,7 +33,7 @@
 
 #include <algorithm>
 
-#include "svdq_internal.h"
+#include "svdq_device.h"
 
 namespace svdq {
 namespace {
@@ -78,7 +78,8 @@ struct SkinnyArgs {
   const uint16_t* lu;     // lora_up [N, r] bf16
   const uint16_t* bias;   // [N] bf16 or null
   uint16_t* y;            // [M, N] bf16
-  int32_t* dump;          // [M, N, G] int32 (debug variant)
+  int32_t* dump;          // window [m_hi - m_lo, n_hi - n_lo, G] int32 (debug variant)
+  int m_lo, m_hi, n_lo, n_hi;
   int M, N, K, G, r;
   int epilogue;           // 0: none, 1: GELU (tanh form) after the bias
 };
@@ -235,7 +236,9 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkinnyArgs<kDump> a
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
               const int m = m0 + 16 * i + l16, n = n0 + 16 * j + 4 * lq + v;
-              if (m < a.M && n < a.N) a.dump[((size_t)m * a.N + n) * G + g] = (acc[v] - kMagicBits) >> 8;
+              if (m >= a.m_lo && m < a.m_hi && n >= a.n_lo && n < a.n_hi)
+                a.dump[((size_t)(m - a.m_lo) * (size_t)(a.n_hi - a.n_lo) + (size_t)(n - a.n_lo)) * G + g] =
+                    (acc[v] - kMagicBits) >> 8;
             }
           } else {
             // bit_cast the whole vector: a bit_cast of one ext-vector element
@@ -385,20 +388,6 @@ hipError_t launch_n16(const SkinnyArgs<kDump>& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int cus_of_current_device() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) { (void)hipGetLastError(); return 256; }
-  if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev];
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
-    (void)hipGetLastError();
-    n = 256;
-  }
-  if (dev >= 0 && dev < 64) cache[dev] = n;
-  return n;
-}
-
 // rows of 16 per workgroup: one wave of workgroups over the CUs where possible,
 // fewer rows per workgroup cost more activation re-reads
 int pick_n16(int N, int M, int G, int r, int cus) {
@@ -429,7 +418,7 @@ hipError_t launch_skinny(const SkinnyArgs<kDump>& a, hipStream_t stream) {
   if constexpr (kDump) {
     return launch_n16<1, true>(a, stream);  // debug path: smallest register set
   } else {
-    switch (pick_n16(a.N, a.M, a.G, a.r, cus_of_current_device())) {
+    switch (pick_n16(a.N, a.M, a.G, a.r, current_cus())) {
       case 1: return launch_n16<1, false>(a, stream);
       case 2: return launch_n16<2, false>(a, stream);
       default: return launch_n16<3, false>(a, stream);
@@ -449,15 +438,16 @@ hipError_t launch_w4a4_gemm_skinny(const uint8_t* act_codes, const uint16_t* act
                                    const uint8_t* w_codes, const uint16_t* w_scales,
                                    const uint16_t* lora_act, const uint16_t* lora_up,
                                    const uint16_t* bias, int64_t M, int64_t N, int64_t K,
-                                   int64_t r, int epilogue, uint16_t* y, int32_t* acc_dump,
+                                   int64_t r, int epilogue, uint16_t* y, const DumpWindow& dump,
                                    hipStream_t stream) {
-  if (acc_dump != nullptr) {
+  if (dump.acc != nullptr) {
     SkinnyArgs<true> a{act_codes, act_scales, w_codes, w_scales, nullptr, nullptr, nullptr,
-                       nullptr, acc_dump, (int)M, (int)N, (int)K, (int)(K / 64), 0, 0};
+                       nullptr, dump.acc, dump.m_lo, dump.m_hi, dump.n_lo, dump.n_hi,
+                       (int)M, (int)N, (int)K, (int)(K / 64), 0, 0};
     return launch_skinny<true>(a, stream);
   }
   SkinnyArgs<false> a{act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,
-                      y, nullptr, (int)M, (int)N, (int)K, (int)(K / 64), (int)r, epilogue};
+                      y, nullptr, 0, 0, 0, 0, (int)M, (int)N, (int)K, (int)(K / 64), (int)r, epilogue};
   return launch_skinny<false>(a, stream);
 }
 

@@ -28,10 +28,25 @@
  *    consecutive k.  Only group_size == 64 and int4 are supported (the int4
  *    scheme's group size in the quantization config on mind-verse.de, section
  *    "Native Ladefunktion in Diffusers").
- *  - Ownership: the caller allocates and frees every buffer; the library never
- *    allocates device memory and keeps no state besides a per-device
- *    capability cache.  Device pointers must be 16-byte aligned.  Outputs must
- *    not overlap inputs or each other.
+ *  - Ownership: the caller allocates and frees every buffer, including the
+ *    device workspace some calls need (below); the library allocates no device
+ *    memory and keeps no state besides a per-device capability cache and the
+ *    test hooks' settings.  Device pointers must be 16-byte aligned.  An output
+ *    must not overlap an input, another output or the workspace
+ *    (INVALID_VALUE); inputs may share memory.
+ *  - Workspace: calls 1 and 2 may split K over several workgroups whose fp32
+ *    partial sums meet in device memory.  svdq_*_workspace_size gives the
+ *    bytes a shape needs on the current device (0: none; NULL may then be
+ *    passed).  A workspace starts with a fixed 1 MiB region of arrival
+ *    counters, then scratch.  The caller zero-fills a workspace once, before
+ *    its first use; every call leaves its counters back at zero and writes
+ *    scratch before reading it, so one workspace serves any later call, of any
+ *    shape whose query fits its capacity, that is ordered after the previous
+ *    one (same stream, or an explicit dependency).  Calls that may run at the same time need distinct
+ *    workspaces.  The caller must not write to it between calls.  A call whose
+ *    workspace is NULL or smaller than the query returns INVALID_VALUE before
+ *    any launch.  The size depends on the test hooks below; query after
+ *    setting them.
  *  - Empty batch: M == 0 is a successful no-op once the dimensions are valid;
  *    nothing is read or written, so the pointers may be NULL.
  *  - Errors: argument and shape errors are returned synchronously, before any
@@ -54,7 +69,8 @@ extern "C" {
 
 typedef enum svdq_status {
   SVDQ_STATUS_SUCCESS = 0,
-  SVDQ_STATUS_INVALID_VALUE = 1,   /* null required pointer, negative dim, misalignment */
+  SVDQ_STATUS_INVALID_VALUE = 1,   /* null required pointer, negative dim, misalignment,
+                                      overlapping output, missing or short workspace */
   SVDQ_STATUS_NOT_SUPPORTED = 2,   /* group_size != 64, K % 64, N % 64, r not in {0,16,...,128} */
   SVDQ_STATUS_ARCH_MISMATCH = 3,   /* current device is not gfx950 */
   SVDQ_STATUS_NO_DEVICE = 4,       /* no HIP device visible */
@@ -98,31 +114,32 @@ svdq_status svdq_check_device(int device);
  *   smooth     device, fp32 [K]   lambda (X is divided by it, W multiplied)
  *   lora_down  device, bf16 [r, K]; may be NULL iff r == 0
  *   M >= 0 (M == 0 is a no-op), K > 0 with K % 64 == 0, r in {0,16,...,128},
- *   group_size == 64
+ *   group_size == 64; M <= 2^24 and M * K <= 2^40, and M <= 2^22 when r > 0
+ *   and K > 4096 (NOT_SUPPORTED beyond)
  *   act_codes  device out, u8   [M, K/2]
  *   act_scales device out, bf16 [M, K/64]
  *   lora_act   device out, bf16 [M, r]; may be NULL iff r == 0
+ *   workspace  device scratch of svdq_quantize_act_workspace_size(M, K, r) bytes
+ *              (see Conventions; may be NULL when that is 0), workspace_bytes its size
  *   stream     hipStream_t or NULL
  * Codes and scales are exactly defined (bit-exact to the rule above); lora_act
- * may differ from a float64 evaluation by one bf16 ulp (summation order).
- * Workspace: when K is split over several workgroups, the fp32 partial sums of
- * lora_act go through a device workspace that the library owns, one per
- * (device, stream), allocated and zero-filled on first use and grown when a
- * call needs more.  An outgrown workspace is kept until the process ends, so a
- * graph captured before the growth stays valid.  The first call on a stream
- * for a given size therefore allocates: make it outside graph capture; a call
- * that would allocate while `stream` is capturing returns HIP_ERROR
- * (hipErrorStreamCaptureUnsupported) and enqueues nothing.  Calls that share a
- * stream are ordered by it; calls on different streams use different
- * workspaces.  A graph captured on a stream uses that stream's workspace:
- * replay it on the same stream (or make sure no other launch using that
- * workspace runs at the same time).  The result of a call does not depend on timing (partials are
- * added in a fixed order).
+ * may differ from a float64 evaluation by one bf16 ulp (summation order).  When
+ * K is split over several workgroups, their fp32 partial sums of lora_act meet
+ * in the workspace and are added in a fixed order, so the result does not
+ * depend on timing.
  */
 svdq_status svdq_quantize_act_lora_down(
     const void* x, const float* smooth, const void* lora_down,
     int64_t M, int64_t K, int64_t r, int64_t group_size,
-    void* act_codes, void* act_scales, void* lora_act, void* stream);
+    void* act_codes, void* act_scales, void* lora_act,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes call 1 (either element format) needs for (M, K, r) on the
+ * current device, with the current test hooks; 0 when it needs none and for
+ * shapes the call rejects (the call reports those).  Host only, no launch.
+ */
+size_t svdq_quantize_act_workspace_size(int64_t M, int64_t K, int64_t r);
 
 /*
  * Test hook for call 1: forces its work split for every later call in this
@@ -150,8 +167,9 @@ svdq_status svdq_debug_set_gemm_path(int path);
  * for every later call in this process (0 = chosen by shape; clipped to the
  * number of group pairs K/128, rounded up).  With splits > 1 each workgroup
  * runs a run of whole quant groups of its tile and the fp32 partial tiles are
- * added in split order through the stream's workspace, so Y may differ from
- * the unsplit result in fp32 rounding order but not between runs.  Ignored by
+ * added in split order through the caller's workspace (query its size after
+ * setting the hook), so Y may differ from the unsplit result in fp32 rounding
+ * order but not between runs.  Ignored by
  * the QKV epilogue and the accumulator dump.  Returns INVALID_VALUE outside
  * 0..64.
  */
@@ -176,18 +194,26 @@ svdq_status svdq_debug_set_gemm_splits(int splits);
  *   M >= 0 (0 is a no-op), N > 0 with N % 64 == 0, K > 0 with K % 64 == 0,
  *   r in {0,16,...,128}, group_size == 64
  *   y          device out, bf16 [M, N]
+ *   workspace  device scratch of svdq_w4a4_gemm_workspace_size(M, N, K, r) bytes
+ *              (see Conventions; may be NULL when that is 0), workspace_bytes its size
  * With few output tiles (fewer than two 128 x 128 tiles per compute unit) the
  * tiled kernel splits K over several workgroups per tile; their fp32 partial
- * tiles go through the stream's workspace (the one call 1 uses, same rules:
- * allocated or grown on first need, never during graph capture) and are added
- * in a fixed order, so Y does not depend on timing.
+ * tiles meet in the workspace and are added in a fixed order, so Y does not
+ * depend on timing.
  */
 svdq_status svdq_w4a4_gemm_lora_up(
     const void* act_codes, const void* act_scales,
     const void* w_codes, const void* w_scales,
     const void* lora_act, const void* lora_up, const void* bias,
     int64_t M, int64_t N, int64_t K, int64_t r, int64_t group_size,
-    void* y, void* stream);
+    void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes call 2 (svdq_w4a4_gemm_lora_up and _ex, any epilogue) needs
+ * for (M, N, K, r) on the current device, with the current test hooks; 0 when
+ * it needs none and for shapes the call rejects.  Host only, no launch.
+ */
+size_t svdq_w4a4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t r);
 
 /*
  * Output epilogues of call 2, applied to y + b before the bf16 rounding.
@@ -216,7 +242,7 @@ svdq_status svdq_w4a4_gemm_lora_up_ex(
     const void* w_codes, const void* w_scales,
     const void* lora_act, const void* lora_up, const void* bias,
     int64_t M, int64_t N, int64_t K, int64_t r, int64_t group_size,
-    int epilogue, void* y, void* stream);
+    int epilogue, void* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Call 2 with the fused QKV epilogue of a diffusion transformer's attention:
@@ -241,7 +267,8 @@ svdq_status svdq_w4a4_gemm_lora_up_ex(
  *   y          device out, bf16 [M, N]
  * Other arguments, errors and the M == 0 rule as for svdq_w4a4_gemm_lora_up;
  * NOT_SUPPORTED for another head_dim or N, INVALID_VALUE for a bad eps or a
- * null or misaligned table.  Runs on the tiled kernel for every M.
+ * null or misaligned table.  Runs unsplit on the tiled kernel for every M, so
+ * it takes no workspace.
  */
 svdq_status svdq_w4a4_gemm_qkv_norm_rope(
     const void* act_codes, const void* act_scales,
@@ -252,15 +279,21 @@ svdq_status svdq_w4a4_gemm_qkv_norm_rope(
     const float* rope_cos, const float* rope_sin, void* y, void* stream);
 
 /*
- * Test hook for call 2: runs the same main loop as svdq_w4a4_gemm_lora_up and
- * writes the int32 group accumulators acc_g[m,n] (the exact integer sums
- * sum_{k in g} q_x q_w, with any internal scaling removed) instead of Y.
- *   acc  device out, int32 [M, N, K/64]  (M * N * K/64 elements)
- * Same shape rules as call 2; no lora, scales or bias are read.
+ * Test hook for call 2: runs the same main loop as svdq_w4a4_gemm_lora_up (the
+ * kernel the shape and the path hook select) over the rows [m0, m0 + mc) and
+ * the 64-aligned column range around [n0, n0 + nc), and writes the int32 group
+ * accumulators of that window (the exact integer sums sum_{k in g} q_x q_w,
+ * any internal scaling removed) instead of Y:
+ *   acc  device out, int32 [mc, nc, K/64]:  acc[(i * nc + j) * K/64 + g]
+ *        = acc_g[m0 + i, n0 + j]
+ * Same shape rules as call 2; the window must lie inside [0, M) x [0, N)
+ * (INVALID_VALUE otherwise); an empty window is a no-op; mc * nc * K/64 above
+ * 2^31 is NOT_SUPPORTED.  No scales, lora or bias are read; no workspace.
  */
 svdq_status svdq_w4a4_group_acc_debug(
     const void* act_codes, const void* w_codes,
-    int64_t M, int64_t N, int64_t K, int64_t group_size,
+    int64_t M, int64_t N, int64_t K,
+    int64_t m0, int64_t mc, int64_t n0, int64_t nc,
     int32_t* acc, void* stream);
 
 /*
@@ -288,18 +321,23 @@ svdq_status svdq_w4a4_group_acc_debug(
  *   matrix core (v_mfma_scale_f32_16x16x128_f8f6f4, the block scales applied
  *   there); w_codes u8 [N, K/2] and w_scales u8 [N, K/32] from
  *   svdq_pack_weights_fp4; epilogue SVDQ_EPILOGUE_NONE or _GELU_TANH; K % 128
- *   == 0; other arguments and errors as for svdq_w4a4_gemm_lora_up_ex.
+ *   == 0; workspace of svdq_fp4_gemm_workspace_size(M, N, K, r) bytes; other
+ *   arguments and errors as for svdq_w4a4_gemm_lora_up_ex.
+ * Call 1's workspace is svdq_quantize_act_workspace_size(M, K, r), as for the
+ * int4 call.
  */
 svdq_status svdq_quantize_act_lora_down_fp4(
     const void* x, const float* smooth, const void* lora_down,
     int64_t M, int64_t K, int64_t r,
-    void* act_codes, void* act_scales, void* lora_act, void* stream);
+    void* act_codes, void* act_scales, void* lora_act,
+    void* workspace, size_t workspace_bytes, void* stream);
 svdq_status svdq_fp4_gemm_lora_up(
     const void* act_codes, const void* act_scales,
     const void* w_codes, const void* w_scales,
     const void* lora_act, const void* lora_up, const void* bias,
     int64_t M, int64_t N, int64_t K, int64_t r, int epilogue,
-    void* y, void* stream);
+    void* y, void* workspace, size_t workspace_bytes, void* stream);
+size_t svdq_fp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t r);
 
 /*
  * AWQ W4A16 linear: 4-bit weights with 16-bit activations, the second kernel

@@ -17,8 +17,18 @@ from bit_diffusion_transformer_svdq_amd._lib import (ARCH_MISMATCH, INVALID_VALU
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "svdq.h")
-FAKE = ctypes.c_void_p(0x10000)     # non-null, 16-byte aligned, never dereferenced
-FAKE_ODD = ctypes.c_void_p(0x10008)
+# Fake device pointers, never dereferenced: 16-byte aligned and far apart, so
+# buffers of any tested size stay disjoint (the entry points reject overlapping
+# outputs).  FAKE_ODD is misaligned.
+_SPACING = 1 << 40
+
+
+def P(i: int) -> ctypes.c_void_p:
+    return ctypes.c_void_p((i + 1) * _SPACING)
+
+
+FAKE = P(0)
+FAKE_ODD = ctypes.c_void_p(P(30).value + 8)
 
 
 def _declared_functions():
@@ -54,19 +64,21 @@ def test_status_strings_and_version():
 
 
 def _quant(**kw):
-    a = dict(x=FAKE, smooth=FAKE, lora_down=FAKE, M=64, K=256, r=16, g=64,
-             codes=FAKE, scales=FAKE, la=FAKE, stream=None)
+    a = dict(x=P(1), smooth=P(2), lora_down=P(3), M=64, K=256, r=16, g=64,
+             codes=P(4), scales=P(5), la=P(6), ws=P(9), wsb=1 << 30, stream=None)
     a.update(kw)
     return lib().svdq_quantize_act_lora_down(a["x"], a["smooth"], a["lora_down"], a["M"], a["K"], a["r"],
-                                             a["g"], a["codes"], a["scales"], a["la"], a["stream"])
+                                             a["g"], a["codes"], a["scales"], a["la"], a["ws"], a["wsb"],
+                                             a["stream"])
 
 
 def _gemm(**kw):
-    a = dict(ac=FAKE, asc=FAKE, wc=FAKE, ws=FAKE, la=FAKE, lu=FAKE, bias=FAKE, M=64, N=256, K=256,
-             r=16, g=64, y=FAKE, stream=None)
+    a = dict(ac=P(1), asc=P(2), wc=P(3), ws_=P(4), la=P(5), lu=P(6), bias=P(7), M=64, N=256, K=256,
+             r=16, g=64, y=P(8), ws=P(9), wsb=1 << 30, stream=None)
     a.update(kw)
-    return lib().svdq_w4a4_gemm_lora_up(a["ac"], a["asc"], a["wc"], a["ws"], a["la"], a["lu"], a["bias"],
-                                        a["M"], a["N"], a["K"], a["r"], a["g"], a["y"], a["stream"])
+    return lib().svdq_w4a4_gemm_lora_up(a["ac"], a["asc"], a["wc"], a["ws_"], a["la"], a["lu"], a["bias"],
+                                        a["M"], a["N"], a["K"], a["r"], a["g"], a["y"], a["ws"], a["wsb"],
+                                        a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -98,7 +110,7 @@ def test_quantize_argument_errors(kw, status):
     (dict(ac=None), INVALID_VALUE),
     (dict(wc=None), INVALID_VALUE),
     (dict(asc=None), INVALID_VALUE),
-    (dict(ws=None), INVALID_VALUE),
+    (dict(ws_=None), INVALID_VALUE),
     (dict(y=None), INVALID_VALUE),
     (dict(la=None), INVALID_VALUE),
     (dict(lu=None), INVALID_VALUE),
@@ -125,8 +137,8 @@ def test_gemm_epilogue_argument():
     def ex(ep, **kw):
         a = dict(M=64)
         a.update(kw)
-        return L.svdq_w4a4_gemm_lora_up_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["M"], 256, 256,
-                                           16, 64, ep, FAKE, None)
+        return L.svdq_w4a4_gemm_lora_up_ex(P(1), P(2), P(3), P(4), P(5), P(6), P(7), a["M"], 256, 256,
+                                           16, 64, ep, P(8), P(9), 1 << 30, None)
     for bad in (-1, 2, 7):
         assert ex(bad) == INVALID_VALUE
         assert b"epilogue" in L.svdq_last_error()
@@ -140,9 +152,9 @@ def test_gemm_epilogue_argument():
 def test_qkv_entry_point_argument_errors():
     L = lib()
 
-    def qkv(M=64, N=768, head_dim=128, eps=1e-6, qn=FAKE, cos=FAKE):
-        return L.svdq_w4a4_gemm_qkv_norm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, M, N, 256, 16, 64,
-                                              head_dim, qn, FAKE, eps, cos, FAKE, FAKE, None)
+    def qkv(M=64, N=768, head_dim=128, eps=1e-6, qn=P(8), cos=P(10), y=P(12)):
+        return L.svdq_w4a4_gemm_qkv_norm_rope(P(1), P(2), P(3), P(4), P(5), P(6), P(7), M, N, 256, 16, 64,
+                                              head_dim, qn, P(9), eps, cos, P(11), y, None)
     assert qkv(head_dim=64) == NOT_SUPPORTED
     assert qkv(N=512) == NOT_SUPPORTED
     assert qkv(N=96) == NOT_SUPPORTED
@@ -152,6 +164,8 @@ def test_qkv_entry_point_argument_errors():
     assert qkv(cos=FAKE_ODD) == INVALID_VALUE
     assert qkv(M=0, qn=None, cos=None) == SUCCESS
     assert qkv(M=0, N=512) == NOT_SUPPORTED
+    assert qkv(y=P(10)) == INVALID_VALUE            # output over an input table
+    assert b"overlap" in L.svdq_last_error()
     if not _gpu_visible():
         assert qkv() == NO_DEVICE
 
@@ -159,8 +173,8 @@ def test_qkv_entry_point_argument_errors():
 def test_awq_entry_points_argument_errors():
     L = lib()
 
-    def awq(M=4, N=64, K=256, g=64, x=FAKE, zeros=FAKE, bias=FAKE):
-        return L.svdq_awq_w4a16_gemm(x, FAKE, FAKE, FAKE, zeros, bias, M, N, K, g, FAKE, None)
+    def awq(M=4, N=64, K=256, g=64, x=P(1), zeros=P(5), bias=P(6), y=P(7)):
+        return L.svdq_awq_w4a16_gemm(x, P(2), P(3), P(4), zeros, bias, M, N, K, g, y, None)
     assert awq(N=48) == NOT_SUPPORTED
     assert awq(K=96) == NOT_SUPPORTED
     assert awq(g=128) == NOT_SUPPORTED
@@ -172,14 +186,15 @@ def test_awq_entry_points_argument_errors():
     assert awq(zeros=None) == INVALID_VALUE
     assert awq(bias=FAKE_ODD) == INVALID_VALUE
     assert awq(M=0, x=None, zeros=None) == SUCCESS
+    assert awq(y=P(3)) == INVALID_VALUE                # output over the codes
     if not _gpu_visible():
         assert awq() == NO_DEVICE
         assert awq(M=1, K=16384) == NO_DEVICE            # the largest staged shapes pass validation
         assert awq(M=4, K=8192) == NO_DEVICE
         assert awq(M=40, K=4096) == NO_DEVICE
 
-    def stacked(Ls=3, M=4, N=64, K=256, g=64, x=FAKE, bias=FAKE):
-        return L.svdq_awq_w4a16_gemm_stacked(x, FAKE, FAKE, FAKE, FAKE, bias, Ls, M, N, K, g, FAKE, None)
+    def stacked(Ls=3, M=4, N=64, K=256, g=64, x=P(1), bias=P(6)):
+        return L.svdq_awq_w4a16_gemm_stacked(x, P(2), P(3), P(4), P(5), bias, Ls, M, N, K, g, P(7), None)
     assert stacked(Ls=-1) == INVALID_VALUE
     assert stacked(Ls=65536) == NOT_SUPPORTED
     assert stacked(N=48) == NOT_SUPPORTED
@@ -201,11 +216,12 @@ def test_awq_entry_points_argument_errors():
 def test_fp4_entry_points_argument_errors():
     L = lib()
 
-    def q(M=64, K=256, r=16, x=FAKE):
-        return L.svdq_quantize_act_lora_down_fp4(x, FAKE, FAKE, M, K, r, FAKE, FAKE, FAKE, None)
+    def q(M=64, K=256, r=16, x=P(1)):
+        return L.svdq_quantize_act_lora_down_fp4(x, P(2), P(3), M, K, r, P(4), P(5), P(6), P(9), 1 << 30, None)
 
-    def g(M=64, N=256, K=256, r=16, ep=0, asc=FAKE):
-        return L.svdq_fp4_gemm_lora_up(FAKE, asc, FAKE, FAKE, FAKE, FAKE, FAKE, M, N, K, r, ep, FAKE, None)
+    def g(M=64, N=256, K=256, r=16, ep=0, asc=P(2)):
+        return L.svdq_fp4_gemm_lora_up(P(1), asc, P(3), P(4), P(5), P(6), P(7), M, N, K, r, ep, P(8),
+                                       P(9), 1 << 30, None)
     assert q(K=192) == NOT_SUPPORTED and g(K=192) == NOT_SUPPORTED
     assert q(x=None) == INVALID_VALUE and g(asc=None) == INVALID_VALUE
     assert g(ep=2) == INVALID_VALUE and g(N=96) == NOT_SUPPORTED
@@ -220,9 +236,20 @@ def test_fp4_entry_points_argument_errors():
 
 def test_debug_hook_argument_errors():
     L = lib()
-    assert L.svdq_w4a4_group_acc_debug(FAKE, FAKE, 4, 64, 64, 64, None, None) == INVALID_VALUE
-    assert L.svdq_w4a4_group_acc_debug(FAKE, FAKE, 4, 64, 96, 64, FAKE, None) == NOT_SUPPORTED
-    assert L.svdq_w4a4_group_acc_debug(FAKE, FAKE, 0, 64, 64, 64, FAKE, None) == SUCCESS
+
+    def dump(M=4, N=64, K=64, m0=0, mc=4, n0=0, nc=64, acc=P(3), ac=P(1)):
+        return L.svdq_w4a4_group_acc_debug(ac, P(2), M, N, K, m0, mc, n0, nc, acc, None)
+    assert dump(acc=None) == INVALID_VALUE
+    assert dump(K=96) == NOT_SUPPORTED
+    assert dump(M=0, mc=0) == SUCCESS
+    assert dump(m0=1) == INVALID_VALUE                 # window beyond the rows
+    assert dump(n0=60, nc=5) == INVALID_VALUE          # window beyond the columns
+    assert dump(mc=-1) == INVALID_VALUE
+    assert dump(mc=0) == SUCCESS                       # empty window: nothing to do
+    assert dump(acc=P(1)) == INVALID_VALUE             # window output over the codes
+    if not _gpu_visible():
+        assert dump() == NO_DEVICE
+        assert dump(M=100, N=256, m0=37, mc=5, n0=70, nc=3) == NO_DEVICE
 
 
 def test_quant_plan_hook_arguments():
@@ -263,6 +290,9 @@ def test_well_formed_calls_without_a_gpu_report_no_device():
     assert lib().svdq_check_device(0) in (NO_DEVICE, ARCH_MISMATCH)
     assert _quant() == NO_DEVICE
     assert _gemm() == NO_DEVICE
+    # inputs may share memory (only outputs must be disjoint)
+    assert _gemm(asc=P(1), wc=P(1)) == NO_DEVICE
+    assert _quant(smooth=P(1), lora_down=P(1)) == NO_DEVICE
     assert lib().svdq_check_device(-1) == INVALID_VALUE
 
 
@@ -287,3 +317,86 @@ def test_packer_argument_errors():
     st = L.svdq_pack_weights(w.ctypes.data_as(vp), lam.ctypes.data_as(vp), 4, 64, 8, 64, 0,
                              codes.ctypes.data_as(vp), sc.ctypes.data_as(vp), FAKE, FAKE)
     assert st == NOT_SUPPORTED   # rank larger than min(N, K)
+
+
+# ---- outputs that overlap, the caller's workspace, size limits ----
+
+@pytest.mark.parametrize("kw", [
+    dict(y=P(1)),                                        # Y over the activation codes
+    dict(y=ctypes.c_void_p(P(3).value + 4096)),          # Y starting inside the weight codes
+    dict(bias=ctypes.c_void_p(P(8).value + 64 * 256 * 2 - 16)),   # bias under Y's last bytes
+])
+def test_gemm_overlapping_output_is_rejected(kw):
+    assert _gemm(**kw) == INVALID_VALUE
+    assert b"overlap" in lib().svdq_last_error()
+
+
+@pytest.mark.parametrize("kw", [
+    dict(codes=P(1)),                                    # codes over x
+    dict(la=P(5)),                                       # two outputs on one buffer
+    dict(scales=ctypes.c_void_p(P(4).value + 64 * 128 - 16)),    # scales overlap the codes' tail
+])
+def test_quantize_overlapping_outputs_are_rejected(kw):
+    assert _quant(**kw) == INVALID_VALUE
+    assert b"overlap" in lib().svdq_last_error()
+
+
+def test_buffers_that_only_touch_are_accepted():
+    """codes [64, 128] end exactly where the scales begin: no overlap."""
+    if _gpu_visible():
+        pytest.skip("checks the no-GPU path")
+    assert _quant(scales=ctypes.c_void_p(P(4).value + 64 * 128)) == NO_DEVICE
+
+
+def test_workspace_size_queries_and_checks():
+    L = lib()
+    assert L.svdq_w4a4_gemm_workspace_size(4608, 12288, 3072, 32) == 0       # many tiles: no split
+    assert L.svdq_w4a4_gemm_workspace_size(0, 256, 256, 16) == 0
+    assert L.svdq_w4a4_gemm_workspace_size(64, 96, 256, 16) == 0             # rejected shape
+    assert L.svdq_quantize_act_workspace_size(64, 100, 16) == 0
+    L.svdq_debug_set_gemm_path(1)
+    L.svdq_debug_set_gemm_splits(2)
+    L.svdq_debug_set_quant_plan(4, 0)
+    try:
+        need_g = L.svdq_w4a4_gemm_workspace_size(64, 256, 256, 16)
+        need_q = L.svdq_quantize_act_workspace_size(64, 256, 16)
+        need_f = L.svdq_fp4_gemm_workspace_size(64, 256, 256, 16)
+        # the fixed 1 MiB counter region, then 2 tiles x 2 splits x 4 fp32 sub-tiles of 64 x 64
+        assert need_g == (1 << 20) + 2 * 2 * 4 * 4096 * 4
+        assert need_f == need_g
+        # 4 row tiles; partials [4 K-blocks][4 tiles][1][4][64] fp32
+        assert need_q == (1 << 20) + 4 * 4 * 1 * 4 * 64 * 4
+        assert L.svdq_quantize_act_workspace_size(64, 256, 0) == 0          # rank 0: nothing to reduce
+        assert _gemm(ws=None, wsb=0) == INVALID_VALUE and b"workspace" in L.svdq_last_error()
+        assert _gemm(ws=P(9), wsb=need_g - 1) == INVALID_VALUE
+        assert _gemm(ws=ctypes.c_void_p(P(9).value + 8), wsb=need_g) == INVALID_VALUE   # misaligned
+        assert _gemm(ws=ctypes.c_void_p(P(8).value + 1024), wsb=need_g) == INVALID_VALUE  # inside Y
+        assert _quant(ws=None, wsb=0) == INVALID_VALUE and b"workspace" in L.svdq_last_error()
+        assert _quant(ws=P(9), wsb=need_q - 16) == INVALID_VALUE
+        assert _quant(ws=P(1), wsb=need_q) == INVALID_VALUE                  # over the input x
+        if not _gpu_visible():
+            assert _gemm(ws=P(9), wsb=need_g) == NO_DEVICE
+            assert _gemm(ws=P(9), wsb=need_g + 4096) == NO_DEVICE
+            assert _quant(ws=P(9), wsb=need_q) == NO_DEVICE
+    finally:
+        L.svdq_debug_set_gemm_splits(0)
+        L.svdq_debug_set_gemm_path(0)
+        L.svdq_debug_set_quant_plan(0, 0)
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="checks the no-GPU path")
+def test_large_shapes_pass_validation_up_to_the_limits():
+    """Codes of 2^32 bytes and more (rows * K / 2) are addressed from 64-bit row
+    bases, so they pass validation; the stated limits are exact."""
+    big_k = 1 << 20
+    assert _gemm(M=1 << 13, N=1 << 13, K=big_k, r=0, la=None, lu=None) == NO_DEVICE     # 4 GiB codes each
+    assert _gemm(M=1 << 24, N=64, K=1024, r=0, la=None, lu=None) == NO_DEVICE         # 2^33 bytes of codes
+    assert _gemm(M=(1 << 24) + 1, N=64, K=1024, r=0, la=None, lu=None) == NOT_SUPPORTED
+    assert _gemm(M=64, N=(1 << 20) + 64, K=256) == NOT_SUPPORTED
+    assert _gemm(M=64, N=256, K=big_k + 64) == NOT_SUPPORTED
+    assert _quant(M=1 << 20, K=big_k, r=0, lora_down=None, la=None) == NO_DEVICE     # M * K = 2^40
+    assert _quant(M=(1 << 20) + 1, K=big_k, r=0, lora_down=None, la=None) == NOT_SUPPORTED
+    # K beyond 4096 is split over workgroups, one workspace counter per 16 rows (2^18 counters)
+    assert _quant(M=1 << 22, K=8192, r=16, wsb=1 << 40) == NO_DEVICE
+    assert _quant(M=(1 << 22) + 1, K=8192, r=16, wsb=1 << 40) == NOT_SUPPORTED
+    assert _quant(M=(1 << 22) + 1, K=4096, r=16, wsb=1 << 40) == NO_DEVICE

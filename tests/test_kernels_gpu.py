@@ -359,3 +359,85 @@ def test_split_shapes_parity(M, K, N):
     _check_quant(got, ref, packed["lora_down"])
     rows = [0, 1, 63, 64, 127, 128, 255, M - 2, M - 1]
     _check_y(got["y"], d, lam, packed, ref, rows=sorted(set(rows)))
+
+
+# ---- the boundary: accumulator windows and caller-owned workspaces ----
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_group_accumulator_window(path):
+    """The dump hook's window: rows and columns at offsets that are not tile
+    or 64 aligned, on both kernels."""
+    import bit_diffusion_transformer_svdq_amd as K
+    d, lam, packed = custom_case(300, 320, 448, 16, seed=91)
+    ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
+    K.debug_set_gemm_path(path)
+    try:
+        acc = K.w4a4_group_acc_debug(to_dev(ref["act_codes"]), to_dev(packed["w_codes"]),
+                                     rows=(37, 100), cols=(70, 129)).cpu().numpy()
+    finally:
+        K.debug_set_gemm_path(0)
+    want = O.group_accumulators(ref["act_codes"], packed["w_codes"], rows=np.arange(37, 137),
+                                cols=np.arange(70, 199))
+    assert np.array_equal(acc, want), np.argwhere(acc != want)[:5]
+
+
+def test_caller_workspace_reused_across_shapes():
+    """One zero-filled workspace given by the caller serves call 1 and call 2 of
+    several shapes in turn (forced K splits, so both use it); the results are
+    bit-identical to the calls with the binding's own workspace and match the
+    oracle."""
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K
+    cases = [custom_case(200, 1024, 192, 32, seed=92), custom_case(96, 3072, 320, 16, seed=93)]
+    K.debug_set_gemm_path(1)
+    K.debug_set_gemm_splits(3)
+    K.debug_set_quant_plan(4, 0)
+    try:
+        need = max(max(K.lib().svdq_quantize_act_workspace_size(d["spec"].M, d["spec"].K, p["lora_down"].shape[0]),
+                       K.lib().svdq_w4a4_gemm_workspace_size(d["spec"].M, d["spec"].N, d["spec"].K,
+                                                             p["lora_down"].shape[0]))
+                   for d, _, p in cases)
+        assert need > 0
+        ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        for rep in range(2):
+            for d, lam, p in cases:
+                x, lam_t = to_dev_bf16(d["x"]), to_dev(np.asarray(lam, np.float32))
+                down, up = to_dev_bf16(p["lora_down"]), to_dev_bf16(p["lora_up"])
+                wc, wsc, b = to_dev(p["w_codes"]), to_dev_bf16(p["w_scales"]), to_dev_bf16(d["bias"])
+                c1, s1, l1 = K.quantize_act_lora_down(x, lam_t, down, workspace=ws)
+                y1 = K.w4a4_gemm_lora_up(c1, s1, wc, wsc, l1, up, b, workspace=ws)
+                c2, s2, l2 = K.quantize_act_lora_down(x, lam_t, down)
+                y2 = K.w4a4_gemm_lora_up(c2, s2, wc, wsc, l2, up, b)
+                torch.cuda.synchronize()
+                assert torch.equal(c1, c2) and torch.equal(s1, s2) and torch.equal(l1, l2)
+                assert torch.equal(y1, y2), rep
+                ref = O.quantize_act_lora_down(d["x"], lam, p["lora_down"])
+                _check_quant({"act_codes": c1.cpu().numpy(), "act_scales": bf16_bits(s1),
+                              "lora_act": bf16_bits(l1)}, ref, p["lora_down"])
+                _check_y(bf16_bits(y1), d, lam, p, ref)
+        # every counter is back at zero after the calls
+        torch.cuda.synchronize()
+        assert int(ws[:1 << 20].view(torch.int32).abs().sum()) == 0
+    finally:
+        K.debug_set_quant_plan(0, 0)
+        K.debug_set_gemm_splits(0)
+        K.debug_set_gemm_path(0)
+
+
+def test_too_small_caller_workspace_is_refused():
+    import torch
+    import bit_diffusion_transformer_svdq_amd as K
+    d, lam, p = custom_case(200, 1024, 192, 32, seed=94)
+    K.debug_set_gemm_path(1)
+    K.debug_set_gemm_splits(2)
+    try:
+        ref = O.quantize_act_lora_down(d["x"], lam, p["lora_down"])
+        need = K.lib().svdq_w4a4_gemm_workspace_size(200, 192, 1024, 32)
+        small = torch.zeros(need - 256, dtype=torch.uint8, device="cuda")
+        with pytest.raises(K.SvdqError, match="workspace"):
+            K.w4a4_gemm_lora_up(to_dev(ref["act_codes"]), to_dev_bf16(ref["act_scales"]), to_dev(p["w_codes"]),
+                                to_dev_bf16(p["w_scales"]), to_dev_bf16(ref["lora_act"]),
+                                to_dev_bf16(p["lora_up"]), None, workspace=small)
+    finally:
+        K.debug_set_gemm_splits(0)
+        K.debug_set_gemm_path(0)

@@ -32,7 +32,7 @@ import numpy as np
 from ._lib import SvdqError, check, lib
 
 __all__ = ["SvdqError", "lib", "check_device", "quantize_act_lora_down", "w4a4_gemm_lora_up",
-           "mlp_pair", "w4a4_gemm_qkv_norm_rope", "w4a4_group_acc_debug", "debug_set_quant_plan", "debug_set_gemm_path", "debug_set_gemm_splits",
+           "mlp_pair", "w4a4_gemm_lora_up_noalloc", "w4a4_gemm_qkv_norm_rope", "w4a4_group_acc_debug", "debug_set_quant_plan", "debug_set_gemm_path", "debug_set_gemm_splits",
            "EPILOGUES", "smooth_from_absmax", "pack_weights", "awq_w4a16_gemm", "awq_w4a16_gemm_stacked",
            "awq_pack_weights",
            "quantize_act_lora_down_fp4", "fp4_gemm_lora_up", "pack_weights_fp4",
@@ -202,6 +202,34 @@ def w4a4_gemm_lora_up(act_codes, act_scales, w_codes, w_scales, lora_act=None, l
         _ptr(lora_act) if r else None, _ptr(lora_up) if r else None, _ptr(bias),
         M, N, K, r, GROUP_SIZE, EPILOGUES[epilogue], _ptr(y), ws, wsb, _stream(stream))
     check(st, "svdq_w4a4_gemm_lora_up_ex")
+    return y
+
+
+def w4a4_gemm_lora_up_noalloc(act_codes, act_scales, w_codes, w_scales, lora_act=None, lora_up=None,
+                              bias=None, out=None, stream=None, epilogue="none"):
+    """Call 2 through the library's fixed device scratch: no workspace and no
+    allocation by the library (``out`` must then be given by a caller that may
+    not allocate either).  Calls on one device must not overlap in time."""
+    torch = _torch()
+    M = act_codes.shape[0]
+    K = act_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    r = 0 if lora_up is None else lora_up.shape[1]
+    _need(act_codes, torch.uint8, (M, K // 2), "act_codes")
+    _need(act_scales, torch.bfloat16, (M, K // GROUP_SIZE), "act_scales")
+    _need(w_codes, torch.uint8, (N, K // 2), "w_codes")
+    _need(w_scales, torch.bfloat16, (N, K // GROUP_SIZE), "w_scales")
+    if r:
+        _need(lora_act, torch.bfloat16, (M, r), "lora_act")
+        _need(lora_up, torch.bfloat16, (N, r), "lora_up")
+    if bias is not None:
+        _need(bias, torch.bfloat16, (N,), "bias")
+    y = _out_y(out, M, N, act_codes.device)
+    st = lib().svdq_w4a4_gemm_lora_up_noalloc(
+        _ptr(act_codes), _ptr(act_scales), _ptr(w_codes), _ptr(w_scales),
+        _ptr(lora_act) if r else None, _ptr(lora_up) if r else None, _ptr(bias),
+        M, N, K, r, GROUP_SIZE, EPILOGUES[epilogue], _ptr(y), _stream(stream))
+    check(st, "svdq_w4a4_gemm_lora_up_noalloc")
     return y
 
 

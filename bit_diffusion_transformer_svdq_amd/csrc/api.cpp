@@ -369,6 +369,44 @@ svdq_status svdq_w4a4_gemm_lora_up_ex(const void* act_codes, const void* act_sca
                      epilogue, nullptr, false, y, workspace, workspace_bytes, stream);
 }
 
+svdq_status svdq_w4a4_gemm_lora_up_noalloc(const void* act_codes, const void* act_scales,
+                                           const void* w_codes, const void* w_scales,
+                                           const void* lora_act, const void* lora_up, const void* bias,
+                                           int64_t M, int64_t N, int64_t K, int64_t r, int64_t group_size,
+                                           int epilogue, void* y, void* stream) {
+  svdq_status s = validate_gemm(act_codes, w_codes, M, N, K, r, group_size);
+  if (s != SVDQ_STATUS_SUCCESS) return s;
+  if (epilogue != SVDQ_EPILOGUE_NONE && epilogue != SVDQ_EPILOGUE_GELU_TANH)
+    return fail(SVDQ_STATUS_INVALID_VALUE, "unknown epilogue %d", epilogue);
+  if (M == 0) return ok();
+  if (!act_scales || !w_scales || !y) return fail(SVDQ_STATUS_INVALID_VALUE, "null act_scales/w_scales/y");
+  if (r > 0 && (!lora_act || !lora_up))
+    return fail(SVDQ_STATUS_INVALID_VALUE, "r=%lld needs lora_act and lora_up", (long long)r);
+  if (!aligned16(act_scales) || !aligned16(w_scales) || !aligned16(y) ||
+      (bias && !aligned16(bias)) || (r > 0 && (!aligned16(lora_act) || !aligned16(lora_up))))
+    return fail(SVDQ_STATUS_INVALID_VALUE, "device pointers must be 16-byte aligned");
+  const size_t need = svdq::gemm_workspace_bytes(M, N, K, r, epilogue, false);
+  if (need > svdq::kStaticScratchBytes)
+    return fail(SVDQ_STATUS_NOT_SUPPORTED, "this shape needs %zu bytes of scratch; the fixed scratch holds %zu",
+                need, svdq::kStaticScratchBytes);
+  s = check_disjoint({{y, sz(M, N, 2), "y"}},
+                     {{act_codes, sz(M, K / 2), "act_codes"}, {act_scales, sz(M, K / 64, 2), "act_scales"},
+                      {w_codes, sz(N, K / 2), "w_codes"}, {w_scales, sz(N, K / 64, 2), "w_scales"},
+                      {r > 0 ? lora_act : nullptr, sz(M, r, 2), "lora_act"},
+                      {r > 0 ? lora_up : nullptr, sz(N, r, 2), "lora_up"}, {bias, sz(N, 2), "bias"}});
+  if (s != SVDQ_STATUS_SUCCESS) return s;
+  s = check_current_device();
+  if (s != SVDQ_STATUS_SUCCESS) return s;
+  hipError_t e = svdq::launch_w4a4_gemm_lora_up_static(
+      static_cast<const uint8_t*>(act_codes), static_cast<const uint16_t*>(act_scales),
+      static_cast<const uint8_t*>(w_codes), static_cast<const uint16_t*>(w_scales),
+      static_cast<const uint16_t*>(lora_act), static_cast<const uint16_t*>(lora_up),
+      static_cast<const uint16_t*>(bias), M, N, K, r, epilogue, static_cast<uint16_t*>(y),
+      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SVDQ_STATUS_HIP_ERROR, "gemm launch (fixed scratch): %s", hipGetErrorString(e));
+  return ok();
+}
+
 svdq_status svdq_w4a4_gemm_qkv_norm_rope(const void* act_codes, const void* act_scales,
                                          const void* w_codes, const void* w_scales,
                                          const void* lora_act, const void* lora_up, const void* bias,

@@ -44,6 +44,19 @@ constexpr size_t ws_bytes(size_t counters, size_t scratch) {
 inline uint32_t* ws_counters(const Workspace& w) { return static_cast<uint32_t*>(w.ptr); }
 inline void* ws_scratch(const Workspace& w) { return static_cast<uint8_t*>(w.ptr) + kWsCounterBytes; }
 
+// Call 2 without any allocation: the workspace is the library's fixed device
+// scratch (one per device, kStaticScratchBytes, counter region first), whose
+// device address is looked up once per device; the first call on a device
+// also clears its counters with a fill kernel on `stream`.  Calls that may
+// overlap on one device race on it.  The caller checks that the plan's
+// gemm_workspace_bytes fits.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+hipError_t launch_w4a4_gemm_lora_up_static(const uint8_t* act_codes, const uint16_t* act_scales,
+                                           const uint8_t* w_codes, const uint16_t* w_scales,
+                                           const uint16_t* lora_act, const uint16_t* lora_up,
+                                           const uint16_t* bias, int64_t M, int64_t N, int64_t K, int64_t r,
+                                           int epilogue, uint16_t* y, hipStream_t stream);
+
 // Compute units of the current device (cached; 256 when no device answers).
 int current_cus();
 

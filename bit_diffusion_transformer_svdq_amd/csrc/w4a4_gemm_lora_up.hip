@@ -55,6 +55,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "svdq_device.h"
 
@@ -785,7 +786,71 @@ hipError_t launch(GemmArgs<kDump> a, const GemmPlan& g, Workspace ws, hipStream_
   return hipGetLastError();
 }
 
+// Fixed device scratch of the no-allocation entry point: a counter region and
+// partial sums, as in a caller's workspace.  Each device holds its own copy
+// until the process ends; host code reaches it only through the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+__global__ void clear_counters(uint32_t* c, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) c[i] = 0;
+}
+
+constexpr int kMaxScratchDevices = 64;
+struct ScratchSlot {
+  void* ptr = nullptr;  // device address of `scratch` on that device
+  bool cleared = false; // counters cleared by an eager (not captured) launch
+};
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[kMaxScratchDevices];
+
+// The current device's scratch as a workspace; the first use on a device
+// looks up its address and clears the counter region on `stream` (a fill
+// kernel: captured into a graph, it runs before the call on every replay,
+// and a later eager call clears once more).
+hipError_t static_workspace(hipStream_t stream, Workspace* ws) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  ScratchSlot& sl = g_scratch[dev];
+  if (sl.ptr == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    sl.ptr = p;
+  }
+  if (!sl.cleared) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return e;
+    const int n = (int)(kWsCounterBytes / 4);
+    hipLaunchKernelGGL(clear_counters, dim3((n + 255) / 256), dim3(256), 0, stream, static_cast<uint32_t*>(sl.ptr),
+                       n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (cs == hipStreamCaptureStatusNone) sl.cleared = true;
+  }
+  *ws = Workspace{sl.ptr, kStaticScratchBytes};
+  return hipSuccess;
+}
+
 }  // namespace
+
+hipError_t launch_w4a4_gemm_lora_up_static(const uint8_t* act_codes, const uint16_t* act_scales,
+                                           const uint8_t* w_codes, const uint16_t* w_scales,
+                                           const uint16_t* lora_act, const uint16_t* lora_up,
+                                           const uint16_t* bias, int64_t M, int64_t N, int64_t K, int64_t r,
+                                           int epilogue, uint16_t* y, hipStream_t stream) {
+  if (gemm_workspace_bytes(M, N, K, r, epilogue, false) > kStaticScratchBytes) return hipErrorInvalidValue;
+  Workspace ws;
+  hipError_t e = static_workspace(stream, &ws);
+  if (e != hipSuccess) return e;
+  return launch_w4a4_gemm_lora_up(act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, r,
+                                  epilogue, nullptr, y, DumpWindow{}, ws, stream);
+}
 
 void set_gemm_path_override(int path) { g_path.store(path, std::memory_order_relaxed); }
 

@@ -245,6 +245,28 @@ svdq_status svdq_w4a4_gemm_lora_up_ex(
     int epilogue, void* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Call 2 (svdq_w4a4_gemm_lora_up_ex) for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid allocation.  It takes no workspace and allocates nothing: when
+ * the shape splits K, the partial sums go through a fixed device scratch the
+ * library holds on each device from its first use until the process ends (64
+ * MiB, the first MiB arrival counters).  The first call on a device clears
+ * those counters with a small fill kernel on `stream`; every call leaves them
+ * at zero.  All calls on one device share that scratch: calls that may run at
+ * the same time on one device (different streams, concurrent graphs) race
+ * and give wrong results; order them.  A shape whose plan needs more scratch
+ * than the fixed size (svdq_w4a4_gemm_workspace_size above 64 MiB) returns
+ * NOT_SUPPORTED before any launch.  Arguments, results and other errors as for
+ * svdq_w4a4_gemm_lora_up_ex; the result is bit-identical to it.
+ */
+svdq_status svdq_w4a4_gemm_lora_up_noalloc(
+    const void* act_codes, const void* act_scales,
+    const void* w_codes, const void* w_scales,
+    const void* lora_act, const void* lora_up, const void* bias,
+    int64_t M, int64_t N, int64_t K, int64_t r, int64_t group_size,
+    int epilogue, void* y, void* stream);
+
+/*
  * Call 2 with the fused QKV epilogue of a diffusion transformer's attention:
  * for FLUX.1-dev the Q, K and V projections are one quantized to_qkv linear
  * whose fused operator also does the Q/K normalization and the rotary

@@ -99,6 +99,17 @@ static void full_mode() {
   // the workspace may not overlap the output
   CHECK(svdq_w4a4_gemm_lora_up(codes.p, scales.p, wc.p, wsc.p, la.p, up.p, bias.p, M, N, K, r, 64, y.p,
                                y.p, 8192, nullptr) == SVDQ_STATUS_INVALID_VALUE);
+  // the no-allocation variant: no workspace argument, a plan beyond the fixed
+  // 64 MiB scratch is refused before any launch
+  g_fake.gemm_need = (size_t(64) << 20) + 1;
+  CHECK(svdq_w4a4_gemm_lora_up_noalloc(codes.p, scales.p, wc.p, wsc.p, la.p, up.p, bias.p, M, N, K, r, 64, 0, y.p,
+                                       nullptr) == SVDQ_STATUS_NOT_SUPPORTED);
+  g_fake.gemm_need = size_t(64) << 20;
+  CHECK(svdq_w4a4_gemm_lora_up_noalloc(codes.p, scales.p, wc.p, wsc.p, la.p, up.p, bias.p, M, N, K, r, 64, 1, y.p,
+                                       nullptr) == SVDQ_STATUS_SUCCESS);
+  CHECK(std::string(g_fake.last) == "gemm_static" && g_fake.last_out == y.p);
+  CHECK(svdq_w4a4_gemm_lora_up_noalloc(codes.p, scales.p, wc.p, wsc.p, la.p, up.p, bias.p, M, N, K, r, 64, 0, la.p,
+                                       nullptr) == SVDQ_STATUS_INVALID_VALUE);
   g_fake.quant_need = g_fake.gemm_need = 0;
   // overlapping outputs and inputs
   CHECK(svdq_w4a4_gemm_lora_up(codes.p, scales.p, wc.p, wsc.p, la.p, up.p, bias.p, M, N, K, r, 64, wc.p,

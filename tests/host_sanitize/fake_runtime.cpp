@@ -85,6 +85,13 @@ hipError_t launch_w4a4_gemm_lora_up(const uint8_t*, const uint16_t*, const uint8
   return hipSuccess;
 }
 
+hipError_t launch_w4a4_gemm_lora_up_static(const uint8_t*, const uint16_t*, const uint8_t*, const uint16_t*,
+                                           const uint16_t*, const uint16_t*, const uint16_t*, int64_t, int64_t,
+                                           int64_t, int64_t, int, uint16_t* y, hipStream_t) {
+  record("gemm_static", y, Workspace{});
+  return hipSuccess;
+}
+
 hipError_t launch_fp4_gemm_lora_up(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const uint16_t*,
                                   const uint16_t*, const uint16_t*, int64_t, int64_t, int64_t, int64_t, int,
                                   uint16_t* y, Workspace ws, hipStream_t) {

@@ -33,6 +33,7 @@ from ._lib import SvdqError, check, lib
 
 __all__ = ["SvdqError", "lib", "check_device", "quantize_act_lora_down", "w4a4_gemm_lora_up",
            "mlp_pair", "w4a4_gemm_lora_up_noalloc", "w4a4_gemm_qkv_norm_rope", "w4a4_group_acc_debug", "debug_set_quant_plan", "debug_set_gemm_path", "debug_set_gemm_splits",
+           "debug_set_fp4_tile",
            "EPILOGUES", "smooth_from_absmax", "pack_weights", "awq_w4a16_gemm", "awq_w4a16_gemm_stacked",
            "awq_pack_weights",
            "quantize_act_lora_down_fp4", "fp4_gemm_lora_up", "pack_weights_fp4",
@@ -161,6 +162,11 @@ def debug_set_gemm_path(path: int = 0) -> None:
 def debug_set_gemm_splits(splits: int = 0) -> None:
     """Test hook: K-splits per tile of the tiled kernel (0 = chosen by shape)."""
     check(lib().svdq_debug_set_gemm_splits(int(splits)), "svdq_debug_set_gemm_splits")
+
+
+def debug_set_fp4_tile(tile: int = 0) -> None:
+    """Test hook: output tile edge of the MXFP4 GEMM (0 = chosen by shape, 128, 256)."""
+    check(lib().svdq_debug_set_fp4_tile(int(tile)), "svdq_debug_set_fp4_tile")
 
 
 EPILOGUES = {"none": 0, "gelu_tanh": 1}

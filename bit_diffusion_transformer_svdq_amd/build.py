@@ -33,7 +33,8 @@ HIP_FLAGS = [
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HOST_API_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
                   "-I", os.path.join(ROCM, "include")]
-KERNELS = ["quant_lora_down.hip", "w4a4_gemm_lora_up.hip", "w4a4_gemm_skinny.hip", "awq_w4a16_gemm.hip"]
+KERNELS = ["quant_lora_down.hip", "w4a4_gemm_lora_up.hip", "w4a4_gemm_skinny.hip", "fp4_gemm_big.hip",
+           "awq_w4a16_gemm.hip"]
 
 
 def _hipcc() -> str:

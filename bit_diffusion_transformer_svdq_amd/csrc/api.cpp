@@ -262,6 +262,13 @@ svdq_status svdq_debug_set_gemm_path(int path) {
   return ok();
 }
 
+svdq_status svdq_debug_set_fp4_tile(int tile) {
+  if (tile != 0 && tile != 128 && tile != 256)
+    return fail(SVDQ_STATUS_INVALID_VALUE, "bad fp4 tile %d (0, 128 or 256)", tile);
+  svdq::set_fp4_tile_override(tile);
+  return ok();
+}
+
 svdq_status svdq_debug_set_gemm_splits(int splits) {
   if (splits < 0 || splits > 64) return fail(SVDQ_STATUS_INVALID_VALUE, "bad split count %d (0..64)", splits);
   svdq::set_gemm_splits_override(splits);

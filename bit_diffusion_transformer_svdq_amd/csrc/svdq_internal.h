@@ -119,6 +119,20 @@ hipError_t launch_fp4_gemm_lora_up(const uint8_t* act_codes, const uint8_t* act_
                                   const uint16_t* bias, int64_t M, int64_t N, int64_t K, int64_t r,
                                   int epilogue, uint16_t* y, Workspace ws, hipStream_t stream);
 
+// Call 2 of the MXFP4 variant on 256 x 256 tiles (one workgroup per CU, no
+// K-split, no workspace); K % 1024 == 0, N % 64 == 0, epilogue none or GELU.
+// launch_fp4_gemm_lora_up picks it when the tiles fill at least one round.
+int fp4_big_tiles(int64_t M, int64_t N);
+hipError_t launch_fp4_gemm_big(const uint8_t* act_codes, const uint8_t* act_scales, const uint8_t* w_codes,
+                               const uint8_t* w_scales, const uint16_t* lora_act, const uint16_t* lora_up,
+                               const uint16_t* bias, int64_t M, int64_t N, int64_t K, int64_t r, int epilogue,
+                               uint16_t* y, hipStream_t stream);
+
+// Test hook: output tile edge of the MXFP4 GEMM for later calls (0 = chosen by
+// shape, 128 = the tiled kernel with K-splits, 256 = the 256 x 256 kernel
+// wherever K % 1024 == 0).
+void set_fp4_tile_override(int tile);
+
 // Test hook: 0 = choose by shape, 1 = always the tiled kernel, 2 = the
 // few-token kernel wherever it is supported.
 void set_gemm_path_override(int path);

@@ -728,17 +728,19 @@ int pick_splits(int tiles, int pairs, int cus) {
 
 std::atomic<int> g_splits{0};  // test hook (0 = automatic)
 std::atomic<int> g_path{0};    // test hook: 0 = by shape, 1 = tiled, 2 = few-token kernel
+std::atomic<int> g_fp4_tile{0};  // test hook: 0 = by shape, 128, 256
 
 // How call 2 runs a shape on the current device.
 struct GemmPlan {
   bool skinny;  // the few-token kernel
+  bool big;     // MXFP4 on 256 x 256 tiles
   int tiles;    // 128 x 128 output tiles (tiled kernel)
   int splits;   // K-splits per tile
   int occ;      // workgroups per CU the tiled kernel is built for (2 or 3)
 };
 
 GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int epilogue, bool fp4) {
-  GemmPlan g{false, (int)(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM)), 1, 3};
+  GemmPlan g{false, false, (int)(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM)), 1, 3};
   const int path = g_path.load(std::memory_order_relaxed);
   if (!fp4 && epilogue != kEpilogueQkv && path != 1 && skinny_supported(M, N, K) &&
       (path == 2 || M <= kSkinnyMaxM)) {
@@ -746,6 +748,16 @@ GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int epilogue, bool fp4) {
     return g;
   }
   const int cus = current_cus();
+  // MXFP4: 256 x 256 tiles once they fill every CU at least once (fewer
+  // tiles run faster as 128 x 128 tiles with K-splits); the test hooks can
+  // force either, and a forced split count forces the 128 x 128 kernel
+  if (fp4 && K % 1024 == 0 && g_splits.load(std::memory_order_relaxed) == 0) {
+    const int tile = g_fp4_tile.load(std::memory_order_relaxed);
+    if (tile == 256 || (tile == 0 && fp4_big_tiles(M, N) >= cus)) {
+      g.big = true;
+      return g;
+    }
+  }
   const int pairs = (int)((K / 64 + 1) / 2);
   if (epilogue != kEpilogueQkv) {
     const int forced = g_splits.load(std::memory_order_relaxed);
@@ -854,13 +866,15 @@ hipError_t launch_w4a4_gemm_lora_up_static(const uint8_t* act_codes, const uint1
 
 void set_gemm_path_override(int path) { g_path.store(path, std::memory_order_relaxed); }
 
+void set_fp4_tile_override(int tile) { g_fp4_tile.store(tile, std::memory_order_relaxed); }
+
 void set_gemm_splits_override(int splits) { g_splits.store(std::max(0, splits), std::memory_order_relaxed); }
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r, int epilogue, bool fp4) {
   (void)r;
   if (M <= 0) return 0;
   const GemmPlan g = gemm_plan(M, N, K, epilogue, fp4);
-  if (g.skinny) return 0;
+  if (g.skinny || g.big) return 0;
   return ws_bytes(split_counters(g), split_bytes(g));
 }
 
@@ -870,12 +884,16 @@ hipError_t launch_fp4_gemm_lora_up(const uint8_t* act_codes, const uint8_t* act_
                                   const uint16_t* bias, int64_t M, int64_t N, int64_t K, int64_t r,
                                   int epilogue, uint16_t* y, Workspace ws, hipStream_t stream) {
   if (K % 128 != 0 || epilogue == kEpilogueQkv) return hipErrorInvalidValue;
+  const GemmPlan g = gemm_plan(M, N, K, epilogue, true);
+  if (g.big)
+    return launch_fp4_gemm_big(act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, r,
+                               epilogue, y, stream);
   // the E8M0 byte pairs of a 64-group travel like the int4 path's bf16 scale
   GemmArgs<false> a{act_codes, reinterpret_cast<const uint16_t*>(act_scales), w_codes,
                     reinterpret_cast<const uint16_t*>(w_scales), lora_act, lora_up, bias,
                     y, nullptr, 0, 0, 0, 0, (int)M, (int)N, (int)K, (int)r, epilogue, QkvEpilogue{}, 1,
                     nullptr, nullptr};
-  return launch<false, true>(a, gemm_plan(M, N, K, epilogue, true), ws, stream);
+  return launch<false, true>(a, g, ws, stream);
 }
 
 hipError_t launch_w4a4_gemm_lora_up(const uint8_t* act_codes, const uint16_t* act_scales,

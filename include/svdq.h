@@ -176,6 +176,18 @@ svdq_status svdq_debug_set_gemm_path(int path);
 svdq_status svdq_debug_set_gemm_splits(int splits);
 
 /*
+ * Test hook for svdq_fp4_gemm_lora_up: the output tile edge for every later
+ * call in this process.  0 chooses by shape (256 x 256 tiles, one workgroup
+ * per CU and no workspace, when K % 1024 == 0 and those tiles fill every CU
+ * at least once; otherwise 128 x 128 tiles with K-splits), 128 forces the
+ * 128 x 128 kernel, 256 the 256 x 256 kernel wherever K % 1024 == 0.  A split
+ * count forced by svdq_debug_set_gemm_splits also selects the 128 x 128
+ * kernel.  Query the workspace size after setting the hook.  Returns
+ * INVALID_VALUE for other values.
+ */
+svdq_status svdq_debug_set_fp4_tile(int tile);
+
+/*
  * Call 2 - W4A4 GEMM with per-group int32 accumulation, per-group
  * dequantization, the fused low-rank up-projection and the bias
  * (mind-verse.de, section "Nunchaku und SVDQuant": fused kernels for the 4-bit

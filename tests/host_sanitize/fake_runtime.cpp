@@ -57,6 +57,7 @@ bool awq_supported(int64_t K, int64_t M) { return K <= (M == 1 ? 16384 : M <= 4 
 void set_quant_plan_override(int, int) {}
 void set_gemm_path_override(int) {}
 void set_gemm_splits_override(int) {}
+void set_fp4_tile_override(int) {}
 
 static void record(const char* name, const void* out, Workspace ws) {
   ++g_fake.launches;

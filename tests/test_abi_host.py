@@ -269,6 +269,14 @@ def test_gemm_path_hook_arguments():
         assert L.svdq_debug_set_gemm_path(p) == SUCCESS
 
 
+def test_fp4_tile_hook_arguments():
+    L = lib()
+    for bad in (-1, 1, 64, 129, 512):
+        assert L.svdq_debug_set_fp4_tile(bad) == INVALID_VALUE
+    for t in (128, 256, 0):
+        assert L.svdq_debug_set_fp4_tile(t) == SUCCESS
+
+
 def test_gemm_splits_hook_arguments():
     L = lib()
     assert L.svdq_debug_set_gemm_splits(-1) == INVALID_VALUE
@@ -354,6 +362,13 @@ def test_workspace_size_queries_and_checks():
     assert L.svdq_w4a4_gemm_workspace_size(0, 256, 256, 16) == 0
     assert L.svdq_w4a4_gemm_workspace_size(64, 96, 256, 16) == 0             # rejected shape
     assert L.svdq_quantize_act_workspace_size(64, 100, 16) == 0
+    # MXFP4 on 256 x 256 tiles (864 of them fill every CU): no K-split, no workspace
+    assert L.svdq_fp4_gemm_workspace_size(4608, 12288, 3072, 32) == 0
+    L.svdq_debug_set_fp4_tile(256)
+    try:
+        assert L.svdq_fp4_gemm_workspace_size(64, 256, 1024, 16) == 0
+    finally:
+        L.svdq_debug_set_fp4_tile(0)
     L.svdq_debug_set_gemm_path(1)
     L.svdq_debug_set_gemm_splits(2)
     L.svdq_debug_set_quant_plan(4, 0)

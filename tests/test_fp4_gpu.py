@@ -115,12 +115,53 @@ def test_fp4_forced_quant_plans():
         _check(got, d, lam, pk)
 
 
+def _tile_rows(M, tile):
+    """One row of every row tile at an offset that walks through the tile,
+    plus the first and the last two rows."""
+    rows = {0, M - 2, M - 1}
+    for t in range((M + tile - 1) // tile):
+        rows.add(min(M - 1, t * tile + (37 * t + 5) % tile))
+    return sorted(r for r in rows if r >= 0)
+
+
 def test_fp4_headline_shape_sampled_rows():
-    """The headline linear (M=4608, K=3072, N=12288, r=32) in the FP4 variant,
-    codes and scales of every token, Y on sampled rows."""
+    """The headline linear (M=4608, K=3072, N=12288, r=32) in the FP4 variant
+    (864 tiles of 256 x 256: the 256 x 256 kernel), codes and scales of every
+    token, Y on one row of every 256-row tile (every column)."""
     d, lam, pk = _case(S.SPECS["mlp_up"])
-    rows = [0, 1, 127, 128, 2047, 4095, 4096, 4607]
-    _check(_run(d, lam, pk), d, lam, pk, rows=rows)
+    _check(_run(d, lam, pk), d, lam, pk, rows=_tile_rows(4608, 256))
+
+
+@pytest.mark.parametrize("M,K,N,r,epi", [(300, 1024, 320, 32, "none"), (64, 1024, 64, 0, "none"),
+                                         (257, 2048, 576, 16, "gelu_tanh"), (513, 3072, 512, 48, "none"),
+                                         (1, 1024, 256, 32, "none"), (256, 4096, 256, 128, "gelu_tanh")])
+def test_fp4_256_tile_kernel_forced(M, K, N, r, epi):
+    """The 256 x 256 kernel forced at small shapes, every element of Y:
+    partial tiles in m and in n, rank chunks of 32 with and without a
+    trailing 16, no low-rank branch, one token, the largest rank, GELU."""
+    import bit_diffusion_transformer_svdq_amd as K_
+    print(f"fp4 256-tile M={M} K={K} N={N} r={r} {epi}", flush=True)
+    d, lam, pk = _case(_spec(M, K, N, r, 3 * M + N))
+    K_.debug_set_fp4_tile(256)
+    try:
+        got = _run(d, lam, pk, epilogue=epi)
+    finally:
+        K_.debug_set_fp4_tile(0)
+    _check(got, d, lam, pk, epilogue=epi)
+
+
+def test_fp4_256_tile_kernel_long_k_sampled_rows():
+    """The MLP down-projection shape (M=4608, K=12288, N=3072, r=32) on the
+    256 x 256 kernel (forced: its 216 tiles would pick the 128 x 128 kernel
+    with K-splits), Y on one row of every 256-row tile."""
+    import bit_diffusion_transformer_svdq_amd as K_
+    d, lam, pk = _case(S.SPECS["mlp_down"])
+    K_.debug_set_fp4_tile(256)
+    try:
+        got = _run(d, lam, pk)
+    finally:
+        K_.debug_set_fp4_tile(0)
+    _check(got, d, lam, pk, rows=_tile_rows(4608, 256))
 
 
 def _bf16_ladder_blocks(s: int) -> np.ndarray:

@@ -121,7 +121,8 @@ hipError_t launch_fp4_gemm_lora_up(const uint8_t* act_codes, const uint8_t* act_
 
 // Call 2 of the MXFP4 variant on 256 x 256 tiles (one workgroup per CU, no
 // K-split, no workspace); K % 1024 == 0, N % 64 == 0, epilogue none or GELU.
-// launch_fp4_gemm_lora_up picks it when the tiles fill at least one round.
+// launch_fp4_gemm_lora_up picks it when there are at least a quarter as many
+// tiles as CUs.
 int fp4_big_tiles(int64_t M, int64_t N);
 hipError_t launch_fp4_gemm_big(const uint8_t* act_codes, const uint8_t* act_scales, const uint8_t* w_codes,
                                const uint8_t* w_scales, const uint16_t* lora_act, const uint16_t* lora_up,

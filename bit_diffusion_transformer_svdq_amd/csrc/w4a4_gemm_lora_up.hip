@@ -70,6 +70,7 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned int u32;
+typedef u32 v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
@@ -236,38 +237,56 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
   const int fw = 64 * (wn * 64 + l16) + 16 * ((lseg >> 1) ^ fsw) + 8 * (lseg & 1);
   const int fa = 64 * (wm * 64 + l16) + 16 * ((lseg >> 1) ^ fsw) + 8 * (lseg & 1);
 
-  // scale role: threads 0..127 -> token slot tid, 128..255 -> weight row tid-128
-  const bool s_is_act = tid < kBM;
+  // scale role: threads 0..127 (waves 0, 1) -> token slot tid, 128..255 ->
+  // weight row tid-128 (wave-uniform, so the buffer resource below is scalar)
+  const bool s_is_act = wave < 2;
   const int s_idx = s_is_act ? tid : tid - kBM;
-  // wave-uniform base row of the workgroup's scales (64-bit), 32-bit offsets within
+  // The thread's row of scales is read 3 group pairs at a time: one load
+  // instruction per wave every 3 pairs instead of two 2-byte gathers per pair
+  // (each instruction touches 64 rows, whatever it moves per lane).  With an
+  // odd group count a row starts 2 bytes into a dword, so 16 bytes are read
+  // from the dword boundary below and each pair's dword is realigned.  A
+  // buffer load bounded by the end of the scale array returns zeros past it
+  // (the last block of a row may run into the next row or past the array;
+  // those groups are never used).  The wave-uniform base is the workgroup's
+  // first row; offsets within fit 32 bits.
   const uint16_t* sbase = s_is_act ? p.act_scales + (size_t)m0 * (size_t)G : p.w_scales + (size_t)n0 * (size_t)G;
   const u32 soff = (u32)(s_is_act ? min(m0 + (kFp4 ? s_idx : sx_token(s_idx)), M - 1) - m0
-                                  : min(n0 + s_idx, N - 1) - n0) * (u32)G;
-  // register ring of raw bf16 scales, pair q in slot q % 3
-  u32 slo[3], shi[3];
-  auto load_scales = [&](int q, int k) {
+                                  : min(n0 + s_idx, N - 1) - n0) * (u32)G * 2u;
+  // bytes from sbase to the end of the array, rounded up to a whole dword: the
+  // range check drops any dword that reaches past it, and with an odd group
+  // count the array ends 2 bytes into a dword (whose other half is never used;
+  // an aligned dword never crosses a page)
+  const size_t s_left = (2 * (size_t)G * (size_t)(s_is_act ? M - m0 : N - n0) + 3) & ~(size_t)3;
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(sbase), (short)0, (int)min(s_left, (size_t)0x7FFFFFFF), 0x00020000);
+  const u32 sshift = (soff & 2u) * 8u;  // 0, or 16 bits for a row that starts mid-dword
+  // register ring of raw scales: block c (pairs 3c .. 3c+2 of the split,
+  // pair d in bits [32d + sshift, 32d + sshift + 32): group 2q in the low
+  // half) in slot c % 2
+  v4u sblk[2];
+  auto load_scales = [&](int c, int slot) {
     if (kDump) return;
-    slo[k] = sbase[soff + (u32)min(2 * (qb + q), G - 1)];
-    shi[k] = sbase[soff + (u32)min(2 * (qb + q) + 1, G - 1)];
+    sblk[slot] = __builtin_amdgcn_raw_buffer_load_b128(srsrc, (int)((soff & ~3u) + 4u * (u32)(qb + 3 * c)), 0, 0);
   };
-  // converted scales of pair q (ring slot k) -> stage buffer `buf`: per group
-  // h, s_x/256 of the token slot (floats 256h + 0..127) or s_w of the weight
-  // row (256h + 128..255)
-  auto put_scale = [&](int q, int k, int buf) {
+  // converted scales of pair q (block slot `slot`, dword d) -> stage buffer
+  // `buf`: per group h, s_x/256 of the token slot (floats 256h + 0..127) or
+  // s_w of the weight row (256h + 128..255)
+  auto put_scale = [&](int slot, int d, int buf) {
     if (kDump) return;
     u32 o = 4u * (u32)(s_is_act ? s_idx : 128 + s_idx);
     __asm__ volatile("" : "+v"(o));  // keeps the per-stage addresses out of registers
     uint8_t* sp = reinterpret_cast<uint8_t*>(sarea(buf)) + o;
+    const u32 w = __builtin_amdgcn_alignbit(sblk[slot][d + 1], sblk[slot][d], sshift);
     if constexpr (kFp4) {
       // the row's four E8M0 bytes of the stage (blocks 4q .. 4q+3), as loaded
-      *reinterpret_cast<u32*>(sp) = slo[k] | (shi[k] << 16);
+      *reinterpret_cast<u32*>(sp) = w;
       return;
     }
-    const float f0 = __builtin_bit_cast(float, slo[k] << 16);
-    const float f1 = __builtin_bit_cast(float, shi[k] << 16);
+    const float f0 = __builtin_bit_cast(float, w << 16);
+    const float f1 = __builtin_bit_cast(float, w & 0xFFFF0000u);
     *reinterpret_cast<float*>(sp) = s_is_act ? f0 * (1.0f / 256.0f) : f0;
     *reinterpret_cast<float*>(sp + 1024) = s_is_act ? f1 * (1.0f / 256.0f) : f1;
-    (void)q;
   };
 
   // With 2 workgroups per CU the LDS has room for the lora tiles: they are
@@ -435,36 +454,40 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
     }
   };
 
-  // Prologue, in issue order: scales of pairs 0 and 1, pair 0, scales of pair
-  // 2, pair 1.  Iteration q then issues the scales of pair q+3 and, last, the
-  // 4 DMAs of pair q+2, so vmcnt(4) at the top of iteration q means that pair q
-  // and the scales of pairs up to q+2 have landed.
+  // Prologue, in issue order: scale block 0 (pairs 0-2), pair 0, pair 1.
+  // Iteration q issues scale block q/3 + 1 when q % 3 == 0 and, last, the 4
+  // DMAs of pair q+2, so at the top of iteration q the wait for pair q (4
+  // younger operations, 5 after an iteration that loaded a block) also covers
+  // every block that put_scale can ask for there.
   load_scales(0, 0);
-  load_scales(1, 1);
   dma_pair(0, 0);
-  load_scales(2, 2);
   dma_pair(min(1, Pl - 1), 1);
+  wait_vm<8, false>();  // block 0
   put_scale(0, 0, 0);
 
-  // Iteration q: stage q complete (own loads: vmcnt, everyone's: barrier); the
-  // scales of pair q+3 go into the ring slot pair q has freed; pair q+2 starts
-  // loading into the stage freed by pair q-1; the scales of pair q+1 are
-  // staged into the scale area pair q-1 has freed; pair q is computed.  The
-  // body is unrolled over 6 pairs (3 tile stages x 2 scale areas) so every LDS
-  // buffer and register-ring index is a compile-time constant.
+  // Iteration q: stage q complete (own loads: vmcnt, everyone's: barrier);
+  // every third pair, the next scale block goes into the ring slot the block
+  // before has freed; pair q+2 starts loading into the stage freed by pair
+  // q-1; the scales of pair q+1 are staged into the scale area pair q-1 has
+  // freed; pair q is computed.  The body is unrolled over 6 pairs (3 tile
+  // stages x 2 scale areas x 2 scale blocks) so every LDS buffer and
+  // register index is a compile-time constant.
   for (int q0 = 0; q0 < Pl; q0 += 6) {
 #pragma unroll
     for (int u = 0; u < 6; ++u) {
       const int q = q0 + u;
-      wait_vm<4, true>();
+      if (!kDump && (u == 1 || u == 4)) wait_vm<5, true>(); else wait_vm<4, true>();
       barrier();
-      load_scales(min(q + 3, Pl - 1), u % 3);
+      if (u % 3 == 0) load_scales((q / 3) + 1, (u / 3 + 1) % 2);
       dma_pair(min(q + 2, Pl - 1), (u + 2) % 3);
-      put_scale(q + 1, (u + 1) % 3, (u + 1) % 2);
+      put_scale(((u + 1) / 3) % 2, (u + 1) % 3, (u + 1) % 2);
       if (q < Pl) compute_pair(u % 3, u % 2, q);
     }
   }
   wait_vm<0, true>();
+  // every wave is done with the ring stages before any wave stages its Y
+  // tile there (after this point a wave may leave early: K-split partials)
+  barrier();
 
   if constexpr (!kDump) {
     // K-split: each wave reduces its own 64 x 64 sub-tile.  It stores its fp32
@@ -651,13 +674,21 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
       }
       return;
     }
-    // bias and store: lane owns Y[m, n .. n+3]
+    // Bias and optional GELU in fp32, then Y goes out through LDS (this
+    // wave's ring stage, free since the barrier after the main loop): the wave
+    // writes its 64 x 64 bf16 sub-tile as rows m of 128 bytes, 16-byte chunk
+    // c of row m at chunk c ^ (m % 8), and reads it back so that each store
+    // instruction writes 8 rows x 128 contiguous bytes instead of 16 rows x
+    // 32 bytes.  N % 64 == 0, so the wave's 64 columns are all in range or
+    // all out of it.
+    uint8_t* stg = wave == 0 ? w0 : wave == 1 ? w1 : wave == 2 ? w2 : a0;
+    const int nw = n0 + wn * 64;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int n = n0 + wn * 64 + 16 * i + 4 * lseg;
+      const int nl = 16 * i + 4 * lseg;  // within the wave's 64 columns
       float bb4[4] = {0.f, 0.f, 0.f, 0.f};
-      if (p.bias != nullptr && n < N) {
-        const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n);
+      if (p.bias != nullptr && nw < N) {
+        const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + nw + nl);
         bb4[0] = __builtin_bit_cast(float, bb.x << 16);
         bb4[1] = __builtin_bit_cast(float, bb.x & 0xFFFF0000u);
         bb4[2] = __builtin_bit_cast(float, bb.y << 16);
@@ -665,20 +696,30 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int m = m0 + wm * 64 + 16 * j + l16;
-        if (m < M && n < N) {
-          float o4[4];
+        float o4[4];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) o4[v] = y[i][j][v] + bb4[v];
-          if (p.epilogue == kEpilogueGelu) {
+        for (int v = 0; v < 4; ++v) o4[v] = y[i][j][v] + bb4[v];
+        if (p.epilogue == kEpilogueGelu) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) o4[v] = gelu_tanh(o4[v]);
-          }
-          uint2 o;
-          o.x = pack_bf16(o4[0], o4[1]);
-          o.y = pack_bf16(o4[2], o4[3]);
-          *reinterpret_cast<uint2*>(p.y + (size_t)m * N + n) = o;
+          for (int v = 0; v < 4; ++v) o4[v] = gelu_tanh(o4[v]);
         }
+        uint2 o;
+        o.x = pack_bf16(o4[0], o4[1]);
+        o.y = pack_bf16(o4[2], o4[3]);
+        const int ml = 16 * j + l16;  // row within the wave's 64
+        *reinterpret_cast<uint2*>(stg + ml * 128 + (((nl >> 3) ^ (ml & 7)) << 4) + 8 * (lseg & 1)) = o;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+    __asm__ volatile("" ::: "memory");
+    if (nw < N) {
+      const int c = lane & 7;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int ml = 8 * t + (lane >> 3);
+        const int m = m0 + wm * 64 + ml;
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + ml * 128 + ((c ^ (ml & 7)) << 4));
+        if (m < M) *reinterpret_cast<uint4*>(p.y + (size_t)m * N + nw + 8 * c) = v;
       }
     }
   }
@@ -748,12 +789,15 @@ GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int epilogue, bool fp4) {
     return g;
   }
   const int cus = current_cus();
-  // MXFP4: 256 x 256 tiles once they fill every CU at least once (fewer
-  // tiles run faster as 128 x 128 tiles with K-splits); the test hooks can
-  // force either, and a forced split count forces the 128 x 128 kernel
+  // MXFP4: 256 x 256 tiles once there are at least a quarter as many as CUs
+  // (measured on MI355X: 96 tiles of 512 x 3072 -> 12288 and 216 tiles of
+  // 4608 x 12288 -> 3072 run 1.2x and 2.2x faster than 128 x 128 tiles with
+  // K-splits; 24 tiles of 512 x 3072 -> 3072 and 48 of 1024 x 12288 -> 3072
+  // run 1.8x and 1.4x slower); the test hooks can force either, and a forced
+  // split count forces the 128 x 128 kernel
   if (fp4 && K % 1024 == 0 && g_splits.load(std::memory_order_relaxed) == 0) {
     const int tile = g_fp4_tile.load(std::memory_order_relaxed);
-    if (tile == 256 || (tile == 0 && fp4_big_tiles(M, N) >= cus)) {
+    if (tile == 256 || (tile == 0 && 4 * fp4_big_tiles(M, N) >= cus)) {
       g.big = true;
       return g;
     }

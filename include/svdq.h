@@ -178,8 +178,9 @@ svdq_status svdq_debug_set_gemm_splits(int splits);
 /*
  * Test hook for svdq_fp4_gemm_lora_up: the output tile edge for every later
  * call in this process.  0 chooses by shape (256 x 256 tiles, one workgroup
- * per CU and no workspace, when K % 1024 == 0 and those tiles fill every CU
- * at least once; otherwise 128 x 128 tiles with K-splits), 128 forces the
+ * per CU and no workspace, when K % 1024 == 0 and there are at least a
+ * quarter as many of those tiles as CUs; otherwise 128 x 128 tiles with
+ * K-splits), 128 forces the
  * 128 x 128 kernel, 256 the 256 x 256 kernel wherever K % 1024 == 0.  A split
  * count forced by svdq_debug_set_gemm_splits also selects the 128 x 128
  * kernel.  Query the workspace size after setting the hook.  Returns

@@ -145,10 +145,8 @@ void awq_w4a16_kernel(const AwqArgs args) {
   const int g_hi = ((wq + 1) * G) / kWaves;
   const int nch = (g_hi - g_lo + 1) >> 1;           // chunks of 2 groups
 
-  // 1. 1/s and x of the thread's first two runs (up to 4 token rows).  The
-  //    LDS DMAs go out after x_hat is staged: while plain loads and LDS DMAs
-  //    are both in flight, the compiler waits for all of them before using a
-  //    loaded value, so DMAs issued first would hold up the staging.
+  // 1. 1/s and x of the thread's first two runs (up to 4 token rows), issued
+  //    before any DMA.
   uint4 xv[2][4];
   v4f sv[2][2];
 #pragma unroll
@@ -174,7 +172,28 @@ void awq_w4a16_kernel(const AwqArgs args) {
     dma16(dsrc + 32 * g, stage_of(s) + 1024 * wave);
   };
 
-  // 2. x_hat = bf16(fl32(x mu)), mu = fl32(1/s), each run of 8 stored in the
+  // 2. The 16 rows' Delta and z (contiguous in [N, G] layout; n0 is a
+  //    multiple of 16, so both start on a 16-byte boundary), a fixed count of
+  //    DMAs per wave (blocks past the last repeat it, pad lanes the last
+  //    slot); then exactly 3 code chunks of this wave, so "at most 3
+  //    outstanding" means everything before has landed.  They go out before
+  //    x_hat is staged, so the weight stream starts at once; the staging
+  //    waits for the x and 1/s loads with an explicit count of the DMAs
+  //    issued after them (vector-memory counters retire in issue order).
+  constexpr int kDzDmas = kDzSlots / (64 * kWaves) + (kDzSlots % (64 * kWaves) != 0);
+#pragma unroll
+  for (int t = 0; t < kDzDmas; ++t) {
+    const int j0 = min(64 * (wq + kWaves * t), dzslots - 64);
+    const int j = min(j0 + lane, 3 * G - 1);
+    const uint8_t* src = j < 2 * G ? reinterpret_cast<const uint8_t*>(a.scales) + (size_t)n0 * G * 2 + 16 * j
+                                   : a.zeros + (size_t)n0 * G + 16 * (j - 2 * G);
+    dma16(src, dzt + 16 * j0);
+  }
+#pragma unroll
+  for (int s = 0; s < kRing; ++s) dma_chunk(s, s);
+  wait_vm<kDzDmas + kRing>();  // the x and 1/s loads of this thread have landed
+
+  // 3. x_hat = bf16(fl32(x mu)), mu = fl32(1/s), each run of 8 stored in the
   //    pair order (0,4), (1,5), (2,6), (3,7); xs[g][row] = sum of the group's
   //    x_hat (the 8 runs of a group sit in 8 consecutive lanes, since runs and
   //    the thread count are multiples of 8).
@@ -224,22 +243,7 @@ void awq_w4a16_kernel(const AwqArgs args) {
     for (int rr = 0; rr < rows; ++rr)
       stage(*reinterpret_cast<const uint4*>(a.x + (size_t)(m0 + rr) * a.K + 8 * c), mu, rr, c);
   }
-  // 3. The 16 rows' Delta and z (contiguous in [N, G] layout; n0 is a
-  //    multiple of 16, so both start on a 16-byte boundary), a fixed count of
-  //    DMAs per wave (blocks past the last repeat it, pad lanes the last
-  //    slot); then exactly 3 code chunks of this wave, so "at most 3
-  //    outstanding" means everything before has landed.
-#pragma unroll
-  for (int t = 0; t < kDzSlots / (64 * kWaves) + (kDzSlots % (64 * kWaves) != 0); ++t) {
-    const int j0 = min(64 * (wq + kWaves * t), dzslots - 64);
-    const int j = min(j0 + lane, 3 * G - 1);
-    const uint8_t* src = j < 2 * G ? reinterpret_cast<const uint8_t*>(a.scales) + (size_t)n0 * G * 2 + 16 * j
-                                   : a.zeros + (size_t)n0 * G + 16 * (j - 2 * G);
-    dma16(src, dzt + 16 * j0);
-  }
-#pragma unroll
-  for (int s = 0; s < kRing; ++s) dma_chunk(s, s);
-  wait_vm<kRing>();  // Delta, z and the x loads of this wave have landed
+  wait_vm<kRing>();  // Delta and z of this wave have landed
   __syncthreads();
 
   // 4. The wave's chunks through the ring: wait for chunk i (the ring is the

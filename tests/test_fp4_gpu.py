@@ -164,6 +164,23 @@ def test_fp4_256_tile_kernel_long_k_sampled_rows():
     _check(got, d, lam, pk, rows=_tile_rows(4608, 256))
 
 
+def test_fp4_256_tile_kernel_several_tiles_per_workgroup():
+    """More 256 x 256 tiles than compute units (M=4000, N=4160: 16 x 17 = 272
+    tiles, ragged in m and in n), so workgroups run several tiles one after
+    another, the last ones partial; Y on one row of every 256-row tile and the
+    last rows, every column."""
+    import bit_diffusion_transformer_svdq_amd as K_
+    M, K, N, r = 4000, 1024, 4160, 16
+    print(f"fp4 256-tile persistent M={M} K={K} N={N} r={r}", flush=True)
+    d, lam, pk = _case(_spec(M, K, N, r, 11))
+    K_.debug_set_fp4_tile(256)
+    try:
+        got = _run(d, lam, pk)
+    finally:
+        K_.debug_set_fp4_tile(0)
+    _check(got, d, lam, pk, rows=_tile_rows(M, 256))
+
+
 def _bf16_ladder_blocks(s: int) -> np.ndarray:
     """Blocks of 32 bf16 patterns whose maximum 6 * 2^s fixes the shared
     exponent at s (elements divide by 2^s exactly), filled with every E2M1

@@ -13,13 +13,13 @@
 // These layers see one conditioning vector per image (M = batch), so the
 // kernel is a weight stream: a workgroup owns 16 output channels (one MFMA
 // n-tile) and one tile of up to 16 tokens, and its four waves split K into
-// quarters.  x_hat of the tile's tokens is first written to LDS in the operand
-// order below, with the per-group sums xs = sum_{k in g} x_hat.  The 16 rows'
-// Delta and z then go into LDS by global_load_lds_dwordx4, and each wave
-// streams its quarter of the 16 code rows through a ring of its own: a chunk
-// is 2 groups x 16 rows x 32 bytes = 1 KB, one DMA instruction, three chunks
-// in flight.  The fp32 partials of the waves are added in wave order through
-// LDS.
+// quarters.  The 16 rows' Delta and z go into LDS by global_load_lds_dwordx4,
+// and each wave streams its quarter of the 16 code rows through a ring of its
+// own: a chunk is 2 groups x 16 rows x 32 bytes = 1 KB, one DMA instruction,
+// three chunks in flight.  These DMAs are issued first; while they stream,
+// x_hat of the tile's tokens is written to LDS in the operand order below,
+// with the per-group sums xs = sum_{k in g} x_hat.  The fp32 partials of the
+// waves are added in wave order through LDS.
 //
 // Per group a wave runs two v_mfma_f32_16x16x32_bf16 with A = x_hat and B =
 // 128 + q in bf16: ((w >> 4j) & 0x000F000F) | 0x43004300 turns nibbles j and

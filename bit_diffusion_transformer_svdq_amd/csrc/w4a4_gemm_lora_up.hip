@@ -11,7 +11,8 @@
 // The kernel computes Y^T tiles: the MFMA A operand is the weight tile (rows n),
 // the B operand the activation tile (columns m).  With the 16x16 MFMA output
 // layout (lane l: column l%16, rows 4*(l/16) + v) every lane then owns four
-// consecutive n of one token row m, so Y rows are written 8 bytes at a time.
+// consecutive n of one token row m; the epilogue stages each wave's sub-tile
+// in LDS so that Y leaves in 128-byte row runs.
 //
 // Data movement.  The packed int4 codes go from memory straight into LDS with
 // global_load_lds_dwordx4 (no registers involved), two quant groups at a time:
@@ -23,13 +24,16 @@
 // retire in issue order, so the wait for stage q is an explicit
 // s_waitcnt vmcnt(4): the four DMAs of the next pair, issued last in every
 // iteration, may stay in flight.  Inside a stage, the 16-byte granule gg (0..3)
-// of row r sits at slot 4r + (gg ^ r[3:2]), which keeps the 8-byte fragment
-// reads free of bank conflicts.  Each of the first 256 threads owns the scales
-// of one token or weight row: it loads those of pair q+3 into a register ring
-// (before the pair's DMAs, so waiting for them never waits for the DMAs) and
-// stores the converted scales of pair q+1 into the second of two scale areas.
-// The epilogue reads the lora_up and lora_act fragments straight from memory
-// (they are L2-resident), which keeps the LDS at 52 KB per workgroup.
+// of row r sits at slot 4r + (gg ^ r[3:2]).  A 64-byte stage row covers 16 of
+// the LDS's 32 four-byte banks, so rows r and r + 2 share banks whatever the
+// granule order: the 8-byte fragment reads of a 16-lane phase find two lanes
+// per bank pair (2-way conflicts), which no swizzle of whole 16-byte DMA
+// granules removes.  Each thread owns the scales of one token or weight row and
+// reads them three group pairs at a time (one 16-byte buffer load), ahead of
+// the pairs' DMAs, then stores the converted scales of pair q+1 into the
+// second of two scale areas.  The epilogue reads the lora_up and lora_act
+// fragments straight from memory (they are L2-resident), which keeps the LDS
+// at 52 KB per workgroup.
 //
 // Main loop, per 64-wide group g and wave (64 n x 64 m, 4 x 4 MFMA tiles):
 //  * fragments: 8-byte LDS reads; nibbles widened to int8 as 16*q with

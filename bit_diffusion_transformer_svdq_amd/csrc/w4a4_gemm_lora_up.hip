@@ -144,6 +144,11 @@ struct GemmArgs {
   int splits;         // K-splits per tile (gridDim.y); > 1 needs part and count
   float* part;        // fp32 partial sub-tiles [tiles][splits][4 waves][16][4][64]
   uint32_t* count;    // arrival counters [tiles][4 waves], zero between launches
+  // Tail split (whole >= 0, one-dimensional grid): workgroups [0, whole) run
+  // the first `whole` tiles of the list unsplit, and each later tile runs as
+  // `tsplit` workgroups, one per K-split; partials and counters are indexed
+  // by the tile's place after `whole` ([tail tiles][tsplit][4 waves]...).
+  int whole, tsplit;
 };
 
 // Workgroup id -> (tile_m, tile_n).  Workgroups are dispatched round-robin over
@@ -153,12 +158,14 @@ struct GemmArgs {
 // few activation tiles and a few weight tiles in that XCD's L2.
 constexpr int kXcds = 8;
 constexpr int kBandM = 8;
-__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int T = tiles_m * tiles_n;
+__device__ __forceinline__ int xcd_pos(int bid, int T) {
   const int x = bid % kXcds;
   const int i = bid / kXcds;
   const int per = T / kXcds, rem = T % kXcds;
-  const int t = x * per + min(x, rem) + i;
+  return x * per + min(x, rem) + i;
+}
+// position t of the tile list -> (tile_m, tile_n)
+__device__ __forceinline__ void tile_at(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int band = t / (kBandM * tiles_n);
   const int first = band * kBandM;
   const int rows = min(tiles_m - first, kBandM);
@@ -189,14 +196,38 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
   const int M = p.M, N = p.N, K = p.K, r = p.r;
   const int G = K >> 6;
   const int P = (G + 1) >> 1;  // group pairs
-  // K-split: workgroup (tile, split) runs pairs [qb, qb + Pl) of the tile
-  // (splits == 1: the whole K); pair indices below are local to the split.
-  const int split = blockIdx.y;
-  const int qb = (int)(((long)split * P) / p.splits);
-  const int Pl = (int)(((long)(split + 1) * P) / p.splits) - qb;
+  // Which tile and K-split this workgroup runs: with a uniform split, tile
+  // blockIdx.x (in XCD order) and split blockIdx.y of p.splits; with a tail
+  // split, the first p.whole workgroups run whole tiles and the rest run the
+  // later tiles p.tsplit workgroups each.  `sub0` indexes the tile's partials
+  // and counters.  Workgroup (tile, split) runs pairs [qb, qb + Pl) of the
+  // tile (splits == 1: the whole K); pair indices below are local to it.
+  const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
+  const int bid = blockIdx.x;
+  int pos, split, nsplit;
+  size_t sub0;
+  if (p.whole < 0) {
+    pos = xcd_pos(bid, tiles_m * tiles_n);
+    split = blockIdx.y;
+    nsplit = p.splits;
+    sub0 = (size_t)bid * 4;
+  } else if (bid < p.whole) {
+    pos = xcd_pos(bid, p.whole);
+    split = 0;
+    nsplit = 1;
+    sub0 = 0;
+  } else {
+    const int u = bid - p.whole;
+    pos = p.whole + u / p.tsplit;
+    split = u - (pos - p.whole) * p.tsplit;
+    nsplit = p.tsplit;
+    sub0 = (size_t)(pos - p.whole) * 4;
+  }
+  const int qb = (int)(((long)split * P) / nsplit);
+  const int Pl = (int)(((long)(split + 1) * P) / nsplit) - qb;
   const int KB = K >> 1;       // bytes per packed row
   int tm, tn;
-  tile_of(blockIdx.x, (M + kBM - 1) / kBM, (N + kBN - 1) / kBN, tm, tn);
+  tile_at(pos, tiles_m, tiles_n, tm, tn);
   const int n0 = tn * kBN;
   const int m0 = tm * kBM;
 
@@ -500,9 +531,9 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
     // counter; the wave that arrives last loads the other partials the same
     // way, adds all of them in split order (the result does not depend on
     // timing) and runs the epilogue.  The counter wraps back to zero.
-    if (p.splits > 1) {
-      const size_t sub = (size_t)blockIdx.x * 4 + wave;
-      float* mine = p.part + ((sub * p.splits + split) << 12);
+    if (nsplit > 1) {
+      const size_t sub = sub0 + wave;
+      float* mine = p.part + ((sub * nsplit + split) << 12);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -515,9 +546,9 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the partial is visible to the agent
       __asm__ volatile("" ::: "memory");
       u32 old = 0;
-      if (lane == 0) old = atomicInc(p.count + sub, (u32)(p.splits - 1));
+      if (lane == 0) old = atomicInc(p.count + sub, (u32)(nsplit - 1));
       old = __shfl(old, 0);
-      if (old != (u32)(p.splits - 1)) return;  // another split of this sub-tile is still running
+      if (old != (u32)(nsplit - 1)) return;  // another split of this sub-tile is still running
       __asm__ volatile("" ::: "memory");
       // two halves of the sub-tile (n tiles i = 2h, 2h + 1); per half, the
       // partials of two splits are loaded together (64 loads in flight) and
@@ -525,12 +556,12 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         v4f acc[2][4];
-        for (int s0 = 0; s0 < p.splits; s0 += 2) {
+        for (int s0 = 0; s0 < nsplit; s0 += 2) {
           v4f t[2][2][4];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const int s2 = min(s0 + e, p.splits - 1);
-            const float* src = p.part + ((sub * p.splits + s2) << 12);
+            const int s2 = min(s0 + e, nsplit - 1);
+            const float* src = p.part + ((sub * nsplit + s2) << 12);
 #pragma unroll
             for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -543,7 +574,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int s2 = s0 + e;
-            if (s2 < p.splits) {
+            if (s2 < nsplit) {
 #pragma unroll
               for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -748,17 +779,18 @@ int pick_occupancy(int tiles, int cus) {
 // about 3 + S/2 pairs).  The split count with the least estimated time wins
 // (fitted to measured times on MI355X: few-tile shapes gain up to 2.4x, and
 // 864 tiles with long K gain about 15 % from S = 2).
+// rounds of `units` workgroups over 3 slots per CU, the last one partial
+double split_rounds(long units, int cus) {
+  const long slots = 3L * cus;
+  const long full = units / slots;
+  const long rest = units - full * slots;
+  const long load = (rest + cus - 1) / cus;
+  return (double)full + (load == 0 ? 0.0 : load == 1 ? 0.45 : load == 2 ? 0.8 : 1.0);
+}
+double split_cost(int pairs, int S) { return (double)pairs / S + (S == 1 ? 2.0 : 3.0 + 0.5 * S); }
+
 int pick_splits(int tiles, int pairs, int cus) {
-  const int slots = 3 * cus;
-  auto est = [&](int S) {
-    const long W = (long)tiles * S;
-    const long full = W / slots;
-    const long rest = W - full * slots;
-    const long load = (rest + cus - 1) / cus;
-    const double part = load == 0 ? 0.0 : load == 1 ? 0.45 : load == 2 ? 0.8 : 1.0;
-    const double over = S == 1 ? 2.0 : 3.0 + 0.5 * S;
-    return ((double)pairs / S + over) * ((double)full + part);
-  };
+  auto est = [&](int S) { return split_cost(pairs, S) * split_rounds((long)tiles * S, cus); };
   int best = 1;
   double bt = est(1);
   for (int S = 2; S <= std::min(pairs, 16); ++S) {
@@ -766,6 +798,31 @@ int pick_splits(int tiles, int pairs, int cus) {
     if (t < bt * 0.97) {  // a split has to win clearly
       bt = t;
       best = S;
+    }
+  }
+  return best;
+}
+
+// Tail split: the tiles of the first round run unsplit and only the tiles
+// after it are split (St workgroups each), which fills the second round
+// without the partial traffic of a uniform split.  Returns St, or 0 where it
+// does not beat `uniform_cost` clearly.  Only for launches of one full round
+// and a partial one: measured on MI355X, 864 tiles of 4608 x 3072 -> 3072 run
+// 9-11 % faster (102-104 -> 93-96 us), while after 3 or 4 full rounds
+// (4608 x 3072 -> 9216 and -> 12288) a split tail was 1-2 % slower, the
+// workgroups having drifted apart by then.
+int pick_tail_split(int tiles, int pairs, int cus, double uniform_cost) {
+  const long slots = 3L * cus;
+  const long whole = (tiles / slots) * slots;
+  const long tail = tiles - whole;
+  if (whole != slots || tail == 0) return 0;
+  int best = 0;
+  double bt = uniform_cost * 0.97;
+  for (int St = 2; St <= std::min(pairs, 4); ++St) {
+    const double t = split_cost(pairs, 1) * (double)(whole / slots) + split_cost(pairs, St) * split_rounds(tail * St, cus);
+    if (t < bt) {
+      bt = t;
+      best = St;
     }
   }
   return best;
@@ -780,12 +837,15 @@ struct GemmPlan {
   bool skinny;  // the few-token kernel
   bool big;     // MXFP4 on 256 x 256 tiles
   int tiles;    // 128 x 128 output tiles (tiled kernel)
-  int splits;   // K-splits per tile
+  int splits;   // K-splits per tile (uniform split)
   int occ;      // workgroups per CU the tiled kernel is built for (2 or 3)
+  int whole;    // tail split: tiles run unsplit (-1: uniform split)
+  int tsplit;   // tail split: K-splits of each later tile
+  int wgs() const { return whole < 0 ? tiles * splits : whole + (tiles - whole) * tsplit; }
 };
 
 GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int epilogue, bool fp4) {
-  GemmPlan g{false, false, (int)(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM)), 1, 3};
+  GemmPlan g{false, false, (int)(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM)), 1, 3, -1, 1};
   const int path = g_path.load(std::memory_order_relaxed);
   if (!fp4 && epilogue != kEpilogueQkv && path != 1 && skinny_supported(M, N, K) &&
       (path == 2 || M <= kSkinnyMaxM)) {
@@ -811,21 +871,38 @@ GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int epilogue, bool fp4) {
     const int forced = g_splits.load(std::memory_order_relaxed);
     g.splits = forced > 0 ? std::min(forced, pairs) : pick_splits(g.tiles, pairs, cus);
     if ((size_t)g.tiles * 4 > kWsMaxCounters) g.splits = 1;  // one workspace counter per wave sub-tile
+    if (forced == 0) {
+      const int St = pick_tail_split(g.tiles, pairs, cus,
+                                     split_cost(pairs, g.splits) * split_rounds((long)g.tiles * g.splits, cus));
+      if (St > 0) {
+        g.splits = 1;
+        g.whole = (int)((g.tiles / (3L * cus)) * 3L * cus);
+        g.tsplit = St;
+      }
+    }
   }
-  g.occ = pick_occupancy(g.tiles * g.splits, cus);
+  g.occ = pick_occupancy(g.wgs(), cus);
   return g;
 }
 
 // K-split partials: one arrival counter per wave sub-tile, and per tile and
 // split four 64 x 64 fp32 sub-tiles.
-size_t split_counters(const GemmPlan& g) { return g.splits > 1 ? (size_t)g.tiles * 4 : 0; }
-size_t split_bytes(const GemmPlan& g) { return g.splits > 1 ? (size_t)g.tiles * g.splits * 4 * 4096 * 4 : 0; }
+size_t split_counters(const GemmPlan& g) {
+  if (g.whole >= 0) return (size_t)(g.tiles - g.whole) * 4;
+  return g.splits > 1 ? (size_t)g.tiles * 4 : 0;
+}
+size_t split_bytes(const GemmPlan& g) {
+  if (g.whole >= 0) return (size_t)(g.tiles - g.whole) * g.tsplit * 4 * 4096 * 4;
+  return g.splits > 1 ? (size_t)g.tiles * g.splits * 4 * 4096 * 4 : 0;
+}
 
 template <bool kDump, bool kFp4 = false>
 hipError_t launch(GemmArgs<kDump> a, const GemmPlan& g, Workspace ws, hipStream_t stream) {
   auto kern = w4a4_gemm_kernel<kDump, kDump ? 1 : 3, kFp4>;
   size_t pad = 0;
   a.splits = kDump ? 1 : g.splits;
+  a.whole = kDump ? -1 : g.whole;
+  a.tsplit = g.tsplit;
   if constexpr (!kDump) {
     const size_t nc = split_counters(g);
     if (nc > 0) {
@@ -842,7 +919,8 @@ hipError_t launch(GemmArgs<kDump> a, const GemmPlan& g, Workspace ws, hipStream_
       if (e != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL(kern, dim3(g.tiles, a.splits), dim3(kThreads), pad, stream, a);
+  const dim3 grid = a.whole >= 0 ? dim3(g.wgs(), 1) : dim3(g.tiles, a.splits);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), pad, stream, a);
   return hipGetLastError();
 }
 
@@ -940,7 +1018,7 @@ hipError_t launch_fp4_gemm_lora_up(const uint8_t* act_codes, const uint8_t* act_
   GemmArgs<false> a{act_codes, reinterpret_cast<const uint16_t*>(act_scales), w_codes,
                     reinterpret_cast<const uint16_t*>(w_scales), lora_act, lora_up, bias,
                     y, nullptr, 0, 0, 0, 0, (int)M, (int)N, (int)K, (int)r, epilogue, QkvEpilogue{}, 1,
-                    nullptr, nullptr};
+                    nullptr, nullptr, -1, 1};
   return launch<false, true>(a, g, ws, stream);
 }
 
@@ -959,12 +1037,12 @@ hipError_t launch_w4a4_gemm_lora_up(const uint8_t* act_codes, const uint16_t* ac
   if (dump.acc != nullptr) {
     GemmArgs<true> a{act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,
                      y, dump.acc, dump.m_lo, dump.m_hi, dump.n_lo, dump.n_hi, (int)M, (int)N, (int)K, 0,
-                     kEpilogueNone, QkvEpilogue{}, 1, nullptr, nullptr};
+                     kEpilogueNone, QkvEpilogue{}, 1, nullptr, nullptr, -1, 1};
     return launch<true>(a, g, Workspace{}, stream);
   }
   GemmArgs<false> a{act_codes, act_scales, w_codes, w_scales, lora_act, lora_up, bias,
                     y, nullptr, 0, 0, 0, 0, (int)M, (int)N, (int)K, (int)r, epilogue, QkvEpilogue{}, 1,
-                    nullptr, nullptr};
+                    nullptr, nullptr, -1, 1};
   if (epilogue == kEpilogueQkv) {
     if (qkv == nullptr || N % 384 != 0) return hipErrorInvalidValue;
     a.qkv = *qkv;

@@ -359,6 +359,9 @@ def test_buffers_that_only_touch_are_accepted():
 def test_workspace_size_queries_and_checks():
     L = lib()
     assert L.svdq_w4a4_gemm_workspace_size(4608, 12288, 3072, 32) == 0       # many tiles: no split
+    # 864 tiles on the 256 CUs assumed without a device (768 slots): one round
+    # runs whole, the last 96 tiles as 2 K-splits each (2 x 4 waves x 16 KB)
+    assert L.svdq_w4a4_gemm_workspace_size(4608, 3072, 3072, 32) == (1 << 20) + 96 * 2 * 4 * 16384
     assert L.svdq_w4a4_gemm_workspace_size(0, 256, 256, 16) == 0
     assert L.svdq_w4a4_gemm_workspace_size(64, 96, 256, 16) == 0             # rejected shape
     assert L.svdq_quantize_act_workspace_size(64, 100, 16) == 0

@@ -773,28 +773,31 @@ int pick_occupancy(int tiles, int cus) {
 
 // K-splits per tile.  A launch runs in rounds of 3 workgroups per CU; a last,
 // partial round with r workgroups takes a fraction of a full round that
-// depends on how many share a CU (1: 0.45, 2: 0.8, 3: 1).  A workgroup costs
+// depends on how many share a CU (1: 0.55, 2: 0.7, 3: 1).  A workgroup costs
 // its group pairs plus a fixed overhead (pipeline fill and epilogue, about 2
 // pairs; with splits also the fp32 partial write and the in-order reduction,
-// about 3 + S/2 pairs).  The split count with the least estimated time wins
-// (fitted to measured times on MI355X: few-tile shapes gain up to 2.4x, and
-// 864 tiles with long K gain about 15 % from S = 2).
+// about 4 + S/2 pairs).  The split count with the least estimated time wins.
+// Fitted to forced-split sweeps on MI355X (rocprofv3 kernel times, S = 1..12):
+// 512 x 3072 -> 3072 (96 tiles) best at S = 4 (25.3 us; S = 2: 27.0), 192 tiles
+// of 256 x 3072 -> 12288 and 1024 x 3072 -> 3072 best at S = 2 (35.8 and 35.4
+// us; S = 4: 39.0 and 36.7), 512 x 12288 -> 3072 at S = 8 (53.8 us; S = 1:
+// 131), 384 tiles equal at S = 1 and 2.
 // rounds of `units` workgroups over 3 slots per CU, the last one partial
 double split_rounds(long units, int cus) {
   const long slots = 3L * cus;
   const long full = units / slots;
   const long rest = units - full * slots;
   const long load = (rest + cus - 1) / cus;
-  return (double)full + (load == 0 ? 0.0 : load == 1 ? 0.45 : load == 2 ? 0.8 : 1.0);
+  return (double)full + (load == 0 ? 0.0 : load == 1 ? 0.55 : load == 2 ? 0.7 : 1.0);
 }
-double split_cost(int pairs, int S) { return (double)pairs / S + (S == 1 ? 2.0 : 3.0 + 0.5 * S); }
+double split_cost(int pairs, int S) { return (double)pairs / S + (S == 1 ? 2.0 : 4.0 + 0.5 * S); }
 
 int pick_splits(int tiles, int pairs, int cus) {
   auto est = [&](int S) { return split_cost(pairs, S) * split_rounds((long)tiles * S, cus); };
   int best = 1;
   double bt = est(1);
-  for (int S = 2; S <= std::min(pairs, 16); ++S) {
-    const double t = est(S);
+  for (int S = 2; S <= std::min(pairs, 16); S *= 2) {  // the measured counts (odd ones leave the
+    const double t = est(S);                                 // 6-pair unrolled loop partly idle)
     if (t < bt * 0.97) {  // a split has to win clearly
       bt = t;
       best = S;
@@ -804,9 +807,9 @@ int pick_splits(int tiles, int pairs, int cus) {
 }
 
 // Tail split: the tiles of the first round run unsplit and only the tiles
-// after it are split (St workgroups each), which fills the second round
-// without the partial traffic of a uniform split.  Returns St, or 0 where it
-// does not beat `uniform_cost` clearly.  Only for launches of one full round
+// after it are split in two, which fills the second round without the
+// partial traffic of a uniform split.  Returns 2, or 0 where it does not beat
+// `uniform_cost` clearly.  Only for launches of one full round
 // and a partial one: measured on MI355X, 864 tiles of 4608 x 3072 -> 3072 run
 // 9-11 % faster (102-104 -> 93-96 us), while after 3 or 4 full rounds
 // (4608 x 3072 -> 9216 and -> 12288) a split tail was 1-2 % slower, the
@@ -816,16 +819,9 @@ int pick_tail_split(int tiles, int pairs, int cus, double uniform_cost) {
   const long whole = (tiles / slots) * slots;
   const long tail = tiles - whole;
   if (whole != slots || tail == 0) return 0;
-  int best = 0;
-  double bt = uniform_cost * 0.97;
-  for (int St = 2; St <= std::min(pairs, 4); ++St) {
-    const double t = split_cost(pairs, 1) * (double)(whole / slots) + split_cost(pairs, St) * split_rounds(tail * St, cus);
-    if (t < bt) {
-      bt = t;
-      best = St;
-    }
-  }
-  return best;
+  // two parts per tail tile, the measured configuration
+  const double t = split_cost(pairs, 1) + split_cost(pairs, 2) * split_rounds(tail * 2, cus);
+  return t < uniform_cost * 0.97 ? 2 : 0;
 }
 
 std::atomic<int> g_splits{0};  // test hook (0 = automatic)

@@ -88,7 +88,17 @@ constexpr int kStaticLds = kStages * 2 * kTile + 2 * 4 * kScale;  // 3 tile stag
 constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 constexpr u32 kNib = 0xF0F0F0F0u;
-constexpr int64_t kSkinnyMaxM = 160;  // up to this many tokens the K-split kernel is faster
+// Few tokens go to the few-token kernel up to 64 (one token chunk), and up to
+// 160 for layers of at most 2^24 weights; measured on MI355X (rocprofv3):
+// 3072 -> 12288 at 96 / 128 / 160 tokens 30.6 / 33.4 / 44.9 us there against
+// 25.4 / 25.6 / 35.4 us on the tiled kernel with K-splits, 12288 -> 3072 at 128
+// tokens 33.8 against 32.5 us, while 3072 -> 3072 stays faster there up to 160
+// tokens (16.4 against 19.8 us) and every shape at 64 tokens (19.2 against 25.0
+// us for 3072 -> 12288).
+constexpr int64_t kSkinnyMaxM = 160;
+bool skinny_preferred(int64_t M, int64_t N, int64_t K) {
+  return M <= 64 || (M <= kSkinnyMaxM && N * K <= ((int64_t)1 << 24));
+}
 
 __device__ __forceinline__ u32 pack_bf16(float a, float b) {
   v2f f = {a, b};
@@ -844,7 +854,7 @@ GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int epilogue, bool fp4) {
   GemmPlan g{false, false, (int)(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM)), 1, 3, -1, 1};
   const int path = g_path.load(std::memory_order_relaxed);
   if (!fp4 && epilogue != kEpilogueQkv && path != 1 && skinny_supported(M, N, K) &&
-      (path == 2 || M <= kSkinnyMaxM)) {
+      (path == 2 || skinny_preferred(M, N, K))) {
     g.skinny = true;
     return g;
   }

@@ -154,8 +154,9 @@ svdq_status svdq_debug_set_quant_plan(int k_blocks, int tiles_per_wg);
 
 /*
  * Test hook for call 2 (and svdq_w4a4_group_acc_debug): 0 chooses the kernel
- * by shape (the few-token kernel, whose waves split K, for up to 160 tokens;
- * the tiled kernel above), 1 forces the tiled kernel, 2 the few-token kernel
+ * by shape (the few-token kernel, whose waves split K, for up to 64 tokens,
+ * and up to 160 for layers of at most 2^24 weights; the tiled kernel
+ * otherwise), 1 forces the tiled kernel, 2 the few-token kernel
  * wherever it is supported.  Both compute the same integers and the same
  * dequantization; Y may differ in fp32 rounding order.  Returns INVALID_VALUE
  * for other values.

@@ -887,7 +887,8 @@ GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, int epilogue, bool fp4) {
       }
     }
   }
-  g.occ = pick_occupancy(g.wgs(), cus);
+  // a tail split assumes the whole tiles fill exactly one round of 3 per CU
+  g.occ = g.whole >= 0 ? 3 : pick_occupancy(g.wgs(), cus);
   return g;
 }
 

@@ -32,7 +32,7 @@ import numpy as np
 from ._lib import SvdqError, check, lib
 
 __all__ = ["SvdqError", "lib", "check_device", "quantize_act_lora_down", "w4a4_gemm_lora_up",
-           "mlp_pair", "w4a4_gemm_lora_up_noalloc", "w4a4_gemm_qkv_norm_rope", "w4a4_group_acc_debug", "debug_set_quant_plan", "debug_set_gemm_path", "debug_set_gemm_splits",
+           "mlp_pair", "w4a4_gemm_lora_up_noalloc", "w4a4_gemm_qkv_norm_rope", "w4a4_group_acc_debug", "debug_set_quant_plan", "debug_set_quant_waves", "debug_set_gemm_path", "debug_set_gemm_splits",
            "debug_set_fp4_tile",
            "EPILOGUES", "smooth_from_absmax", "pack_weights", "awq_w4a16_gemm", "awq_w4a16_gemm_stacked",
            "awq_pack_weights",
@@ -152,6 +152,12 @@ def quantize_act_lora_down(x, smooth, lora_down=None, out=None, stream=None, wor
 def debug_set_quant_plan(k_blocks: int = 0, tiles_per_wg: int = 0) -> None:
     """Test hook: force call 1's work split for later calls (0 = automatic)."""
     check(lib().svdq_debug_set_quant_plan(int(k_blocks), int(tiles_per_wg)), "svdq_debug_set_quant_plan")
+
+
+def debug_set_quant_waves(waves: int = 0) -> None:
+    """Test hook: call 1's kernel (0 by shape, 1 one wave per row tile, 2..8 the
+    row-tile kernel with that many waves per K-block)."""
+    check(lib().svdq_debug_set_quant_waves(int(waves)), "svdq_debug_set_quant_waves")
 
 
 def debug_set_gemm_path(path: int = 0) -> None:

@@ -30,6 +30,7 @@ SIGNATURES = {
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
     "svdq_quantize_act_workspace_size": (_size, [_i64, _i64, _i64]),
     "svdq_debug_set_quant_plan": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
+    "svdq_debug_set_quant_waves": (ctypes.c_int, [ctypes.c_int]),
     "svdq_debug_set_gemm_path": (ctypes.c_int, [ctypes.c_int]),
     "svdq_debug_set_gemm_splits": (ctypes.c_int, [ctypes.c_int]),
     "svdq_debug_set_fp4_tile": (ctypes.c_int, [ctypes.c_int]),

@@ -256,6 +256,12 @@ svdq_status svdq_debug_set_quant_plan(int k_blocks, int tiles_per_wg) {
   return ok();
 }
 
+svdq_status svdq_debug_set_quant_waves(int waves) {
+  if (waves < 0 || waves > 8) return fail(SVDQ_STATUS_INVALID_VALUE, "bad wave count %d (0..8)", waves);
+  svdq::set_quant_waves_override(waves);
+  return ok();
+}
+
 svdq_status svdq_debug_set_gemm_path(int path) {
   if (path < 0 || path > 2) return fail(SVDQ_STATUS_INVALID_VALUE, "bad gemm path %d (0, 1 or 2)", path);
   svdq::set_gemm_path_override(path);

@@ -98,15 +98,17 @@ struct QuantArgs {
 };
 
 // One 64-wide group of one wave: smooth, quantize, pack, and accumulate the
-// lora_down partial.  mu_g points at the group's 64 reciprocals in LDS and
-// lf_g at its lora_down fragments in LDS ([NT][2 halves][64 lanes]).  Returns
+// lora_down partial.  mu_g points at the group's 64 reciprocals in LDS; the
+// lora_down fragment of rank tile t, half i is lf_g[(2t + i) * fstride + flane]
+// (in LDS: [NT][2 halves][64 lanes], fstride 64, flane the lane; in registers:
+// an array of 2 NT fragments, fstride 1, flane 0).  Returns
 // the row's codes as bytes 4*seg..+3 (code_a) and 16+4*seg..+3 (code_b) of
 // the group's 32, and the scale's bf16 bits (int4), or the two E8M0 exponents
 // of the group's 32-blocks (MXFP4: block 2g in the low byte).
 template <int NT, bool kFp4>
 __device__ __forceinline__ void quant_group(const uint4& xa, const uint4& xb, const float* mu_g,
-                                            const v8bf* lf_g, int lane, v4f* lacc, u32& code_a,
-                                            u32& code_b, u32& scale) {
+                                            const v8bf* lf_g, int fstride, int flane, int lane,
+                                            v4f* lacc, u32& code_a, u32& code_b, u32& scale) {
   const int seg = lane >> 4;
   const v4f m0a = *reinterpret_cast<const v4f*>(mu_g + 8 * seg);
   const v4f m0b = *reinterpret_cast<const v4f*>(mu_g + 8 * seg + 4);
@@ -245,7 +247,7 @@ __device__ __forceinline__ void quant_group(const uint4& xa, const uint4& xb, co
     for (int i = 0; i < 2; ++i) {
       const v4u av = {xh[4 * i], xh[4 * i + 1], xh[4 * i + 2], xh[4 * i + 3]};
       lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av),
-                                                        lf_g[(2 * t + i) * 64 + lane], lacc[t],
+                                                        lf_g[(2 * t + i) * fstride + flane], lacc[t],
                                                         0, 0, 0);
     }
   }
@@ -408,7 +410,8 @@ __global__ __launch_bounds__(64 * kMaxTiles) void quant_lora_down_kernel(QuantAr
     for (int s = 0; s < kDepth; ++s) {
       const int gl = rnd * kDepth + s;
       u32 ca, cb, sc;
-      quant_group<NT, kFp4>(ra[s], rb[s], mu_s + 64 * gl, lf_s + gl * NT * 128, lane, lacc, ca, cb, sc);
+      quant_group<NT, kFp4>(ra[s], rb[s], mu_s + 64 * gl, lf_s + gl * NT * 128, 64, lane, lane, lacc, ca, cb,
+                            sc);
       const int gn = g0 + min(gl + kDepth, gc - 1);
       ra[s] = *reinterpret_cast<const uint4*>(xrow + 64 * gn);
       rb[s] = *reinterpret_cast<const uint4*>(xrow + 64 * gn + 32);
@@ -421,7 +424,8 @@ __global__ __launch_bounds__(64 * kMaxTiles) void quant_lora_down_kernel(QuantAr
     const int gl = nfull * kDepth + s;
     if (gl < gc) {
       u32 ca, cb, sc;
-      quant_group<NT, kFp4>(ra[s], rb[s], mu_s + 64 * gl, lf_s + gl * NT * 128, lane, lacc, ca, cb, sc);
+      quant_group<NT, kFp4>(ra[s], rb[s], mu_s + 64 * gl, lf_s + gl * NT * 128, 64, lane, lane, lacc, ca, cb,
+                            sc);
       emit(gl, ca, cb, sc);
     }
   }
@@ -491,11 +495,212 @@ __global__ __launch_bounds__(64 * kMaxTiles) void quant_lora_down_kernel(QuantAr
   }
 }
 
+// Few row tiles (a few hundred tokens): a workgroup owns ONE row tile and one
+// K-block, and its KW waves split the block's groups into KW consecutive runs.
+// With one wave per row tile (the kernel above) a short row count leaves most
+// compute units idle unless K is cut into many blocks, whose partials then meet
+// through memory (a store, its completion, an atomic and the loads: several
+// round trips on the critical path).  Here the waves' lora partials are added
+// in LDS, in wave order, and only the K-blocks (few or one) meet through the
+// workspace as above.  No wave shares a group with another, so each loads its
+// own lora_down fragments with its X (a ring of kRowDepth groups in registers)
+// and only the reciprocals mu of the block, computed once per workgroup, go
+// through LDS.
+constexpr int kMaxKW = 8;  // waves per workgroup in the row-tile kernel
+
+template <int NT>
+constexpr int row_depth() { return NT <= 2 ? 4 : (NT <= 4 ? 3 : 2); }
+
+template <int NT, bool kFp4>
+__global__ __launch_bounds__(64 * kMaxKW) void quant_lora_down_rows_kernel(QuantArgs a) {
+  constexpr int R = NT * 16;
+  constexpr int kD = row_depth<NT>();
+  constexpr int nt1 = NT > 0 ? NT : 1;
+  extern __shared__ __align__(16) float rsm[];
+  float* mu_s = rsm;                   // [GB * 64]
+  v4f* red_s = reinterpret_cast<v4f*>(rsm + a.GB * 64);  // [KW][NT][64 lanes]
+
+  const int lane = threadIdx.x & 63;
+  const int kw = threadIdx.x >> 6;
+  const int KW = blockDim.x >> 6;
+  const int nthr = blockDim.x;
+  const int tile = blockIdx.x;
+  const int kb = blockIdx.y;
+  const int g0 = kb * a.GB;
+  const int gc = min(a.GB, a.G - g0);
+  const int wb = gc * kw / KW;         // this wave's groups: [wb, we) of the block
+  const int n = gc * (kw + 1) / KW - wb;
+  const int rho = lane & 15;
+  const int seg = lane >> 4;
+  const int row = tile * 16 + rho;
+  const bool row_ok = row < a.M;
+  const int K = a.K;
+
+  // 1. lambda of the block (short loads, first, so that waiting for them
+  //    leaves the ring in flight), then the ring: X and the lora_down
+  //    fragments of the wave's first kD groups.  Every load is unconditional
+  //    (indexes past the end repeat the last one), so each wait is an exact
+  //    vmcnt.
+  constexpr int kMu = 8;
+  const int nmu = 64 * gc;
+  float lv[kMu];
+#pragma unroll
+  for (int j = 0; j < kMu; ++j) lv[j] = a.lam[64 * g0 + min(j * nthr + (int)threadIdx.x, nmu - 1)];
+
+  const int gw = g0 + wb;              // first group of the wave
+  const int nl = max(n, 1) - 1;        // last valid local index
+  const uint16_t* xrow = a.x + (size_t)(row_ok ? row : a.M - 1) * K + 8 * seg;
+  const uint16_t* lrow = a.lora_down + (size_t)rho * K + 8 * seg;
+  uint4 ra[kD], rb[kD];
+  v8bf lf[kD][2 * nt1];
+  auto load_slot = [&](int s, int j) __attribute__((always_inline)) {
+    const int g = gw + min(j, nl);
+    ra[s] = *reinterpret_cast<const uint4*>(xrow + 64 * g);
+    rb[s] = *reinterpret_cast<const uint4*>(xrow + 64 * g + 32);
+    if constexpr (NT > 0) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          lf[s][2 * t + h] = *reinterpret_cast<const v8bf*>(lrow + (size_t)16 * t * K + 64 * g + 32 * h);
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < kD; ++s) load_slot(s, s);
+
+  // 2. mu = fl32(1 / lambda) into LDS; no __syncthreads, whose fence would wait
+  //    for the ring as well
+#pragma unroll
+  for (int j = 0; j < kMu; ++j) mu_s[min(j * nthr + (int)threadIdx.x, nmu - 1)] = 1.0f / lv[j];
+  for (int c = kMu * nthr + (int)threadIdx.x; c < nmu; c += nthr) mu_s[c] = 1.0f / a.lam[64 * g0 + c];
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+
+  uint8_t* crow = a.codes + (size_t)row * (K >> 1);
+  uint16_t* srow = a.scales + (size_t)row * a.G;
+  v4f lacc[nt1];
+#pragma unroll
+  for (int t = 0; t < nt1; ++t) lacc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // 3. the wave's groups in rounds of kD, each slot consumed and refilled in
+  //    place; codes of groups 2i and 2i+1 (counted from the wave's first group)
+  //    leave together
+  if (n > 0) {
+    const bool pair_aligned = (((size_t)row * a.G + gw) & 1) == 0;
+    u32 pa = 0, pb = 0, ps = 0;
+    auto emit = [&](int j, u32 ca, u32 cb, u32 sc) __attribute__((always_inline)) {
+      if ((j & 1) == 0) {
+        pa = ca;
+        pb = cb;
+        ps = sc;
+      } else {
+        store_group_pair(pa, pb, ps, ca, cb, sc, gw + j - 1, seg, row_ok, pair_aligned, crow, srow);
+      }
+    };
+    const int nfull = n / kD;
+    for (int rnd = 0; rnd < nfull; ++rnd) {
+#pragma unroll
+      for (int s = 0; s < kD; ++s) {
+        const int j = rnd * kD + s;
+        u32 ca, cb, sc;
+        quant_group<NT, kFp4>(ra[s], rb[s], mu_s + 64 * (wb + j), lf[s], 1, 0, lane, lacc, ca, cb, sc);
+        load_slot(s, j + kD);
+        emit(j, ca, cb, sc);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kD; ++s) {
+      const int j = nfull * kD + s;
+      if (j < n) {
+        u32 ca, cb, sc;
+        quant_group<NT, kFp4>(ra[s], rb[s], mu_s + 64 * (wb + j), lf[s], 1, 0, lane, lacc, ca, cb, sc);
+        emit(j, ca, cb, sc);
+      }
+    }
+    if (n & 1) store_group(pa, pb, ps, gw + n - 1, seg, row_ok, crow, srow);
+  }
+
+  if constexpr (NT > 0) {
+    // 4. the waves' partials, added in wave order by wave 0 (lane l holds rows
+    //    4*(l/16)+v of the tile, rank 16t + l%16)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) red_s[(kw * NT + t) * 64 + lane] = lacc[t];
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): LDS writes done, code stores may fly
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    if (kw != 0) return;
+    v4f sum[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) sum[t] = lacc[t];
+    for (int w = 1; w < KW; ++w)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) sum[t] += red_s[(w * NT + t) * 64 + lane];
+
+    if (a.KB > 1) {
+      // 5. K-blocks meet through the workspace, as in the kernel above
+      float* mine = a.part + ((size_t)kb * a.T + tile) * NT * 256;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          __hip_atomic_store(mine + (t * 4 + v) * 64 + lane, sum[t][v], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      __asm__ volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the partial is visible to the agent
+      __asm__ volatile("" ::: "memory");
+      u32 old = 0;
+      if (lane == 0) old = atomicInc(a.count + tile, (u32)(a.KB - 1));
+      old = __shfl(old, 0);
+      if (old != (u32)(a.KB - 1)) return;
+      __asm__ volatile("" ::: "memory");
+      v4f tot[NT];
+      constexpr int kRd = 8;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        tot[t] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j0 = 0; j0 < a.KB; j0 += kRd) {
+          v4f pv[kRd];
+#pragma unroll
+          for (int i = 0; i < kRd; ++i) {
+            const int j = min(j0 + i, a.KB - 1);
+            const float* p = a.part + (((size_t)j * a.T + tile) * NT + t) * 256;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              pv[i][e] = __hip_atomic_load(p + e * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+#pragma unroll
+          for (int i = 0; i < kRd; ++i) {
+            const int j = j0 + i;
+            if (j < a.KB) {
+              const v4f v = (j == kb) ? sum[t] : pv[i];
+              tot[t] = (j == 0) ? v : tot[t] + v;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) sum[t] = tot[t];
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int rr = tile * 16 + 4 * (lane >> 4) + v;
+        if (rr < a.M)
+          a.lora_act[(size_t)rr * R + 16 * t + rho] = (uint16_t)(pack_bf16(sum[t][v], 0.f) & 0xFFFFu);
+      }
+  }
+}
+
 // ---------------------------------------------------------------- host side
 
 struct Plan {
   int TB, GB, KB, nrb;
   size_t lds;
+  int KW = 0;  // 0: one wave per row tile (TB tiles per workgroup); else the row-tile kernel's waves
 };
 
 size_t lds_bytes(int GB, int NT) { return (size_t)GB * NT * 2048; }  // dynamic part
@@ -545,16 +750,84 @@ Plan make_plan(int T, int G, int NT, int cus) {
   return best;
 }
 
-std::atomic<int> g_force_tb{0}, g_force_kb{0};  // test hook (0 = automatic)
+// The row-tile kernel's plan: KB K-blocks of GB groups (at most kMaxGB, for
+// the reciprocals in LDS), KW waves per workgroup splitting each block.
+Plan rows_plan(int T, int G, int NT, int KB, int KW) {
+  KB = std::max(KB, (G + kMaxGB - 1) / kMaxGB);
+  const int GB = (G + KB - 1) / KB;
+  KB = (G + GB - 1) / GB;
+  KW = std::max(1, std::min({KW, kMaxKW, GB}));
+  Plan p{1, GB, KB, T, (size_t)GB * 256 + (size_t)KW * NT * 1024};
+  p.KW = KW;
+  return p;
+}
+
+// Row-tile plans are used up to this many row tiles, while what they read (X
+// and, per row tile, the lora_down slices: T G (2 + 2 NT) KB) stays below
+// kRowsMaxKB, and with a low-rank branch (without one the kernel above has no
+// partials to add either).  Measured against the kernel above (HIP graph
+// replays, r = 32): faster at 64 to 2048 tokens for K = 3072 (6.8 / 7.7 /
+// 8.2 / 9.2 / 12.0 us at 64 / 256 / 512 / 1024 / 2048 tokens against 9.7 /
+// 12.2 / 11.3 / 13.8 / 13.5) and at 64 to 1024 tokens for K = 12288 (9.4 /
+// 12.9 / 19.9 against 16.7 / 20.9 / 22.8 us); slower at 2048 tokens for
+// K = 12288 (31.0 against 25.1 us), where 128 row tiles each reading the
+// whole 768 KiB lora_down make 151 MB with X.
+constexpr int kRowsMaxTiles = 128;
+constexpr double kRowsMaxKB = 96.0 * 1024;
+
+// Estimated time (us) of a row-tile plan, fitted (least squares) to a sweep of
+// HIP-graph-replayed launches on MI355X: 64 to 2048
+// tokens, K = 3072, 12288 and 15360, r = 32, KW in {2, 3, 4, 6, 8} and 4 to 24
+// K-blocks (rms error 1.3 us; on each of the twelve swept shapes the plan it
+// picks is the measured best or within 1 us of it).  Terms: launch and first
+// round trip; each group a wave walks, per workgroup sharing a compute unit
+// (the quantizer's dependency chain, ~0.25 us); the KB of X and lora_down a
+// compute unit reads; waves per compute unit; and with split K, the
+// workspace round trips and each batch of 8 partial reads.
+double rows_cost(int T, int G, int NT, int KW, int KB, int cus) {
+  const Plan p = rows_plan(T, G, NT, KB, KW);
+  const int gpw = (p.GB + p.KW - 1) / p.KW;
+  const long wgs = (long)T * p.KB;
+  const long per_cu = (wgs + cus - 1) / cus;
+  const double kb_per_cu = (double)p.GB * (2 + 2 * NT) * per_cu;
+  const int batches = p.KB == 1 ? 0 : 1 + (p.KB - 1) / 8;
+  return 1.74 + 0.252 * gpw * per_cu + 0.028 * kb_per_cu + 0.539 * p.KW * per_cu + 1.214 * batches +
+         (p.KB > 1 ? 1.462 : 0.0);
+}
+
+Plan best_rows_plan(int T, int G, int NT, int cus) {
+  Plan best = rows_plan(T, G, NT, 1, 2);
+  double best_cost = 1e300;
+  for (int KW : {2, 3, 4, 6, 8}) {
+    for (int KB = 1; KB <= std::min(G, 32); ++KB) {
+      const Plan p = rows_plan(T, G, NT, KB, KW);
+      if (p.KB != KB || p.KW != KW) continue;  // clipped: the same plan as another (KB, KW)
+      const double c = rows_cost(T, G, NT, KW, KB, cus);
+      if (c < best_cost - 1e-9) {
+        best_cost = c;
+        best = p;
+      }
+    }
+  }
+  return best;
+}
+
+std::atomic<int> g_force_tb{0}, g_force_kb{0}, g_force_kw{0};  // test hooks (0 = automatic)
 
 // The plan of a call on the current device, with the test hook's forced split.
 Plan plan_for(int64_t M, int64_t K, int64_t r) {
   const int NT = (int)(r / 16);
   const int T = (int)((M + 15) / 16);
   const int G = (int)(K / 64);
-  Plan p = make_plan(T, G, NT, current_cus());
-  const int force_kb = g_force_kb.load(), force_tb = g_force_tb.load();
-  if (force_kb > 0 || force_tb > 0) {
+  const int cus = current_cus();
+  const int force_kb = g_force_kb.load(), force_tb = g_force_tb.load(), force_kw = g_force_kw.load();
+  Plan p = make_plan(T, G, NT, cus);
+  if (force_kw > 1) {
+    p = rows_plan(T, G, NT, force_kb > 0 ? std::min(force_kb, G) : 1, force_kw);
+  } else if (force_kw == 0 && force_kb == 0 && force_tb == 0 && NT > 0 && T <= kRowsMaxTiles &&
+             (double)T * G * (2 + 2 * NT) <= kRowsMaxKB) {
+    p = best_rows_plan(T, G, NT, cus);
+  } else if (force_kb > 0 || force_tb > 0) {
     const int TB = force_tb > 0 ? std::min(force_tb, kMaxTiles) : p.TB;
     const int KB0 = force_kb > 0 ? std::min(force_kb, G) : p.KB;
     const int GB = (G + KB0 - 1) / KB0;
@@ -566,7 +839,7 @@ Plan plan_for(int64_t M, int64_t K, int64_t r) {
   // C ABI rejects such shapes
   if (p.KB > 1 && NT > 0 && (size_t)T > kWsMaxCounters) {
     const int GB = std::min(G, kMaxGB);
-    p = Plan{p.TB, GB, (G + GB - 1) / GB, p.nrb, lds_bytes(GB, NT)};
+    p = p.KW > 0 ? rows_plan(T, G, NT, 1, p.KW) : Plan{p.TB, GB, (G + GB - 1) / GB, p.nrb, lds_bytes(GB, NT)};
   }
   return p;
 }
@@ -583,6 +856,16 @@ size_t part_bytes(const Plan& p, int64_t M, int64_t r) {
 template <int NT, bool kFp4>
 hipError_t launch_nt(const QuantArgs& a, const Plan& p, hipStream_t stream) {
   const dim3 grid(p.nrb, p.KB);
+  if (p.KW > 0) {
+    auto kern = quant_lora_down_rows_kernel<NT, kFp4>;
+    if (p.lds > 64 * 1024) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, grid, dim3(64 * p.KW), p.lds, stream, a);
+    return hipGetLastError();
+  }
   const dim3 block(64 * p.TB);
   auto kern = quant_lora_down_kernel<NT, kFp4>;
   if (p.lds + kMuBytes > 64 * 1024) {
@@ -600,6 +883,8 @@ void set_quant_plan_override(int k_blocks, int tiles_per_wg) {
   g_force_kb.store(std::max(0, k_blocks));
   g_force_tb.store(std::max(0, tiles_per_wg));
 }
+
+void set_quant_waves_override(int waves) { g_force_kw.store(std::max(0, waves)); }
 
 size_t quant_workspace_bytes(int64_t M, int64_t K, int64_t r) {
   if (M <= 0) return 0;

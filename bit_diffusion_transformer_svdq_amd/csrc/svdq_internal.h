@@ -75,6 +75,7 @@ hipError_t launch_quant_lora_down(const uint16_t* x, const float* lam, const uin
 // Test hook: forces call 1's work split (K-blocks, row tiles per workgroup);
 // 0 keeps the automatic choice.  Affects later launches of this process.
 void set_quant_plan_override(int k_blocks, int tiles_per_wg);
+void set_quant_waves_override(int waves);
 
 // Window of the accumulator dump: rows [m_lo, m_hi) and columns [n_lo, n_hi)
 // of the launched problem go to acc[((m - m_lo) * (n_hi - n_lo) + n - n_lo) * G + g].

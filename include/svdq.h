@@ -153,6 +153,17 @@ size_t svdq_quantize_act_workspace_size(int64_t M, int64_t K, int64_t r);
 svdq_status svdq_debug_set_quant_plan(int k_blocks, int tiles_per_wg);
 
 /*
+ * Test hook for call 1: picks its kernel for every later call in this process.
+ * 0 chooses by shape; 1 forces the kernel with one wave per row tile of 16
+ * tokens; 2..8 force the row-tile kernel, in which a workgroup owns one row
+ * tile and that many waves split each K-block's groups, their lora_down
+ * partials added in LDS (k_blocks of svdq_debug_set_quant_plan still sets the
+ * K-blocks, tiles_per_wg is not used).  Codes and scales do not change;
+ * lora_act may change by a bf16 ulp.  Returns INVALID_VALUE outside 0..8.
+ */
+svdq_status svdq_debug_set_quant_waves(int waves);
+
+/*
  * Test hook for call 2 (and svdq_w4a4_group_acc_debug): 0 chooses the kernel
  * by shape (the few-token kernel, whose waves split K, for up to 64 tokens,
  * and up to 160 for layers of at most 2^24 weights; the tiled kernel

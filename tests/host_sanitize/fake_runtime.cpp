@@ -55,6 +55,7 @@ size_t quant_workspace_bytes(int64_t, int64_t, int64_t) { return g_fake.quant_ne
 size_t gemm_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int, bool) { return g_fake.gemm_need; }
 bool awq_supported(int64_t K, int64_t M) { return K <= (M == 1 ? 16384 : M <= 4 ? 8192 : 4096); }
 void set_quant_plan_override(int, int) {}
+void set_quant_waves_override(int) {}
 void set_gemm_path_override(int) {}
 void set_gemm_splits_override(int) {}
 void set_fp4_tile_override(int) {}

@@ -259,6 +259,10 @@ def test_quant_plan_hook_arguments():
     assert L.svdq_debug_set_quant_plan(2, 13) == INVALID_VALUE
     assert L.svdq_debug_set_quant_plan(3, 12) == SUCCESS
     assert L.svdq_debug_set_quant_plan(0, 0) == SUCCESS
+    assert L.svdq_debug_set_quant_waves(-1) == INVALID_VALUE
+    assert L.svdq_debug_set_quant_waves(9) == INVALID_VALUE
+    assert L.svdq_debug_set_quant_waves(8) == SUCCESS
+    assert L.svdq_debug_set_quant_waves(0) == SUCCESS
 
 
 def test_gemm_path_hook_arguments():

@@ -115,6 +115,22 @@ def test_fp4_forced_quant_plans():
         _check(got, d, lam, pk)
 
 
+def test_fp4_row_tile_quant_kernel():
+    """MXFP4 call 1 through the row-tile kernel (one workgroup per row tile,
+    waves splitting K; one and two K-blocks)."""
+    import bit_diffusion_transformer_svdq_amd as K
+    d, lam, pk = _case(_spec(130, 1152, 64, 32, 11))
+    for waves, kb in [(8, 0), (4, 2)]:
+        K.debug_set_quant_waves(waves)
+        K.debug_set_quant_plan(kb, 0)
+        try:
+            got = _run(d, lam, pk)
+        finally:
+            K.debug_set_quant_waves(0)
+            K.debug_set_quant_plan(0, 0)
+        _check(got, d, lam, pk)
+
+
 def _tile_rows(M, tile):
     """One row of every row tile at an offset that walks through the tile,
     plus the first and the last two rows."""

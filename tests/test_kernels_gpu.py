@@ -47,7 +47,7 @@ def test_tiny_config_full_parity():
     d, lam, packed = oracle_case("tiny")
     got = _run(d, lam, packed)
     ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
-    _check_quant(got, ref)
+    _check_quant(got, ref, packed["lora_down"])
     _check_y(got["y"], d, lam, packed, ref)
 
 
@@ -68,7 +68,7 @@ def test_edge_shapes(M, K, N, r):
     d, lam, packed = custom_case(M, K, N, r, seed=M + N)
     got = _run(d, lam, packed)
     ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
-    _check_quant(got, ref)
+    _check_quant(got, ref, packed["lora_down"])
     _check_y(got["y"], d, lam, packed, ref)
 
 
@@ -89,7 +89,7 @@ def test_both_gemm_kernels_parity(path, M, K, N, r):
         acc = K_.w4a4_group_acc_debug(to_dev(ref["act_codes"]), to_dev(packed["w_codes"])).cpu().numpy()
     finally:
         K_.debug_set_gemm_path(0)
-    _check_quant(got, ref)
+    _check_quant(got, ref, packed["lora_down"])
     _check_y(got["y"], d, lam, packed, ref)
     want = O.group_accumulators(ref["act_codes"], packed["w_codes"])
     assert np.array_equal(acc, want), np.argwhere(acc != want)[:5]
@@ -109,7 +109,7 @@ def test_no_bias_and_rank0():
     d, lam, packed = custom_case(96, 256, 128, 0, seed=11)
     got = _run(d, lam, packed, bias=False)
     ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
-    _check_quant(got, ref)
+    _check_quant(got, ref, packed["lora_down"])
     _check_y(got["y"], d, lam, packed, ref, bias=False)
 
 
@@ -123,7 +123,7 @@ def test_extreme_groups_zero_and_saturated():
     d = dict(d, x=x)
     got = _run(d, lam, packed)
     ref = O.quantize_act_lora_down(x, lam, packed["lora_down"])
-    _check_quant(got, ref)
+    _check_quant(got, ref, packed["lora_down"])
     assert np.all(got["act_scales"][:, 1] == 0)
     _check_y(got["y"], d, lam, packed, ref)
 
@@ -140,7 +140,7 @@ def test_bf16_rounding_ties_in_smoothing():
     assert ties.sum() > 100
     got = _run(d, lam2, packed)
     ref = O.quantize_act_lora_down(d["x"], lam2, packed["lora_down"])
-    _check_quant(got, ref)
+    _check_quant(got, ref, packed["lora_down"])
 
 
 def test_empty_batch_is_a_noop():
@@ -225,6 +225,36 @@ def test_forced_work_splits(plan, M, K, r):
         K_.debug_set_quant_plan(0, 0)
     _check_quant(got, ref, packed["lora_down"] if r else None)
     for k in got:  # the K-block partials are added in a fixed order
+        assert np.array_equal(got[k], again[k]), k
+
+
+@pytest.mark.parametrize("waves,kb,M,K,r", [
+    (8, 0, 200, 448, 32),    # 7 groups: one group per wave, 7 waves (ragged last row tile)
+    (8, 2, 200, 448, 32),    # blocks of 4 and 3 groups: a wave of the last block has none
+    (8, 1, 64, 3072, 32),    # 48 groups over 8 waves, 6 each: pairs only
+    (8, 0, 61, 3072, 128),   # 8 rank tiles, one K-block
+    (5, 3, 130, 1344, 48),   # 21 groups in 3 blocks of 7 over 5 waves: odd runs, K-block partials
+    (3, 0, 33, 384, 0),      # no low-rank branch
+    (2, 4, 40, 3072, 16),    # 4 blocks of 12 over 2 waves
+    (8, 0, 16, 15360, 32),   # 240 groups: 4 blocks of 60 (LDS bound), one row tile
+])
+def test_row_tile_kernel_forced(waves, kb, M, K, r):
+    """Call 1's row-tile kernel (a workgroup per row tile, its waves splitting
+    each K-block, partials added in LDS in wave order): the oracle's codes and
+    scales bit for bit, lora_act within its bound, the same bits on a repeat."""
+    import bit_diffusion_transformer_svdq_amd as K_
+    d, lam, packed = custom_case(M, K, 64, r, seed=M + K + waves)
+    ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
+    K_.debug_set_quant_waves(waves)
+    K_.debug_set_quant_plan(kb, 0)
+    try:
+        got = _quant(d, lam, packed)
+        again = _quant(d, lam, packed)
+    finally:
+        K_.debug_set_quant_waves(0)
+        K_.debug_set_quant_plan(0, 0)
+    _check_quant(got, ref, packed["lora_down"] if r else None)
+    for k in got:
         assert np.array_equal(got[k], again[k]), k
 
 
@@ -342,7 +372,7 @@ def test_forced_gemm_splits(splits, M, K, N, r):
     finally:
         K_.debug_set_gemm_splits(0)
         K_.debug_set_gemm_path(0)
-    _check_quant(got, ref)
+    _check_quant(got, ref, packed["lora_down"])
     _check_y(got["y"], d, lam, packed, ref)
     assert np.array_equal(got["y"], again["y"])
 

@@ -1,4 +1,4 @@
-"""Seeded random shapes through the automatic plans of both calls.
+"""Seeded random shapes through the automatic plans of both calls (int4 and MXFP4).
 
 Kernel choice, work splits, K-splits and tail splits are all picked by the
 host's cost models from the shape, so a plan that no hand-picked test forces
@@ -6,8 +6,8 @@ could still be wrong.  Each shape runs calls 1 and 2 with every plan left
 automatic and is checked against the CPU oracle: codes and scales bit-exact,
 lora_act within its fp32 summation bound, Y within relative Frobenius 5e-3 and
 max-abs 1e-2 * max|Y*| on every row.  Shapes: M in [1, 700), K a multiple of 64
-up to 2496, N a multiple of 64 (the ABI's rule) up to 768, r in {0, 16, 32, 48,
-64}.
+up to 2496 (of 128 up to 2560 for MXFP4, the ABI's rule), N a multiple of 64 (the
+ABI's rule) up to 768, r in {0, 16, 32, 48, 64}.
 """
 import numpy as np
 import pytest
@@ -18,12 +18,12 @@ from tests.gpu_util import bf16_bits, check_quant, check_y, custom_case, to_dev,
 pytestmark = pytest.mark.gpu
 
 
-def _shapes(n, seed):
+def _shapes(n, seed, kq=64):
     rng = np.random.default_rng(seed)
     out = []
     for _ in range(n):
         M = int(rng.integers(1, 700))
-        K = 64 * int(rng.integers(1, 40))
+        K = kq * int(rng.integers(1, 2560 // kq))
         N = 64 * int(rng.integers(1, 13))
         r = int(rng.choice([0, 16, 32, 48, 64]))
         out.append((M, K, N, r))
@@ -55,3 +55,10 @@ def test_random_shape_automatic_plans(M, K, N, r):
     ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
     check_quant(got, ref, packed["lora_down"])
     check_y(bf16_bits(y), d, lam, packed, ref)
+
+
+@pytest.mark.parametrize("M,K,N,r", _shapes(12, 20261204, kq=128))
+def test_random_shape_automatic_plans_mxfp4(M, K, N, r):
+    from tests.test_fp4_gpu import _case, _check, _run, _spec
+    d, lam, pk = _case(_spec(M, K, N, r, M + K + N + r))
+    _check(_run(d, lam, pk), d, lam, pk)

@@ -315,6 +315,20 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkinnyArgs<kDump> a
       }
   }
 
+  // The thread's output items e = tid + it * kThreads (it < N16, since a chunk
+  // has at most 64 * NT / 2 items): their bias pairs are loaded here, so that
+  // the loads' round trip passes during the reduction instead of after it.
+  static_assert(kMC * (NT / 2) <= kThreads * N16, "output items per thread");
+  const int rows = min(kMC, a.M - m0);
+  u32 bpair[N16];
+#pragma unroll
+  for (int it = 0; it < N16; ++it) {
+    const int e = tid + it * kThreads;
+    const int m = e / (NT / 2), nl = 2 * (e - m * (NT / 2));
+    const int gn = min(n0 + nl, a.N - 2);  // N is a multiple of 16: gn, gn + 1 < N
+    bpair[it] = a.bias ? *reinterpret_cast<const u32*>(a.bias + gn) : 0u;
+  }
+
   // 5. fixed-order reduction: slot w' = y(w') + y(w'+4), then
   //    out = ((slot0 + slot1) + slot2) + slot3, plus the bias
   constexpr size_t kSlot = slot_floats<N16>();
@@ -349,11 +363,12 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkinnyArgs<kDump> a
         }
   }
   lds_barrier();
-  const int rows = min(kMC, a.M - m0);
-  for (int e = tid; e < rows * (NT / 2); e += kThreads) {  // two consecutive n per thread
+#pragma unroll
+  for (int it = 0; it < N16; ++it) {  // two consecutive n per item
+    const int e = tid + it * kThreads;
     const int m = e / (NT / 2), nl = 2 * (e - m * (NT / 2));
     const int gm = m0 + m, gn = n0 + nl;
-    if (gn < a.N) {  // N is a multiple of 16, so gn + 1 < N too
+    if (m < rows && gn < a.N) {  // N is a multiple of 16, so gn + 1 < N too
       float o[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -361,7 +376,7 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkinnyArgs<kDump> a
         const int j = nn >> 4, v = nn & 3, q = (nn >> 2) & 3, i = m >> 4, ln = q * 16 + (m & 15);
         const size_t off = (size_t)(((j * 4 + i) * 4 + v) * kSlotStride) + ln;
         o[h] = ((red[off] + red[kSlot + off]) + red[2 * kSlot + off]) + red[3 * kSlot + off];
-        if (a.bias) o[h] += __builtin_bit_cast(float, (u32)a.bias[gn + h] << 16);
+        if (a.bias) o[h] += __builtin_bit_cast(float, h == 0 ? bpair[it] << 16 : bpair[it] & 0xFFFF0000u);
         if (a.epilogue == 1) o[h] = gelu_tanh(o[h]);
       }
       *reinterpret_cast<u32*>(a.y + (size_t)gm * a.N + gn) = pack_bf16(o[0], o[1]);

@@ -406,6 +406,36 @@ def test_workspace_size_queries_and_checks():
         L.svdq_debug_set_quant_plan(0, 0)
 
 
+def test_call1_plan_choice_through_the_workspace_query():
+    """Call 1's plan shows in its workspace: 1 MiB of counters, then K-blocks x
+    row tiles x r/16 KB of fp32 partials when K is split.  The row-tile
+    kernel's plan for a few thousand tokens or fewer (K-blocks from its cost
+    model on the 256 CUs assumed without a device: 8 blocks of 6 groups for
+    64-512 tokens at K = 3072, 24 blocks of 10 groups for 64 tokens at
+    K = 15360), the one-wave kernel's plan past the 96 MB read cap (2048 x 12288:
+    16 blocks) and at the headline (6 blocks), and both test hooks."""
+    L = lib()
+    part = lambda kb, M, r: (1 << 20) + kb * ((M + 15) // 16) * (r // 16) * 1024
+    assert L.svdq_quantize_act_workspace_size(64, 3072, 32) == part(8, 64, 32)
+    assert L.svdq_quantize_act_workspace_size(512, 3072, 32) == part(8, 512, 32)
+    assert L.svdq_quantize_act_workspace_size(300, 3072, 16) == part(8, 300, 16)
+    assert L.svdq_quantize_act_workspace_size(64, 15360, 32) == part(24, 64, 32)
+    assert L.svdq_quantize_act_workspace_size(1024, 12288, 32) == part(4, 1024, 32)
+    assert L.svdq_quantize_act_workspace_size(2048, 12288, 32) == part(16, 2048, 32)
+    assert L.svdq_quantize_act_workspace_size(4608, 3072, 32) == part(6, 4608, 32)
+    try:
+        assert L.svdq_debug_set_quant_waves(1) == SUCCESS        # the one-wave kernel's own plan
+        assert L.svdq_quantize_act_workspace_size(64, 3072, 32) == part(24, 64, 32)
+        assert L.svdq_debug_set_quant_waves(8) == SUCCESS        # row-tile kernel, 2 forced K-blocks
+        assert L.svdq_debug_set_quant_plan(2, 0) == SUCCESS
+        assert L.svdq_quantize_act_workspace_size(200, 448, 32) == part(2, 200, 32)
+        assert L.svdq_debug_set_quant_plan(0, 0) == SUCCESS      # one K-block: nothing to add up
+        assert L.svdq_quantize_act_workspace_size(200, 448, 32) == 0
+    finally:
+        L.svdq_debug_set_quant_waves(0)
+        L.svdq_debug_set_quant_plan(0, 0)
+
+
 @pytest.mark.skipif(_gpu_visible(), reason="checks the no-GPU path")
 def test_large_shapes_pass_validation_up_to_the_limits():
     """Codes of 2^32 bytes and more (rows * K / 2) are addressed from 64-bit row

@@ -776,14 +776,14 @@ constexpr int kRowsMaxTiles = 128;
 constexpr double kRowsMaxKB = 96.0 * 1024;
 
 // Estimated time (us) of a row-tile plan, fitted (least squares) to a sweep of
-// HIP-graph-replayed launches on MI355X: 64 to 2048
-// tokens, K = 3072, 12288 and 15360, r = 32, KW in {2, 3, 4, 6, 8} and 4 to 24
-// K-blocks (rms error 1.3 us; on each of the twelve swept shapes the plan it
-// picks is the measured best or within 1 us of it).  Terms: launch and first
-// round trip; each group a wave walks, per workgroup sharing a compute unit
-// (the quantizer's dependency chain, ~0.25 us); the KB of X and lora_down a
-// compute unit reads; waves per compute unit; and with split K, the
-// workspace round trips and each batch of 8 partial reads.
+// HIP-graph-replayed launches on MI355X: 64 to 2048 tokens, K = 3072, 12288
+// and 15360, r = 32, KW in {2, 3, 4, 6, 8} and 1 to 24 K-blocks (rms error
+// 1.3 us; on each of the twelve swept shapes its pick is within 1.3 us of the
+// measured best, and is the best on seven).  Terms: launch and first round
+// trip; each group a wave walks, per workgroup sharing a compute unit (the
+// quantizer's dependency chain, ~0.25 us); the KB of X and lora_down a compute
+// unit reads; waves per compute unit; and with split K, the workspace round
+// trips and each batch of 8 partial reads.
 double rows_cost(int T, int G, int NT, int KW, int KB, int cus) {
   const Plan p = rows_plan(T, G, NT, KB, KW);
   const int gpw = (p.GB + p.KW - 1) / p.KW;

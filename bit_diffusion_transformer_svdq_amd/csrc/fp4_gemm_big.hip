@@ -52,6 +52,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int u32;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
@@ -393,7 +394,8 @@ void fp4_gemm_big_kernel(const Fp4BigArgs p) {
       const int m = m0 + wm * 128 + ml;
       const uint4 v = *reinterpret_cast<const uint4*>((ml < 64 ? stage_lo : stage_hi) + (ml & 63) * 256 +
                                                       ((c ^ (ml & 15)) << 4));
-      if (m < M) *reinterpret_cast<uint4*>(p.y + (size_t)m * N + n) = v;
+      // streaming (non-temporal) stores: Y is not read again by this launch
+      if (m < M) __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(p.y + (size_t)m * N + n));
     }
   }
 }

@@ -764,7 +764,9 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
         const int ml = 8 * t + (lane >> 3);
         const int m = m0 + wm * 64 + ml;
         const uint4 v = *reinterpret_cast<const uint4*>(stg + ml * 128 + ((c ^ (ml & 7)) << 4));
-        if (m < M) *reinterpret_cast<uint4*>(p.y + (size_t)m * N + nw + 8 * c) = v;
+        // streaming (non-temporal) stores: Y is not read again by this launch
+        if (m < M)
+          __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(p.y + (size_t)m * N + nw + 8 * c));
       }
     }
   }

@@ -535,13 +535,17 @@ svdq_status svdq_w4a4_group_acc_debug(const void* act_codes, const void* w_codes
   if (s != SVDQ_STATUS_SUCCESS) return s;
   s = check_current_device();
   if (s != SVDQ_STATUS_SUCCESS) return s;
-  // the launched problem: rows [m0, m0 + mc) and the 64-aligned column range
-  // around the window; the window is then relative to it
+  // the launched problem: the rows from the 16-row block holding m0 (codes
+  // arrays keep their storage order only in views at multiples of 16 rows) to
+  // m0 + mc, and the 64-aligned column range around the window; the window is
+  // then relative to it
+  const int64_t mb = m0 / 16 * 16;
   const int64_t nb = n0 / 64 * 64, ne = (n0 + nc + 63) / 64 * 64;
-  const uint8_t* ac = static_cast<const uint8_t*>(act_codes) + (size_t)m0 * (size_t)(K / 2);
+  const uint8_t* ac = static_cast<const uint8_t*>(act_codes) + (size_t)mb * (size_t)(K / 2);
   const uint8_t* wc = static_cast<const uint8_t*>(w_codes) + (size_t)nb * (size_t)(K / 2);
-  const svdq::DumpWindow win{acc, 0, (int)mc, (int)(n0 - nb), (int)(n0 - nb + nc)};
-  hipError_t e = svdq::launch_w4a4_gemm_lora_up(ac, nullptr, wc, nullptr, nullptr, nullptr, nullptr, mc, ne - nb,
+  const svdq::DumpWindow win{acc, (int)(m0 - mb), (int)(m0 - mb + mc), (int)(n0 - nb), (int)(n0 - nb + nc)};
+  hipError_t e = svdq::launch_w4a4_gemm_lora_up(ac, nullptr, wc, nullptr, nullptr, nullptr, nullptr,
+                                                m0 + mc - mb, ne - nb,
                                                 K, 0, SVDQ_EPILOGUE_NONE, nullptr, nullptr, win, svdq::Workspace{},
                                                 static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SVDQ_STATUS_HIP_ERROR, "gemm debug launch: %s", hipGetErrorString(e));

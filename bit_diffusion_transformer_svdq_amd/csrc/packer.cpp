@@ -371,6 +371,9 @@ svdq_status pack_impl(const uint16_t* w, const float* smooth, int64_t N, int64_t
         w_scales[static_cast<size_t>(n) * G + g] = sb;
         const double s = bf16_to_double(sb);
         uint8_t* out = &w_codes[static_cast<size_t>(n) * (K / 2) + g * 32];
+        // storage order: rows with bit 3 set hold the two 8-byte halves of every
+        // 16-byte granule exchanged (byte j of the row at j ^ 8)
+        const int flip = (n & 8) ? 8 : 0;
         for (int e = 0; e < 64; e += 2) {
           int q0 = 0, q1 = 0;
           if (s > 0) {
@@ -379,7 +382,7 @@ svdq_status pack_impl(const uint16_t* w, const float* smooth, int64_t N, int64_t
             q0 = std::max(-7, std::min(7, q0));
             q1 = std::max(-7, std::min(7, q1));
           }
-          out[e / 2] = static_cast<uint8_t>((q0 & 0xF) | ((q1 & 0xF) << 4));
+          out[(e / 2) ^ flip] = static_cast<uint8_t>((q0 & 0xF) | ((q1 & 0xF) << 4));
         }
       }
     }

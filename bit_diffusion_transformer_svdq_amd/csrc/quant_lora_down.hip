@@ -259,16 +259,19 @@ __device__ __forceinline__ void quant_group(const uint4& xa, const uint4& xb, co
 // (two 32-lane swaps, then two 16-lane swaps) gives lane seg the dwords of
 // 16 contiguous bytes: group g bytes 0-15, 16-31, group g+1 bytes 0-15, 16-31.
 // Each store instruction then writes 64 contiguous bytes per row instead of
-// four separate 4-byte pieces, and scale stores halve.
+// four separate 4-byte pieces, and scale stores halve.  `swap`: the row is
+// stored with the two 8-byte halves of every 16-byte granule exchanged (the
+// int4 storage order for rows with bit 3 set; see the GEMM kernel).
 __device__ __forceinline__ void store_group_pair(u32 a0, u32 b0, u32 s0, u32 a1, u32 b1, u32 s1, int g,
-                                                 int seg, bool row_ok, bool scale_pair_aligned,
+                                                 int seg, bool row_ok, bool scale_pair_aligned, bool swap,
                                                  uint8_t* crow, uint16_t* srow) {
   const v2u32 t02 = __builtin_amdgcn_permlane32_swap(a0, a1, false, false);
   const v2u32 t13 = __builtin_amdgcn_permlane32_swap(b0, b1, false, false);
   const v2u32 u01 = __builtin_amdgcn_permlane16_swap(t02[0], t13[0], false, false);
   const v2u32 u23 = __builtin_amdgcn_permlane16_swap(t02[1], t13[1], false, false);
   if (row_ok) {
-    *reinterpret_cast<uint4*>(crow + 32 * g + 16 * seg) = uint4{u01[0], u01[1], u23[0], u23[1]};
+    *reinterpret_cast<uint4*>(crow + 32 * g + 16 * seg) =
+        swap ? uint4{u23[0], u23[1], u01[0], u01[1]} : uint4{u01[0], u01[1], u23[0], u23[1]};
     if (seg == 0) {
       if (scale_pair_aligned) {
         *reinterpret_cast<u32*>(srow + g) = s0 | (s1 << 16);
@@ -281,10 +284,10 @@ __device__ __forceinline__ void store_group_pair(u32 a0, u32 b0, u32 s0, u32 a1,
 }
 
 // the last group of an odd-sized block: 4-byte code stores
-__device__ __forceinline__ void store_group(u32 a, u32 b, u32 sc, int g, int seg, bool row_ok,
+__device__ __forceinline__ void store_group(u32 a, u32 b, u32 sc, int g, int seg, bool row_ok, bool swap,
                                             uint8_t* crow, uint16_t* srow) {
   if (row_ok) {
-    uint8_t* c = crow + 32 * g + 4 * seg;
+    uint8_t* c = crow + 32 * g + ((4 * seg) ^ (swap ? 8 : 0));
     *reinterpret_cast<u32*>(c) = a;
     *reinterpret_cast<u32*>(c + 16) = b;
     if (seg == 0) srow[g] = (uint16_t)sc;
@@ -381,6 +384,7 @@ __global__ __launch_bounds__(64 * kMaxTiles) void quant_lora_down_kernel(QuantAr
   if (!tile_ok) return;  // no barrier follows
 
   uint8_t* crow = a.codes + (size_t)row * (K >> 1);
+  const bool swap = !kFp4 && (row & 8) != 0;  // int4 storage order of the row
   uint16_t* srow = a.scales + (size_t)row * a.G;
   v4f lacc[NT > 0 ? NT : 1];
 #pragma unroll
@@ -401,7 +405,7 @@ __global__ __launch_bounds__(64 * kMaxTiles) void quant_lora_down_kernel(QuantAr
       pb = cb;
       ps = sc;
     } else {
-      store_group_pair(pa, pb, ps, ca, cb, sc, g0 + gl - 1, seg, row_ok, pair_aligned, crow, srow);
+      store_group_pair(pa, pb, ps, ca, cb, sc, g0 + gl - 1, seg, row_ok, pair_aligned, swap, crow, srow);
     }
   };
   const int nfull = gc / kDepth;
@@ -429,7 +433,7 @@ __global__ __launch_bounds__(64 * kMaxTiles) void quant_lora_down_kernel(QuantAr
       emit(gl, ca, cb, sc);
     }
   }
-  if (gc & 1) store_group(pa, pb, ps, g0 + gc - 1, seg, row_ok, crow, srow);
+  if (gc & 1) store_group(pa, pb, ps, g0 + gc - 1, seg, row_ok, swap, crow, srow);
 
   if constexpr (NT > 0) {
     // lane l holds rows 4*(l/16)+v of the tile, rank 16t + l%16
@@ -579,6 +583,7 @@ __global__ __launch_bounds__(64 * kMaxKW) void quant_lora_down_rows_kernel(Quant
   __asm__ volatile("" ::: "memory");
 
   uint8_t* crow = a.codes + (size_t)row * (K >> 1);
+  const bool swap = !kFp4 && (row & 8) != 0;  // int4 storage order of the row
   uint16_t* srow = a.scales + (size_t)row * a.G;
   v4f lacc[nt1];
 #pragma unroll
@@ -596,7 +601,7 @@ __global__ __launch_bounds__(64 * kMaxKW) void quant_lora_down_rows_kernel(Quant
         pb = cb;
         ps = sc;
       } else {
-        store_group_pair(pa, pb, ps, ca, cb, sc, gw + j - 1, seg, row_ok, pair_aligned, crow, srow);
+        store_group_pair(pa, pb, ps, ca, cb, sc, gw + j - 1, seg, row_ok, pair_aligned, swap, crow, srow);
       }
     };
     const int nfull = n / kD;
@@ -619,7 +624,7 @@ __global__ __launch_bounds__(64 * kMaxKW) void quant_lora_down_rows_kernel(Quant
         emit(j, ca, cb, sc);
       }
     }
-    if (n & 1) store_group(pa, pb, ps, gw + n - 1, seg, row_ok, crow, srow);
+    if (n & 1) store_group(pa, pb, ps, gw + n - 1, seg, row_ok, swap, crow, srow);
   }
 
   if constexpr (NT > 0) {

@@ -24,11 +24,17 @@
 // retire in issue order, so the wait for stage q is an explicit
 // s_waitcnt vmcnt(4): the four DMAs of the next pair, issued last in every
 // iteration, may stay in flight.  Inside a stage, the 16-byte granule gg (0..3)
-// of row r sits at slot 4r + (gg ^ r[3:2]).  A 64-byte stage row covers 16 of
-// the LDS's 32 four-byte banks, so rows r and r + 2 share banks whatever the
-// granule order: the 8-byte fragment reads of a 16-lane phase find two lanes
-// per bank pair (2-way conflicts), which no swizzle of whole 16-byte DMA
-// granules removes.  Each thread owns the scales of one token or weight row and
+// of row r sits at slot 4r + (gg ^ r[2:1]).  An 8-byte fragment read of a
+// 16-lane phase (16 rows, one 8-byte piece of each) then finds no two lanes on
+// one bank pair: a 64-byte stage row covers 16 of the 32 four-byte banks, so a
+// piece's bank pair is set by r[0], the granule slot (r[2:1]) and its half in
+// the granule, and the half is r[3] because of the int4 storage order of the
+// codes (rows with bit 3 set hold the two 8-byte halves of every 16-byte
+// granule exchanged; calls 1 and the packer write them so).  With the plain
+// order and a granule swizzle alone, rows r and r + 8 met on every bank pair,
+// which no swizzle of whole 16-byte DMA granules avoids.  The 16-byte reads of
+// the MXFP4 variant (8-lane phases) are conflict-free with the same swizzle.
+// Each thread owns the scales of one token or weight row and
 // reads them three group pairs at a time (one 16-byte buffer load), ahead of
 // the pairs' DMAs, then stores the converted scales of pair q+1 into the
 // second of two scale areas.  The epilogue reads the lora_up and lora_act
@@ -250,7 +256,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
   const int lseg = lane >> 4;
 
   // DMA role: instruction k (0, 1) of a wave fills slots 256k + 64*wave + lane
-  // of each operand tile, i.e. row s >> 2, granule (s & 3) ^ r[3:2]: four lanes
+  // of each operand tile, i.e. row s >> 2, granule (s & 3) ^ r[2:1]: four lanes
   // cover the 64 bytes of one row.  The workgroup's first row is a 64-bit base
   // pointer; lane offsets within its 128 rows fit 32 bits for every K.
   const uint8_t* wbase = p.w_codes + (size_t)n0 * (size_t)KB;
@@ -260,7 +266,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
   for (int k = 0; k < 2; ++k) {
     const int s = 256 * k + 64 * wave + lane;
     const int row = s >> 2;
-    gsel[k] = (u32)((s & 3) ^ ((row >> 2) & 3));
+    gsel[k] = (u32)((s & 3) ^ ((row >> 1) & 3));
     woff[k] = (u32)(min(n0 + row, N - 1) - n0) * (u32)KB + 16u * (gsel[k] & 1u);
     aoff[k] = (u32)(min(m0 + row, M - 1) - m0) * (u32)KB + 16u * (gsel[k] & 1u);
   }
@@ -275,12 +281,13 @@ __global__ __launch_bounds__(kThreads, kOcc) void w4a4_gemm_kernel(const GemmArg
   };
 
   // Fragment read offsets for the first group of a pair: row R, granule
-  // lseg >> 1, 8-byte half lseg & 1.  The rows of fragment i (R + 16i) share
-  // the swizzle R[3:2] of R = wX*64 + l16, and the second group of the pair
-  // sits 32 bytes away (granule + 2 flips bit 1 of the slot): offset ^ 32.
-  const int fsw = (l16 >> 2) & 3;
-  const int fw = 64 * (wn * 64 + l16) + 16 * ((lseg >> 1) ^ fsw) + 8 * (lseg & 1);
-  const int fa = 64 * (wm * 64 + l16) + 16 * ((lseg >> 1) ^ fsw) + 8 * (lseg & 1);
+  // lseg >> 1, 8-byte half (lseg & 1) ^ R[3] (the storage order).  The rows of
+  // fragment i (R + 16i) share R[3:1] of R = wX*64 + l16, and the second group
+  // of the pair sits 32 bytes away (granule + 2 flips bit 1 of the slot):
+  // offset ^ 32.
+  const int fsw = (l16 >> 1) & 3;
+  const int fw = 64 * (wn * 64 + l16) + 16 * ((lseg >> 1) ^ fsw) + 8 * ((lseg & 1) ^ ((l16 >> 3) & 1));
+  const int fa = 64 * (wm * 64 + l16) + 16 * ((lseg >> 1) ^ fsw) + 8 * ((lseg & 1) ^ ((l16 >> 3) & 1));
 
   // scale role: threads 0..127 (waves 0, 1) -> token slot tid, 128..255 ->
   // weight row tid-128 (wave-uniform, so the buffer resource below is scalar)

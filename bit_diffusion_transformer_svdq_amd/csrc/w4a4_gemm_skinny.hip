@@ -263,7 +263,17 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkinnyArgs<kDump> a
   // The swaps are done in place on the ring registers (x <-> z, y <-> w
   // halves), which keeps the compiler from copying ring slots (a copy of a
   // register still being loaded waits for it).
+  // Rows with bit 3 set arrive in the int4 storage order (the two 8-byte
+  // halves of every 16-byte granule exchanged) and are put back first; the
+  // lane's row has bit 3 of l16 (row bases are multiples of 16; clamped rows
+  // past N or M only feed outputs that are not stored).
+  const bool half_swapped = (l16 & 8) != 0;
   auto split = [&](uint4& f, uint2& g0, uint2& g1) {
+    const u32 x = f.x, y = f.y;
+    f.x = half_swapped ? f.z : f.x;
+    f.y = half_swapped ? f.w : f.y;
+    f.z = half_swapped ? x : f.z;
+    f.w = half_swapped ? y : f.w;
     __asm__ volatile("v_permlane32_swap_b32 %0, %1" : "+v"(f.x), "+v"(f.z));
     __asm__ volatile("v_permlane32_swap_b32 %0, %1" : "+v"(f.y), "+v"(f.w));
     g0 = uint2{f.x, f.y};

@@ -23,7 +23,14 @@
  *    lora_up = L2^T [N,r].  Every array is dense, row-major, no padding.
  *  - bf16 arrays are passed as raw 16-bit patterns (IEEE bfloat16).
  *  - int4 codes: two per byte along K, element 2i in the low nibble of byte i,
- *    two's complement, values in [-7, 7].  Codes are [rows, K/2] bytes.
+ *    two's complement, values in [-7, 7].  Codes are [rows, K/2] bytes in the
+ *    storage order: in every row whose index in the array has bit 3 set (rows
+ *    8-15 of each 16), the two 8-byte halves of every 16-byte piece of the row
+ *    are exchanged (byte j of the row sits at j ^ 8); rows 0-7 of each 16 are
+ *    in the plain order.  Call 1 writes and call 2 reads this order, and
+ *    svdq_pack_weights writes it, so a view of a codes array must start at a
+ *    multiple of 16 rows.  (It lets call 2 read its LDS fragments without bank
+ *    conflicts.)  MXFP4 and AWQ codes keep the plain order.
  *  - Scales: bf16 [rows, K/group_size], one per row per group of group_size
  *    consecutive k.  Only group_size == 64 and int4 are supported (the int4
  *    scheme's group size in the quantization config on mind-verse.de, section

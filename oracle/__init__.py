@@ -10,4 +10,4 @@ from .svdq_oracle import (GROUP, QMAX, SMOOTH_EPS, activation_absmax, bf16_to_f6
                           lowrank_split, pack_int4, pack_weights,
                           quantize_act_lora_down, quantize_activation_groups,
                           quantize_weight_groups, smooth_activations,
-                          smooth_factors, smoothed_weight, unpack_int4)
+                          smooth_factors, smoothed_weight, storage_order, unpack_int4)

@@ -36,8 +36,9 @@ bfloat16 (8 significant bits), ``fl32(v)`` rounds to nearest-even binary32,
 Layouts (nn.Linear convention, the module tree is unchanged by the swap described
 in mind-verse.de § "Native Ladefunktion in Diffusers"): X [M, K], W [N, K],
 lora_down = L1^T [r, K], lora_up = L2^T [N, r], Y [M, N].  int4 codes are packed
-two per byte along K, element 2i in the low nibble, two's complement; scales are
-row-major [rows, K / group].
+two per byte along K, element 2i in the low nibble, two's complement, the rows
+in the boundary's storage order (``storage_order``); scales are row-major
+[rows, K / group].
 """
 from __future__ import annotations
 
@@ -92,17 +93,34 @@ def f64_to_bf16(v) -> np.ndarray:
 # int4 packing (two's complement nibbles, element 2i low, 2i+1 high)
 # ---------------------------------------------------------------------------
 
+def storage_order(b) -> np.ndarray:
+    """The storage order of packed int4 rows at the library's C boundary
+    (include/svdq.h, "Layouts"): in every row whose index in the array has bit 3
+    set (rows 8-15 of each 16), the two 8-byte halves of every 16-byte piece of
+    the row are exchanged, i.e. byte j of the row is stored at j ^ 8.  Rows
+    0-7 of each 16 keep the plain order.  The exchange is its own inverse.  It
+    is a layout convention of the boundary, not part of the method."""
+    b = np.array(b, dtype=np.uint8, copy=True)
+    swapped = (np.arange(b.shape[0]) & 8) != 0
+    if swapped.any():
+        if b.shape[1] % 16:
+            raise ValueError("packed rows of 9 or more rows need a multiple of 16 bytes")
+        b[swapped] = b[swapped][:, np.arange(b.shape[1]) ^ 8]
+    return b
+
+
 def pack_int4(q) -> np.ndarray:
-    """Pack int codes in [-8, 7] of shape [rows, K] (K even) into uint8 [rows, K/2]."""
+    """Pack int codes in [-8, 7] of shape [rows, K] (K even) into uint8 [rows, K/2]:
+    element 2i in the low nibble of byte i, then the rows in ``storage_order``."""
     q = np.asarray(q, dtype=np.int64)
     lo = q[:, 0::2] & 0xF
     hi = q[:, 1::2] & 0xF
-    return (lo | (hi << 4)).astype(np.uint8)
+    return storage_order((lo | (hi << 4)).astype(np.uint8))
 
 
 def unpack_int4(codes) -> np.ndarray:
     """Decode uint8 [rows, K/2] into int8 [rows, K] (inverse of ``pack_int4``)."""
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    c = storage_order(codes).astype(np.int64)
     nib = np.empty((c.shape[0], c.shape[1] * 2), dtype=np.int64)
     nib[:, 0::2] = c & 0xF
     nib[:, 1::2] = c >> 4

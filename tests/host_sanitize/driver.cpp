@@ -61,8 +61,10 @@ static void run_calls(svdq_status want) {
   CHECK(svdq_w4a4_group_acc_debug(codes.p, wc.p, M, N, K, 37, 5, 70, 3, acc.as<int32_t>(), nullptr) == want);
   if (want == SVDQ_STATUS_SUCCESS) {
     CHECK(std::string(g_fake.last) == "dump" && g_fake.last_out == acc.p);
-    // rows [37, 42) launched as rows [0, 5); columns [64, 128) launched, window [6, 9)
-    CHECK(g_fake.last_window[0] == 0 && g_fake.last_window[1] == 5);
+    // rows [37, 42) launched from the 16-row block at 32 (storage order of the
+    // codes), as rows [0, 10) with the window [5, 10); columns [64, 128)
+    // launched, window [6, 9)
+    CHECK(g_fake.last_window[0] == 5 && g_fake.last_window[1] == 10);
     CHECK(g_fake.last_window[2] == 6 && g_fake.last_window[3] == 9);
   }
 }

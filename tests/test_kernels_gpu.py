@@ -11,8 +11,8 @@ import pytest
 
 import oracle as O
 import synthetic as S
-from tests.gpu_util import (bf16_bits, check_quant as _check_quant, check_y as _check_y, custom_case,
-                            oracle_case, to_dev, to_dev_bf16)
+from tests.gpu_util import (Y_MAX_ABS, Y_REL_FRO, bf16_bits, check_quant as _check_quant, check_y as _check_y,
+                            custom_case, oracle_case, to_dev, to_dev_bf16, y_errors)
 
 pytestmark = pytest.mark.gpu
 
@@ -395,6 +395,30 @@ def test_split_shapes_parity(M, K, N):
 
 
 # ---- the boundary: accumulator windows and caller-owned workspaces ----
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_row_views_at_multiples_of_16(path):
+    """Codes arrays are in the boundary's storage order (rows 8-15 of every 16
+    with their 8-byte halves exchanged), so a view starting at a multiple of 16
+    rows is a valid input of call 2: rows 48.. of call 1's outputs give the
+    oracle's Y of those rows, on both kernels."""
+    import bit_diffusion_transformer_svdq_amd as K
+    import torch
+    d, lam, packed = custom_case(150, 256, 192, 16, seed=17)
+    codes, scales, la = K.quantize_act_lora_down(to_dev_bf16(d["x"]), to_dev(lam), to_dev_bf16(packed["lora_down"]))
+    ref = O.quantize_act_lora_down(d["x"], lam, packed["lora_down"])
+    K.debug_set_gemm_path(path)
+    try:
+        y = K.w4a4_gemm_lora_up(codes[48:], scales[48:], to_dev(packed["w_codes"]), to_dev_bf16(packed["w_scales"]),
+                                la[48:], to_dev_bf16(packed["lora_up"]), to_dev_bf16(d["bias"]))
+        torch.cuda.synchronize()
+    finally:
+        K.debug_set_gemm_path(0)
+    y_ref, _ = O.linear_output(ref["act_codes"], ref["act_scales"], packed["w_codes"], packed["w_scales"],
+                               ref["lora_act"], packed["lora_up"], d["bias"], rows=np.arange(48, 150))
+    rel, mx = y_errors(bf16_bits(y), y_ref)
+    assert rel <= Y_REL_FRO and mx <= Y_MAX_ABS, (rel, mx)
+
 
 @pytest.mark.parametrize("path", [1, 2])
 def test_group_accumulator_window(path):

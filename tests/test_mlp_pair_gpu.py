@@ -101,7 +101,7 @@ def _check_pair(du, up, dn, rows=None):
                                 a["lora_act"], pu["lora_up"], bu, epilogue="gelu_tanh")
     _assert_bar(hb, h_star, "H")
     _assert_bar(yb, ref["y"], "Y")
-    dq = np.abs(O.unpack_int4(codes_d.cpu().numpy()[sel]).astype(int)
+    dq = np.abs(O.unpack_int4(codes_d.cpu().numpy())[sel].astype(int)
                 - O.unpack_int4(ref["a_down"]["act_codes"]).astype(int))
     assert dq.max() <= 1 and (dq == 0).mean() >= 0.99, (dq.max(), (dq == 0).mean())
     # call 1 of the down-projection on the oracle's H: bit-exact

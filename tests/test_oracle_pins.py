@@ -74,6 +74,22 @@ def test_packing_golden_and_roundtrip():
     assert np.array_equal(O.pack_int4(O.unpack_int4(b)), b)
 
 
+def test_storage_order_golden():
+    """Rows 8-15 of every 16 hold their 8-byte halves exchanged; a hand-derived
+    9-row example (rows 0-7 plain, row 8 exchanged) and the round trip over 40
+    rows of random codes."""
+    gold = json.load(open(os.path.join(GOLD, "int4_storage_order.json")))
+    q = np.tile(np.array(gold["codes_every_row"], dtype=np.int8), (gold["rows"], 1))
+    b = O.pack_int4(q)
+    for r in range(8):
+        assert b[r].tolist() == gold["bytes_row0"], r
+    assert b[8].tolist() == gold["bytes_row8"]
+    rq = np.random.default_rng(5).integers(-8, 8, size=(40, 128)).astype(np.int8)
+    assert np.array_equal(O.unpack_int4(O.pack_int4(rq)), rq)
+    with pytest.raises(ValueError):
+        O.pack_int4(np.zeros((9, 8), np.int8))  # 4-byte rows cannot hold the order
+
+
 # ------------------------------------------------------ golden quantization ---
 
 def _golden_act_inputs(gold):

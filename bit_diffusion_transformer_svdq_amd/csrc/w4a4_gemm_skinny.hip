@@ -15,7 +15,10 @@
 // a chunk of up to 64 tokens, and its 8 waves split K: wave w takes groups
 // [w*G/8, (w+1)*G/8).  Every weight byte is read from HBM once, by one wave,
 // straight into registers (16 rows x 64 bytes, a group pair, per load
-// instruction), with a ring of 3 pairs in flight.  The token rows are
+// instruction), one pair in flight per wave: with two or three in flight (all
+// of a wave's pairs at 64 tokens) every shape ran 1-8 % slower, since the
+// chip's memory system then holds more requests than it serves well.  The
+// token rows are
 // small and shared by every workgroup (L2).  At the end the 8 partial tiles
 // are added in a fixed order through LDS, so results do not depend on timing.
 //
@@ -50,7 +53,7 @@ typedef u32 v2u32 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMC = 64;              // token rows per chunk (4 MFMA columns of 16)
-constexpr int kDepth = 3;            // group pairs in flight per wave
+constexpr int kDepth = 1;            // group pairs in flight per wave (ring slots)
 constexpr int kSlotStride = 65;      // floats per (tile, v) row of a reduction slot (bank padding)
 constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23

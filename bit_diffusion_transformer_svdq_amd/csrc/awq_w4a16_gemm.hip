@@ -16,7 +16,7 @@
 // quarters.  The 16 rows' Delta and z go into LDS by global_load_lds_dwordx4,
 // and each wave streams its quarter of the 16 code rows through a ring of its
 // own: a chunk is 2 groups x 16 rows x 32 bytes = 1 KB, one DMA instruction,
-// three chunks in flight.  These DMAs are issued first; while they stream,
+// two chunks in flight.  These DMAs are issued first; while they stream,
 // x_hat of the tile's tokens is written to LDS in the operand order below,
 // with the per-group sums xs = sum_{k in g} x_hat.  The fp32 partials of the
 // waves are added in wave order through LDS.
@@ -47,7 +47,7 @@ typedef unsigned int u32;
 typedef u32 v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;                // waves per n-tile (they split K)
-constexpr int kRing = 3;                 // code chunks in flight per wave
+constexpr int kRing = 2;                 // code chunks in flight per wave (3 and 1: slower)
 // workgroups per CU an instance fits in (LDS), at most 5 (registers)
 constexpr int awq_occupancy(int rows, int kmax, int tiles) {
   const int g = kmax / 64;
@@ -117,12 +117,12 @@ void awq_w4a16_kernel(const AwqArgs args) {
   constexpr int kRingStage = 1024 * kWaves * kTiles;
   // Code ring: stage s holds, for each wave w, one chunk (2 groups x 16 rows
   // x 32 bytes = 1 KB) at 1024 w.
-  __shared__ __attribute__((aligned(16))) uint8_t ring0[kRingStage], ring1[kRingStage], ring2[kRingStage];
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[kRingStage], ring1[kRingStage], ring2[kRing > 2 ? kRingStage : 16];
   __shared__ __attribute__((aligned(16))) uint8_t dz_s[kTiles * 16 * kDzSlots];  // per tile [16][G] Delta, z
   __shared__ __attribute__((aligned(16))) float xs_s[16 * kGMax];                 // [G][16] sum x_hat
   __shared__ __attribute__((aligned(16))) uint4 xh_s[kRowsMax * kKMax / 8];       // [rows][K/8]
   auto stage_of = [&](int s) -> uint8_t* { return s == 0 ? ring0 : s == 1 ? ring1 : ring2; };
-  static_assert(kRing == 3, "one LDS object per ring stage");
+  static_assert(kRing == 2 || kRing == 3, "one LDS object per ring stage");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -175,8 +175,8 @@ void awq_w4a16_kernel(const AwqArgs args) {
   // 2. The 16 rows' Delta and z (contiguous in [N, G] layout; n0 is a
   //    multiple of 16, so both start on a 16-byte boundary), a fixed count of
   //    DMAs per wave (blocks past the last repeat it, pad lanes the last
-  //    slot); then exactly 3 code chunks of this wave, so "at most 3
-  //    outstanding" means everything before has landed.  They go out before
+  //    slot); then exactly kRing code chunks of this wave, so "at most
+  //    kRing outstanding" means everything before has landed.  They go out before
   //    x_hat is staged, so the weight stream starts at once; the staging
   //    waits for the x and 1/s loads with an explicit count of the DMAs
   //    issued after them (vector-memory counters retire in issue order).

@@ -20,7 +20,9 @@
 //    SIMD), so a stage is 32 MFMAs (1024 cycles) for 32 KB of operand data:
 //    half the LDS and L2 bytes per MFMA of the 128 x 128 tile;
 //  * a ring of four 128-wide k stages in LDS (32 KB each), filled by
-//    global_load_lds_dwordx4 four stages ahead, with one barrier per stage;
+//    global_load_lds_dwordx4 three stages ahead (four ahead, and two, were
+//    slower: more requests in flight than the memory system serves well only
+//    queue, fewer leave too little time), with one barrier per stage;
 //  * the fragments of stage q+1 are read from LDS while the MFMAs of stage q
 //    run (two register sets), so the matrix core does not wait on LDS latency;
 //  * the E8M0 exponents move like the codes, 16 bytes (4 stages) per row at
@@ -253,15 +255,17 @@ void fp4_gemm_big_kernel(const Fp4BigArgs p) {
       }
   };
 
-  // Stage q goes into LDS buffer q % 4, four stages ahead of its MFMAs, and
-  // the exponents of stages 4c .. 4c+3 into area c % 2, issued right after
-  // stage 4c; past the end the loads repeat the last stage or block (into a
-  // buffer nobody reads again), so every iteration issues the same
-  // operations and the loop body has no branch.  At the top of iteration q,
-  // the wait leaves the stages q+2 and q+3 (and exponents issued after them)
-  // in flight, which with the barrier means stage q+1 and its exponents are
-  // in LDS for every wave; stage q's fragments are already in registers and
-  // its buffer is free for stage q+4.  The fragments of stage q+1 are then
+  // Stage q goes into LDS buffer q % 4, three stages ahead of its MFMAs
+  // (issued in iteration q - 3), and the exponents of stages 4c .. 4c+3 into
+  // area c % 2, issued right after stage 4c (in iteration 4c - 3); past the
+  // end the loads repeat the last stage or block (into a buffer nobody reads
+  // again), so every iteration issues the same operations and the loop body
+  // has no branch.  At the top of iteration q, the wait leaves only what
+  // iteration q-1 issued in flight (stage q+2, and an exponent block when
+  // q % 4 == 2), which with the barrier means stage q+1 and its exponents
+  // are in LDS for every wave; stage q's fragments are already in registers,
+  // and stage q-1's buffer, read in iteration q-2, is free for stage q+3.
+  // The fragments of stage q+1 are then
   // read while stage q's MFMAs run.  Unrolled by 8 (two exponent areas x four
   // stages), so every buffer, area and register-set index is a constant.
   Frags f[2];
@@ -270,18 +274,17 @@ void fp4_gemm_big_kernel(const Fp4BigArgs p) {
   dma_exps(0, 0);
   dma_stage(min(1, S - 1), 1);
   dma_stage(min(2, S - 1), 2);
-  dma_stage(min(3, S - 1), 3);
-  wait_vm_lds<24>();
+  wait_vm_lds<16>();
   barrier();
   read_stage(f[0], 0, 0, 0);
   auto iteration = [&](int q, auto uc) {
     constexpr int u = decltype(uc)::value;  // q % 8
     // vector-memory operations issued after the ones that must have landed:
     // 8 per stage, plus 2 for an exponent block issued after them
-    if constexpr ((u & 3) == 0 || (u & 3) == 3) wait_vm_lds<16>(); else wait_vm_lds<18>();
+    if constexpr ((u & 3) == 2) wait_vm_lds<10>(); else wait_vm_lds<8>();
     barrier();
-    dma_stage(min(q + 4, S - 1), u & 3);
-    if constexpr ((u & 3) == 0) dma_exps(min((q >> 2) + 1, C - 1), ((u >> 2) + 1) & 1);
+    dma_stage(min(q + 3, S - 1), (u + 3) & 3);
+    if constexpr ((u & 3) == 1) dma_exps(min((q >> 2) + 1, C - 1), ((u >> 2) + 1) & 1);
     __builtin_amdgcn_sched_barrier(0);
     read_stage(f[(u + 1) & 1], (u + 1) & 3, ((u + 1) >> 2) & 1, (u + 1) & 3);
     mfma_stage(f[u & 1]);

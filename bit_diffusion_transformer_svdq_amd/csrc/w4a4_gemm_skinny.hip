@@ -18,8 +18,7 @@
 // instruction), one pair in flight per wave: with two or three in flight (all
 // of a wave's pairs at 64 tokens) every shape ran 1-8 % slower, since the
 // chip's memory system then holds more requests than it serves well.  The
-// token rows are
-// small and shared by every workgroup (L2).  At the end the 8 partial tiles
+// token rows are small and shared by every workgroup (L2).  At the end the 8 partial tiles
 // are added in a fixed order through LDS, so results do not depend on timing.
 //
 // Per group and wave: N16 weight fragments and up to 4 activation fragments
@@ -129,10 +128,14 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkinnyArgs<kDump> a
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // 1. the wave's group pairs: fragments in a ring of kDepth pairs, issued
-  //    first (the weight stream is the bulk of the traffic).  A lane loads 16
-  //    bytes, so each instruction moves 64 contiguous bytes of each of 16 rows
-  //    (runs of 32 bytes halve what the memory system delivers): lanes 0-31
+  // 1. the wave's group pairs: fragments in a ring of kDepth pairs.  The
+  //    first is issued after the scale and lora staging below: those short
+  //    loads then do not queue behind the chip-wide weight stream, and the
+  //    first pair lands about when the staging barrier is passed (2-7 %
+  //    faster than issuing the pair first, on every few-token shape measured).
+  //    A lane loads 16 bytes, so each instruction moves 64 contiguous bytes of
+  //    each of 16 rows (runs of 32 bytes halve what the memory system
+  //    delivers): lanes 0-31
   //    get group 2p, lanes 32-63 group 2p+1.  Rows past N or M re-read the
   //    last row, pairs past the wave's range re-read its last pair, and the
   //    missing half of a last odd pair re-reads the group before it, so every
@@ -153,12 +156,10 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkinnyArgs<kDump> a
 #pragma unroll
     for (int i = 0; i < 4; ++i) ra[s][i] = *reinterpret_cast<const uint4*>(arow[i] + off);
   };
-  fetch(0, min(p_begin, plast));
 
   // 2. scales (wave: rows wave, wave+8, ...; lane: group) and lora tiles
   //    (16 bytes per thread) into LDS; the debug variant needs neither.  They
-  //    are waited for with the first pair only; the rest of the ring is
-  //    issued after them and streams while the first pairs are computed.
+  //    are issued before any pair; the ring follows them.
   if constexpr (!kDump) {
     for (int g0 = 0; g0 < G; g0 += 64) {
       const int g = min(g0 + lane, G - 1);
@@ -192,6 +193,7 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkinnyArgs<kDump> a
       *reinterpret_cast<uint4*>(lu_s + (size_t)row * a.r + k) = *reinterpret_cast<const uint4*>(src);
     }
   }
+  fetch(0, min(p_begin, plast));
 #pragma unroll
   for (int s = 1; s < kDepth; ++s) fetch(s, min(p_begin + s, plast));
 

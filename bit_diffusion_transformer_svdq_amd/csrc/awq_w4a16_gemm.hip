@@ -343,6 +343,10 @@ constexpr AwqClass kClasses[] = {
     {16, 4096, 1, awq_w4a16_kernel<16, 4096, 1>},
 };
 constexpr AwqClass kWide = {4, 3072, 3, awq_w4a16_kernel<4, 3072, 3>};
+// one token, K <= 4096: two or three n-tiles per workgroup (the tiles share the
+// x_hat staging, so a workgroup re-reads x and 1/s once per 32 or 48 rows)
+constexpr AwqClass kOne2 = {1, 4096, 2, awq_w4a16_kernel<1, 4096, 2>};
+constexpr AwqClass kOne3 = {1, 4096, 3, awq_w4a16_kernel<1, 4096, 3>};
 constexpr int kCus = 256;
 const AwqClass* awq_class(int64_t K, int64_t rows) {
   for (const AwqClass& c : kClasses)
@@ -366,6 +370,17 @@ hipError_t launch_awq_w4a16(const uint16_t* x, const float* smooth, const uint8_
       ntiles * mtiles > (int64_t)awq_occupancy(c->rows, c->kmax, 1) * kCus &&
       (ntiles + kWide.tiles - 1) / kWide.tiles * mtiles <= (int64_t)awq_occupancy(4, 3072, 3) * kCus)
     c = &kWide;
+  // One token (measured on MI355X, HIP-graph replays): stacked launches run
+  // two tiles per workgroup (38 x 3072 -> 18432 276 -> 255 us, 38 x 3072 ->
+  // 9216 139 -> 129 us); a single launch takes the fewest tiles per workgroup
+  // (2 or 3) that bring the grid within one workgroup per CU (3072 -> 9216:
+  // 3 tiles, 8.47 -> 7.93 us; 3072 -> 6144: 2 tiles, 7.26 -> 6.70 us), else
+  // one (3072 -> 18432 with 2 or 3 tiles: 12.1 / 12.2 against 11.8 us).
+  if (rows == 1 && K <= kOne2.kmax && c->tiles == 1) {
+    if (L > 1) c = &kOne2;
+    else if ((ntiles + 1) / 2 <= kCus) c = &kOne2;
+    else if ((ntiles + 2) / 3 <= kCus) c = &kOne3;
+  }
   const dim3 grid((unsigned)((ntiles + c->tiles - 1) / c->tiles), (unsigned)mtiles, (unsigned)L);
   hipLaunchKernelGGL(c->kernel, grid, dim3(64 * kWaves * c->tiles), 0, stream, a);
   return hipGetLastError();

@@ -366,8 +366,12 @@ hipError_t launch_awq_w4a16(const uint16_t* x, const float* smooth, const uint8_
   const AwqClass* c = awq_class(K, rows);
   if (!c) return hipErrorInvalidValue;  // excluded by the caller's awq_supported check
   const int64_t ntiles = N / 16, mtiles = (M + 15) / 16;
+  // Two to four tokens: three tiles per workgroup when one tile per workgroup
+  // would need more than one wave of workgroups, and always for stacked
+  // launches (their grids are L times larger: 38 x 3072 -> 9216 at four tokens
+  // 219 -> 163 us, at two 181 -> 149 us, HIP-graph replays on MI355X)
   if (rows > 1 && rows <= kWide.rows && K <= kWide.kmax &&
-      ntiles * mtiles > (int64_t)awq_occupancy(c->rows, c->kmax, 1) * kCus &&
+      (L > 1 || ntiles * mtiles > (int64_t)awq_occupancy(c->rows, c->kmax, 1) * kCus) &&
       (ntiles + kWide.tiles - 1) / kWide.tiles * mtiles <= (int64_t)awq_occupancy(4, 3072, 3) * kCus)
     c = &kWide;
   // One token (measured on MI355X, HIP-graph replays): stacked launches run

@@ -11,9 +11,10 @@
 //   Y[m,n] = bf16( sum_g Delta[n,g] * sum_{k in g} x_hat[m,k] (q[n,k] - z[n,g]) + b[n] )
 //
 // These layers see one conditioning vector per image (M = batch), so the
-// kernel is a weight stream: a workgroup owns 16 output channels (one MFMA
-// n-tile) and one tile of up to 16 tokens, and its four waves split K into
-// quarters.  The 16 rows' Delta and z go into LDS by global_load_lds_dwordx4,
+// kernel is a weight stream: an n-tile of 16 output channels (one MFMA tile)
+// and a tile of up to 16 tokens are served by four waves that split K into
+// quarters; a workgroup holds one to three n-tiles, which share the staged
+// x_hat (the host picks the count per shape).  The 16 rows' Delta and z go into LDS by global_load_lds_dwordx4,
 // and each wave streams its quarter of the 16 code rows through a ring of its
 // own: a chunk is 2 groups x 16 rows x 32 bytes = 1 KB, one DMA instruction,
 // two chunks in flight.  These DMAs are issued first; while they stream,
@@ -92,7 +93,8 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
 // kRowsMax x kKMax: the largest token tile and K the instance stages;
 // kTiles: n-tiles per workgroup, each served by its own 4 waves, all sharing
 // the staged x_hat (several tiles per workgroup let a grid with more tiles
-// than one wave of workgroups run in one).  Every LDS area is a static
+// than one wave of workgroups run in one, and re-read x and 1/s once per 32
+// or 48 rows instead of once per 16).  Every LDS area is a static
 // object: the compiler then tracks which of them a DMA in flight writes, and
 // waits only for the ring stage a read depends on (an access to dynamic LDS
 // would wait for every DMA in flight).
